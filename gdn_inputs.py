@@ -248,3 +248,38 @@ def torch_decode_inputs(B, H, dk, dv, steps, *, per_key=False, device="cuda",
     log_alpha = torch.rand(la_shape, generator=g, device=device, dtype=f32) * (hi - lo) + lo
     beta = torch.sigmoid(torch.randn((steps, B, H), generator=g, device=device, dtype=f32))
     return dict(state0=state0, q=q, k=k, v=v, log_alpha=log_alpha, beta=beta)
+
+
+def torch_seq_inputs(prefix_lens, branch_lens, branch_parent, H, dk, dv, *, conv=True,
+                     device="cuda", la_range=(-0.1, -0.001), seed=0):
+    """Full-size flat-stream inputs drawn on the device (same distributions
+    and draw order as `seq_inputs`; q/k/v bf16, the rest float32)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = torch.float32
+    Np, Nb = int(sum(prefix_lens)), int(sum(branch_lens))
+    N = Np + Nb
+
+    def unit(shape):
+        x = torch.randn(shape, generator=g, device=device, dtype=f32)
+        return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    q = unit((N, H, dk))
+    k = unit((N, H, dk))
+    v = torch.randn((N, H, dv), generator=g, device=device, dtype=f32).to(torch.bfloat16)
+    lo, hi = la_range
+    log_alpha = torch.rand((N, H), generator=g, device=device, dtype=f32) * (hi - lo) + lo
+    beta = torch.sigmoid(torch.randn((N, H), generator=g, device=device, dtype=f32))
+    conv_w = None
+    if conv:
+        conv_w = torch.rand((H * (2 * dk + dv), 4), generator=g, device=device, dtype=f32) - 0.5
+    cu = torch.zeros(len(prefix_lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(prefix_lens, dtype=torch.int64), 0).to(torch.int32)
+    bcu = torch.zeros(len(branch_lens) + 1, dtype=torch.int32)
+    bcu[1:] = torch.cumsum(torch.tensor(branch_lens, dtype=torch.int64), 0).to(torch.int32)
+    return dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, conv_w=conv_w,
+                cu_seqlens=cu.to(device), branch_cu=bcu.to(device),
+                branch_parent=torch.tensor(branch_parent, dtype=torch.int32, device=device),
+                Np=Np, Nb=Nb, N=N)

@@ -1,0 +1,34 @@
+"""MI355X-native (gfx950) Gated DeltaNet recurrence library.
+
+Thin Python binding over the C ABI of libgdn_mi355x.so (include/gdn_mi355x.h):
+shared-context prefill and forked branches (the two-call GDN fork of the
+Flide page), eager decode, and deferred base + log decode with its merge
+(the DeltaLog page). Tensors are torch device tensors; every step of the
+computation runs in the HIP kernels.
+"""
+
+from ._lib import (  # noqa: F401
+    GDN_BF16,
+    GDN_F32,
+    GDNError,
+    deltalog_append_decode,
+    deltalog_merge,
+    gdn_decode_eager,
+    gdn_fork_branches,
+    gdn_prefill_shared,
+    load,
+    prefill_workspace_bytes,
+    status_string,
+)
+
+__all__ = [
+    "gdn_prefill_shared",
+    "gdn_fork_branches",
+    "gdn_decode_eager",
+    "deltalog_append_decode",
+    "deltalog_merge",
+    "prefill_workspace_bytes",
+    "status_string",
+    "load",
+    "GDNError",
+]

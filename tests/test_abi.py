@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects bad host-side arguments before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_mi355x.h")
+LIB = os.path.join(ROOT, "linear_attention_recurrent_gdn_amd", "libgdn_mi355x.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import linear_attention_recurrent_gdn_amd.build as b
+        b.build()
+    from linear_attention_recurrent_gdn_amd import _lib
+    return _lib.load()
+
+
+def test_header_declares_the_five_operations():
+    names = declared_functions()
+    for op in ["gdn_prefill_shared", "gdn_fork_branches", "gdn_decode_eager",
+               "deltalog_append_decode", "deltalog_merge"]:
+        assert op in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    from linear_attention_recurrent_gdn_amd import _lib
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+        assert n in _lib.SIGNATURES, f"{n} has no binding"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings(lib):
+    assert lib.gdn_status_string(OK) == b"ok"
+    assert b"invalid" in lib.gdn_status_string(INVALID)
+    assert lib.gdn_max_log_capacity() >= 16
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)  # never dereferenced: every call below fails validation first
+NULL = None
+
+
+def eager(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, state=FAKE, slot=NULL, o=FAKE, B=2, H=2,
+             dk=128, dv=128, S=2, var=0, io=1, od=0)
+    a.update(kw)
+    return lib.gdn_decode_eager(a["q"], a["k"], a["v"], a["la"], a["beta"], a["state"], a["slot"],
+                                a["o"], a["B"], a["H"], a["dk"], a["dv"], a["S"], a["var"], a["io"],
+                                a["od"], NULL)
+
+
+def test_decode_validation(lib):
+    assert eager(lib, q=NULL) == INVALID
+    assert eager(lib, beta=NULL) == INVALID          # GDN needs beta
+    assert eager(lib, H=0) == INVALID
+    assert eager(lib, B=-1) == INVALID
+    assert eager(lib, B=3, S=2) == INVALID            # identity slots need B <= n_slots
+    assert eager(lib, var=7) == INVALID
+    assert eager(lib, io=5) == INVALID
+    assert eager(lib, dk=96, dv=96) == UNSUPPORTED
+    assert eager(lib, dk=128, dv=64) == UNSUPPORTED
+
+
+def test_append_validation(lib):
+    def call(Mcap=8, merge_at=8, log_len=FAKE, var=0):
+        return lib.deltalog_append_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          log_len, NULL, FAKE, 2, 2, 128, 128, 2, Mcap, merge_at,
+                                          var, 1, 0, NULL)
+    assert call(log_len=NULL) == INVALID
+    assert call(Mcap=0) == INVALID
+    assert call(merge_at=9) == INVALID
+    assert call(merge_at=-1) == INVALID
+    assert call(Mcap=lib.gdn_max_log_capacity() + 1, merge_at=1) == UNSUPPORTED
+
+
+def test_merge_validation(lib):
+    assert lib.deltalog_merge(NULL, FAKE, FAKE, FAKE, FAKE, NULL, 2, 2, 128, 128, 2, 8, 1, 0, 1,
+                              NULL) == INVALID
+    assert lib.deltalog_merge(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 2, 2, 48, 48, 2, 8, 1, 0, 1,
+                              NULL) == UNSUPPORTED
+
+
+def test_prefill_validation_and_workspace(lib):
+    need = lib.gdn_prefill_workspace_bytes(1000, 3, 4, 128, 128, 64)
+    assert need > 0
+
+    def call(ws=FAKE, ws_bytes=need, chunk=64, final=FAKE, cu=FAKE, d=128):
+        return lib.gdn_prefill_shared(FAKE, FAKE, FAKE, FAKE, FAKE, cu, 3, 1000, 4, d, d, chunk,
+                                      NULL, 0, NULL, NULL, FAKE, final, NULL, 1, 0, ws, ws_bytes,
+                                      NULL)
+    assert call(final=NULL) == INVALID
+    assert call(cu=NULL) == INVALID
+    assert call(chunk=48) == UNSUPPORTED
+    assert call(d=80) == UNSUPPORTED
+    assert call(ws=NULL) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    # fork: the parent state and o are required
+    assert lib.gdn_fork_branches(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 100, 4, 128, 128,
+                                 64, NULL, 0, NULL, NULL, FAKE, NULL, NULL, 1, 0, FAKE, need,
+                                 NULL) == INVALID
