@@ -1,0 +1,366 @@
+"""Benchmark of the GDN decode / fork hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--fork-reps R] [--no-cpu]
+
+Headline workload (one JSON line on stdout): large-batch decode under the
+deferred base + log schedule -- B=256 sequences, H=32 heads, d_k=d_v=128,
+merge every M=8 steps with per-slot log phases (each slot starts with a
+pre-populated log of 0..M-1 entries, so every step merges a different
+eighth of the slots), bf16 q/k/v, fp32 state, fp32 o. A step is one
+deltalog_append_decode launch over the whole batch (8192 head-steps); all
+512 steps of inputs are pre-staged in HBM and the timed region cycles
+through them. `value` is head-steps per second.
+
+Alongside: the eager step on the same workload (state-write ratio and
+speedup), the two-call fork (8 requests x 8192-token contexts, 20 branches
+of 64 tokens each, H=16, d=128, conv width 4) as branches per second, the
+roofline of the deferred kernel from HIP events on its stream, and the fp64
+CPU oracle timed on a bounded sample of the same decode workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public figure
+
+METRIC = "GDN decode head-steps/s + achieved HBM GB/s (DeltaLog M=8); fork branches/s"
+
+# algorithmic bytes of one head-step (d_k = d_v = 128, bf16 q/k/v, fp32 o,
+# fp32 state / log_u / log_lambda, bf16 log_k, scalar decay)
+D = 128
+STATE_B = 4 * D * D                # one fp32 [d_k][d_v] state tile
+QKV_B = 2 * 3 * D                  # bf16 q, k, v
+SCAL_B = 4 + 4                     # log_alpha, beta
+O_B = 4 * D                        # fp32 o
+LEN_B = 4 + 4                      # log length read + write
+ENTRY_B = 4 * D + 2 * D + 4        # one log entry: u (fp32), k (bf16), Lambda (fp32)
+
+
+def deferred_bytes(m, merges):
+    """Bytes one head-step moves under the deferred schedule with m logged
+    entries: base read, inputs, replay of m entries, o, and either a base
+    write (merging step) or one appended entry."""
+    return (STATE_B + QKV_B + SCAL_B + O_B + LEN_B + ENTRY_B * m
+            + (STATE_B if merges else ENTRY_B))
+
+
+def eager_bytes():
+    return 2 * STATE_B + QKV_B + SCAL_B + O_B
+
+
+def state_write_bytes(merges):
+    """Bytes of recurrent state written per head-step: base and log."""
+    return STATE_B if merges else ENTRY_B
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--fork-reps", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-fork", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.stream)
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+# ---------------------------------------------------------------- decode
+def setup_decode(torch, gdn, gi, B=256, H=32, steps=512, M=8, seed=0):
+    dev = "cuda"
+    t = gi.torch_decode_inputs(B, H, D, D, steps, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    phase = rng.integers(0, M, size=B)
+    lengths = np.repeat(phase, H)
+    ent = gi.log_entries(rng, B * H, M, D, D, lengths, io="bf16")
+    logs = dict(
+        log_u=torch.from_numpy(ent["u"]).to(dev).view(B, H, M, D),
+        log_k=torch.from_numpy(ent["k_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        .view(B, H, M, D),
+        log_lam=torch.from_numpy(ent["lam"]).to(dev).view(B, H, M),
+        log_len=torch.from_numpy(lengths.astype(np.int32)).to(dev).view(B, H),
+    )
+    return t, logs, phase
+
+
+def run_deferred(torch, gdn, t, logs, base, o, M, steps_range):
+    S = t["q"].shape[0]
+    for i in steps_range:
+        s = i % S
+        gdn.deltalog_append_decode(t["q"][s], t["k"][s], t["v"][s], t["log_alpha"][s],
+                                   t["beta"][s], base, logs["log_u"], logs["log_k"],
+                                   logs["log_lam"], logs["log_len"], o, merge_at=M)
+
+
+def run_eager(torch, gdn, t, state, o, steps_range):
+    S = t["q"].shape[0]
+    for i in steps_range:
+        s = i % S
+        gdn.gdn_decode_eager(t["q"][s], t["k"][s], t["v"][s], t["log_alpha"][s], t["beta"][s],
+                             state, o)
+
+
+def schedule_bytes(phase, H, M, first, K):
+    """Exact algorithmic bytes of K deferred steps starting at step `first`,
+    from the deterministic per-slot log lengths; plus state-write bytes."""
+    m = np.asarray(phase, dtype=np.int64).copy()
+    for _ in range(first):
+        m = np.where(m + 1 >= M, 0, m + 1)
+    total = 0
+    writes = 0
+    for _ in range(K):
+        merges = m + 1 >= M
+        total += int(sum(deferred_bytes(int(mi), bool(mg)) for mi, mg in zip(m, merges))) * H
+        writes += int(sum(state_write_bytes(bool(mg)) for mg in merges)) * H
+        m = np.where(merges, 0, m + 1)
+    return total, writes
+
+
+# ---------------------------------------------------------------- fork
+def bench_fork(torch, gdn, gi, reps):
+    w = gi.WORKLOADS["fork_prefill"]
+    R, H, d = w["R"], w["H"], w["d"]
+    pl, bl, par = gi.fork_layout(R, w["prefix"], w["branches_per_req"], w["branch_len"])
+    t = gi.torch_seq_inputs(pl, bl, par, H, d, d, conv=True, seed=0)
+    Np, Nb, NB = t["Np"], t["Nb"], len(bl)
+    cc = H * 3 * d
+    dev = "cuda"
+    st = torch.empty((R, H, d, d), device=dev)
+    win = torch.empty((R, 3, cc), device=dev, dtype=torch.bfloat16)
+    o_p = torch.empty((Np, H, d), device=dev)
+    o_b = torch.empty((Nb, H, d), device=dev)
+    ws = torch.empty(max(gdn.prefill_workspace_bytes(max(Np, Nb), max(R, NB), H, d, d), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        gdn.gdn_prefill_shared(t["q"][:Np], t["k"][:Np], t["v"][:Np], t["log_alpha"][:Np],
+                               t["beta"][:Np], t["cu_seqlens"], st, o=o_p, conv_w=t["conv_w"],
+                               qk_l2norm=True, final_window=win, workspace=ws)
+
+    def fork():
+        gdn.gdn_fork_branches(t["q"][Np:], t["k"][Np:], t["v"][Np:], t["log_alpha"][Np:],
+                              t["beta"][Np:], t["branch_cu"], t["branch_parent"], st, o_b,
+                              parent_window=win, conv_w=t["conv_w"], qk_l2norm=True,
+                              workspace=ws)
+
+    prefill()
+    fork()
+    tp, tf = [], []
+    for _ in range(reps):
+        with Timer(torch, stream) as a:
+            prefill()
+        with Timer(torch, stream) as b:
+            fork()
+        tp.append(a.ms)
+        tf.append(b.ms)
+    tp_ms, tf_ms = float(np.median(tp)), float(np.median(tf))
+    return dict(branches=NB, prefill_ms=tp_ms, fork_ms=tf_ms,
+                branches_per_s=NB / ((tp_ms + tf_ms) / 1e3),
+                branch_phase_branches_per_s=NB / (tf_ms / 1e3),
+                prefix_token_heads_per_s=Np * H / (tp_ms / 1e3))
+
+
+# ---------------------------------------------------------------- HBM probe
+def hbm_probe(torch, stream, nbytes=4 << 30, reps=5):
+    """Attainable HBM bandwidth on this GPU: a plain device copy (read +
+    write nbytes each) and a read-only sum over nbytes, best of reps."""
+    n = nbytes // 4
+    a = torch.rand(n, device="cuda")
+    b = torch.empty_like(a)
+    copy, read = [], []
+    b.copy_(a)
+    a.sum()
+    for _ in range(reps):
+        with Timer(torch, stream) as t:
+            b.copy_(a)
+        copy.append(2 * nbytes / (t.ms / 1e3) / 1e9)
+        with Timer(torch, stream) as t:
+            a.sum()
+        read.append(nbytes / (t.ms / 1e3) / 1e9)
+    del a, b
+    return dict(copy_gbps=max(copy), read_gbps=max(read), bytes=nbytes)
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(torch, t, target_s):
+    """The fp64 oracle (plain step-by-step recurrence) on a bounded sample
+    of the decode workload: the first b sequences (all heads, all staged
+    steps), b chosen from a calibration run to take about target_s."""
+    import oracle
+
+    steps, B, H = t["q"].shape[:3]
+
+    def sample(b, nsteps):
+        host = lambda x: x[:nsteps, :b].float().cpu().numpy().astype(np.float64)  # noqa: E731
+        return (host(t["q"]), host(t["k"]), host(t["v"]), host(t["log_alpha"]), host(t["beta"]),
+                t["state0"][:b].cpu().numpy().astype(np.float64))
+
+    threads = oracle.max_threads()
+    q, k, v, la, be, s0 = sample(2, 64)
+    t0 = time.perf_counter()
+    oracle.decode(q, k, v, la, be, s0, nthreads=threads)
+    rate = 2 * H * 64 / (time.perf_counter() - t0)
+    b = int(max(1, min(B, target_s * rate / (H * steps))))
+    q, k, v, la, be, s0 = sample(b, steps)
+    t0 = time.perf_counter()
+    oracle.decode(q, k, v, la, be, s0, nthreads=threads)
+    dt = time.perf_counter() - t0
+    hs = b * H * steps
+    return dict(value=hs / dt, unit="head-steps/s", cores=threads, kind="oracle",
+                sample=f"{b} of {B} sequences x {H} heads x {steps} steps ({hs} head-steps, "
+                       f"plain fp64 recurrence, {dt:.1f} s)")
+
+
+def measured_traffic(ms_per_launch):
+    """HBM bytes per launch of the deferred kernel from the committed
+    counter summary (two rocprofv3 --pmc passes, copy-calibrated), or None
+    when the decode sources changed since the counters were taken."""
+    from linear_attention_recurrent_gdn_amd import profiling
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    prof = profiling.read_profile_block(os.path.join(here, "profiles", "decode_large_traffic.md"))
+    if not prof or prof.get("source_hash") != profiling.source_hash(profiling.DECODE_SOURCES):
+        return None, None
+    t = prof["traffic_bytes"]
+    return t, t / (ms_per_launch / 1e3) / 1e9
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); decode slot-heads "
+              "and fork requests shard across GPUs with no exchange, so a multi-GPU run is "
+              "not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gdn_inputs as gi
+    import linear_attention_recurrent_gdn_amd as gdn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gdn.load()
+    torch.manual_seed(0)
+    B, H, M, NSTEP = 256, 32, 8, 512
+    K, W = args.steps, args.warmup
+    stream = torch.cuda.current_stream()
+
+    log("staging decode inputs ...")
+    t, logs, phase = setup_decode(torch, gdn, gi, B, H, NSTEP, M)
+    base = t["state0"].clone()
+    o = torch.empty((B, H, D), device="cuda")
+
+    log(f"deferred decode: {W} warmup + {K} timed steps")
+    run_deferred(torch, gdn, t, logs, base, o, M, range(W))
+    with Timer(torch, stream) as tm:
+        run_deferred(torch, gdn, t, logs, base, o, M, range(W, W + K))
+    ms_step = tm.ms / K
+    head_steps = B * H * K
+    value = head_steps / (tm.ms / 1e3)
+    alg_bytes, state_writes = schedule_bytes(phase, H, M, W, K)
+    achieved = alg_bytes / (tm.ms / 1e3) / 1e9
+    traffic, traffic_gbps = measured_traffic(ms_step)
+
+    log("eager decode on the same workload")
+    state = t["state0"].clone()
+    run_eager(torch, gdn, t, state, o, range(W))
+    with Timer(torch, stream) as te:
+        run_eager(torch, gdn, t, state, o, range(W, W + K))
+    eager_value = head_steps / (te.ms / 1e3)
+    eager_gbps = eager_bytes() * head_steps / (te.ms / 1e3) / 1e9
+    eager_writes = STATE_B * head_steps
+
+    fork = None
+    if not args.no_fork:
+        log("two-call fork ...")
+        fork = bench_fork(torch, gdn, gi, args.fork_reps)
+
+    probe = hbm_probe(torch, stream)
+
+    cpu = None
+    if not args.no_cpu:
+        log("CPU oracle baseline ...")
+        cpu = cpu_baseline(torch, t, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_large: deferred base+log decode, B=256, H=32, d_k=d_v=128, "
+                        "merge every M=8 steps with per-slot log phases, bf16 q/k/v, fp32 "
+                        "state and o, 512 pre-staged steps",
+            "B": B, "H": H, "d_k": D, "d_v": D, "M": M, "io": "bf16", "state": "f32",
+        },
+        "hbm_gbps_effective": achieved,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel<128,128,GDN,bf16,f32,append>",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
+            "traffic_gbps": traffic_gbps,
+            "bytes_per_launch": alg_bytes / K,
+            "launch_ms": ms_step,
+        },
+        "eager": {"value": eager_value, "unit": "head-steps/s", "ms_per_step": te.ms / K,
+                  "hbm_gbps_effective": eager_gbps,
+                  "speedup_deferred_vs_eager": value / eager_value},
+        "state_write_bytes_per_head_step": {
+            "deferred": state_writes / head_steps, "eager": eager_writes / head_steps,
+            "ratio": eager_writes / state_writes},
+        "fork": fork,
+        "hbm_probe": probe,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

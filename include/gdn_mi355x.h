@@ -200,7 +200,7 @@ int gdn_decode_eager(const void *q, const void *k, const void *v,
  *  log_lambda [n_slots, H, Mcap] (GDN_SCALAR) or [n_slots, H, Mcap, d_k] fp32
  *  log_len    [n_slots, H] int32 device, in/out; values outside [0, Mcap]
  *             are clamped into it
- *  Mcap       1 .. gdn_max_log_capacity();  merge_at 0 .. Mcap
+ *  Mcap       1 .. gdn_max_log_capacity() (16);  merge_at 0 .. Mcap
  *  other arguments as gdn_decode_eager.
  */
 int deltalog_append_decode(const void *q, const void *k, const void *v,

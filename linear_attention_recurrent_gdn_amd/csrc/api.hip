@@ -12,7 +12,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kMaxLog = 64;
+constexpr int kMaxLog = 16;  // log capacity the decode kernels hold on chip
 
 bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 bool dtype_ok(int t) { return t == GDN_F32 || t == GDN_BF16; }

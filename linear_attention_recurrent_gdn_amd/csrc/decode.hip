@@ -45,6 +45,19 @@ constexpr int kWaves = kThreads / kWave;
 
 enum Mode { kEager = 0, kAppend = 1, kMergeOnly = 2 };
 
+// Entries a log may hold: the whole log of a slot-head is prefetched into
+// registers with the base stream, so its capacity is a compile-time bound.
+constexpr int kMaxLog = 16;
+
+// Sum over aligned groups of SEG lanes (SEG a power of two <= 64); every
+// lane of a group ends with the group total.
+template <int SEG>
+__device__ __forceinline__ float wave_sum_seg(float x) {
+#pragma unroll
+    for (int off = 1; off < SEG; off <<= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
 // Thread -> (row, float4 column) map of one [DK][DV] fp32 tile.
 template <int DK, int DV>
 struct TileMap {
@@ -60,12 +73,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     using Map = TileMap<DK, DV>;
     constexpr bool kPerKey = VAR != kScalar;
     constexpr bool kDelta = VAR != kRwkv6;
-    constexpr int LS = kPerKey ? DK : 1;  // log-decay entries per log slot
+    constexpr int LS = kPerKey ? DK : 1;                 // log-decay values per log entry
+    constexpr int ML = MODE == kEager ? 0 : kMaxLog;     // log entries held on chip
+    constexpr int NKE = ML ? (ML * DK + kThreads - 1) / kThreads : 1;  // key-side elems/thread
+    constexpr int NUE = ML ? (ML * DV + kThreads - 1) / kThreads : 1;  // value-side elems/thread
+    constexpr int SEG = DK < kWave ? DK : kWave;         // lanes summing one key range
+    constexpr int NSEG = DK / SEG;                       // partial sums per key vector
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK], s_lam[DK];
     __shared__ float s_red[kWaves][2][DV];
-    __shared__ float s_dt;
-    extern __shared__ float s_dyn[];
+    __shared__ float s_cpart[ML + 1][NSEG], s_dpart[ML + 1][NSEG], s_dtpart[NSEG];
+    __shared__ float s_kt[(ML + 1) * DK];  // k~_e (per-key decay) or k_e (scalar), merging steps
+    __shared__ float s_u[(ML + 1) * DV];   // u_e
+    __shared__ float s_fac[ML + 1];        // scalar decay: exp(Lam_t - Lam_e)
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -83,86 +103,111 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const size_t sh = (size_t)slot * a.H + h;  // slot-head
     float *S = a.state + sh * DK * DV;
     const int Mcap = a.Mcap;
-
-    int m = 0;
-    bool merge = true;
-    if (MODE != kEager) {
-        m = min(max(a.log_len[sh], 0), Mcap);
-        if (MODE == kAppend)
-            merge = (a.merge_at > 0 && m + 1 >= a.merge_at) || m >= Mcap;
-        else
-            merge = m > 0 && m >= a.min_len;
-    }
-    if (!merge && MODE == kMergeOnly) return;
-
-    const int nl = Mcap + 1;
-    float *s_c = s_dyn;              // [nl] replay coefficient <k~_e, k>
-    float *s_d = s_c + nl;           // [nl] replay coefficient <k~_e, q>
-    float *s_kt = s_d + nl;          // [nl][DK] k~_e (merging steps)
-    float *s_u = s_kt + nl * DK;     // [nl][DV] u_e   (merging steps)
-
     const float *lam_log = MODE != kEager ? a.log_lam + sh * Mcap * LS : nullptr;
     const TI *logk = MODE != kEager ? static_cast<const TI *>(a.log_k) + sh * Mcap * DK : nullptr;
     float *logu = MODE != kEager ? a.log_u + sh * Mcap * DV : nullptr;
 
-    // ---------------------------------------------------------- ReplayPrep
-    for (int i = tid; i < DK; i += kThreads) {
-        float lam = 0.f;
-        if (MODE != kEager && m > 0) lam = lam_log[(m - 1) * LS + (kPerKey ? i : 0)];
-        if (MODE != kMergeOnly) {
-            const float *la = a.log_alpha + (size_t)row * LS;
-            lam = lam + la[kPerKey ? i : 0];
-            s_k[i] = to_f32(static_cast<const TI *>(a.k)[(size_t)row * DK + i]);
-            s_q[i] = to_f32(static_cast<const TI *>(a.q)[(size_t)row * DK + i]);
-        }
-        s_lam[i] = lam;
-        s_a[i] = expf(lam);
-    }
-    __syncthreads();
-
-    for (int e = wave; e < m; e += kWaves) {
-        float pc = 0.f, pd = 0.f;
-        const float lam_e_s = kPerKey ? 0.f : lam_log[e];
-        for (int i = lane; i < DK; i += kWave) {
-            const float lam_e = kPerKey ? lam_log[e * LS + i] : lam_e_s;
-            const float kt = to_f32(logk[(size_t)e * DK + i]) * expf(s_lam[i] - lam_e);
-            if (MODE != kMergeOnly) {
-                pc = fmaf(kt, s_k[i], pc);
-                pd = fmaf(kt, s_q[i], pd);
-            }
-            if (merge) s_kt[e * DK + i] = kt;
-        }
-        if (MODE != kMergeOnly) {
-            pc = wave_sum(pc);
-            pd = wave_sum(pd);
-            if (lane == 0) {
-                s_c[e] = pc;
-                s_d[e] = pd;
-            }
-        }
-    }
-    if (MODE != kMergeOnly) {
-        if (wave == kWaves - 1) {
-            float p = 0.f;
-            for (int i = lane; i < DK; i += kWave) p = fmaf(s_k[i], s_q[i], p);
-            p = wave_sum(p);
-            if (lane == 0) s_dt = p;
-        }
-        if (merge)
-            for (int i = tid; i < DK; i += kThreads) s_kt[m * DK + i] = s_k[i];
-    } else {
-        for (int idx = tid; idx < m * DV; idx += kThreads) s_u[idx] = logu[idx];
-    }
-
-    // ---------------------------------------------------------- stream base
+    // ---- one round trip. The base stream is issued first; everything else
+    // is a small branch-free load behind it (addresses clamped in bounds,
+    // conversions deferred), so no wait can fall between the base loads. The
+    // log length is uniform and comes through the scalar path, so the log
+    // entries that depend on it are issued while the base is in flight.
     const int col = (tid % Map::TPR) * 4;
     const int r0 = tid / Map::TPR;
     float4 reg[Map::P];
 #pragma unroll
     for (int p = 0; p < Map::P; ++p)
-        reg[p] = *reinterpret_cast<const float4 *>(S + (size_t)(r0 + p * Map::RPP) * DV + col);
-    __syncthreads();  // ReplayPrep results visible
+        reg[p] = load_stream(S + (size_t)(r0 + p * Map::RPP) * DV + col);
 
+    int m_raw = 0;
+    if (MODE != kEager) m_raw = a.log_len[sh];
+    const int ik = min(tid, DK - 1), iv = min(tid, DV - 1);
+    TI k_raw{}, q_raw{}, v_raw{};
+    float lax = 0.f, bx = 1.f;
+    if (MODE != kMergeOnly) {
+        k_raw = static_cast<const TI *>(a.k)[(size_t)row * DK + ik];
+        q_raw = static_cast<const TI *>(a.q)[(size_t)row * DK + ik];
+        v_raw = static_cast<const TI *>(a.v)[(size_t)row * DV + iv];
+        lax = a.log_alpha[(size_t)row * LS + (kPerKey ? ik : 0)];
+        if (kDelta) bx = a.beta[row];
+    }
+
+    const int m = MODE == kEager ? 0 : min(max(m_raw, 0), Mcap);
+    bool merge = true;
+    if (MODE == kAppend) merge = (a.merge_at > 0 && m + 1 >= a.merge_at) || m >= Mcap;
+    if (MODE == kMergeOnly) merge = m > 0 && m >= a.min_len;
+    if (!merge && MODE == kMergeOnly) return;
+
+    const int e_last = max(m - 1, 0);  // a valid entry index for clamped loads
+    float lam_prev = 0.f, lam_e_s = 0.f;
+    TI kl_raw[NKE];
+    float ll[kPerKey ? NKE : 1], ul[NUE];
+    if (MODE != kEager) {
+        lam_prev = lam_log[e_last * LS + (kPerKey ? ik : 0)];
+        if (!kPerKey) lam_e_s = lam_log[min(tid, e_last)];
+#pragma unroll
+        for (int r = 0; r < NKE; ++r) {
+            const int idx = tid + r * kThreads, e = min(idx / DK, e_last), i = idx % DK;
+            kl_raw[r] = logk[(size_t)e * DK + i];
+            if (kPerKey) ll[r] = lam_log[e * LS + i];
+        }
+#pragma unroll
+        for (int r = 0; r < NUE; ++r) {
+            const int idx = tid + r * kThreads, e = min(idx / DV, e_last), j = idx % DV;
+            ul[r] = logu[e * DV + j];
+        }
+    }
+    if (m == 0) lam_prev = 0.f;
+    const float kx = to_f32(k_raw), qx = to_f32(q_raw), vx = to_f32(v_raw);
+
+    // ---- ReplayPrep (key side, once per slot-head)
+    if (tid < DK) {
+        const float lam = MODE == kMergeOnly ? lam_prev : lam_prev + lax;
+        s_lam[tid] = lam;
+        s_a[tid] = expf(lam);
+        s_k[tid] = kx;
+        s_q[tid] = qx;
+    }
+    if (!kPerKey && tid < m) s_fac[tid] = lam_e_s;  // Lam_e, turned into a factor below
+    if (MODE != kMergeOnly) {  // k . q
+        float p = wave_sum_seg<SEG>(kx * qx);
+        if (tid < DK && lane % SEG == 0) s_dtpart[tid / SEG] = p;
+    }
+    __syncthreads();
+    if (!kPerKey && tid < m) s_fac[tid] = expf(s_lam[0] - s_fac[tid]);  // exp(Lam_t - Lam_e)
+    if (ML > 0) {
+#pragma unroll
+        for (int r = 0; r < NKE; ++r) {
+            const int idx = tid + r * kThreads, e = idx / DK, i = idx % DK;
+            float pc = 0.f, pd = 0.f;
+            if (e < m) {
+                // per-key: fold the decay ratio into k~ here; scalar: it
+                // factors out of the sums and is applied per entry
+                const float kl = to_f32(kl_raw[r]);
+                const float kt = kPerKey ? kl * expf(s_lam[i] - ll[r]) : kl;
+                pc = kt * s_k[i];
+                pd = kt * s_q[i];
+                if (merge) s_kt[e * DK + i] = kt;
+            }
+            if (MODE != kMergeOnly) {
+                pc = wave_sum_seg<SEG>(pc);
+                pd = wave_sum_seg<SEG>(pd);
+                if (e < m && lane % SEG == 0) {
+                    s_cpart[e][i / SEG] = pc;
+                    s_dpart[e][i / SEG] = pd;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NUE; ++r) {
+            const int idx = tid + r * kThreads, e = idx / DV;
+            if (e < m) s_u[idx] = ul[r];
+        }
+    }
+    if (MODE != kMergeOnly && merge && tid < DK) s_kt[m * DK + tid] = kx;
+    if (!kPerKey) __syncthreads();  // s_fac ready for the value columns and the merge
+
+    // ---- AppendDecode: S^T k^ and S^T q^ over the key rows
     if (MODE != kMergeOnly) {
         float ax[4] = {0.f, 0.f, 0.f, 0.f}, ao[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -191,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         }
         __syncthreads();
 
-        // ------------------------------------------------------ AppendDecode
+        // the value columns: replay the log, form u, o; append or stage
         if (tid < DV) {
             const int j = tid;
             float x = 0.f, oo = 0.f;
@@ -201,32 +246,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
                 oo += s_red[w][1][j];
             }
             for (int e = 0; e < m; ++e) {
-                const float ue = logu[e * DV + j];
-                x = fmaf(s_c[e], ue, x);
-                oo = fmaf(s_d[e], ue, oo);
-                if (merge) s_u[e * DV + j] = ue;
+                float c = 0.f, d = 0.f;
+#pragma unroll
+                for (int g = 0; g < NSEG; ++g) {
+                    c += s_cpart[e][g];
+                    d += s_dpart[e][g];
+                }
+                if (!kPerKey) {
+                    c *= s_fac[e];
+                    d *= s_fac[e];
+                }
+                const float ue = s_u[e * DV + j];
+                x = fmaf(c, ue, x);
+                oo = fmaf(d, ue, oo);
             }
-            const float vj = to_f32(static_cast<const TI *>(a.v)[(size_t)row * DV + j]);
-            const float u = kDelta ? a.beta[row] * (vj - x) : vj;
-            oo = fmaf(s_dt, u, oo);
+            float dt = 0.f;
+#pragma unroll
+            for (int g = 0; g < NSEG; ++g) dt += s_dtpart[g];
+            const float u = kDelta ? bx * (vx - x) : vx;
+            oo = fmaf(dt, u, oo);
             static_cast<TO *>(a.o)[(size_t)row * DV + j] = from_f32<TO>(oo);
             if (merge)
                 s_u[m * DV + j] = u;
             else
                 logu[m * DV + j] = u;
         }
-        if (MODE == kAppend && !merge) {
-            TI *lk = static_cast<TI *>(a.log_k) + (sh * Mcap + m) * DK;
-            for (int i = tid; i < DK; i += kThreads) {
-                lk[i] = static_cast<const TI *>(a.k)[(size_t)row * DK + i];
-                if (kPerKey) a.log_lam[(sh * Mcap + m) * DK + i] = s_lam[i];
-            }
-            if (!kPerKey && tid == 0) a.log_lam[sh * Mcap + m] = s_lam[0];
+        if (MODE == kAppend && !merge && tid < DK) {
+            static_cast<TI *>(a.log_k)[(sh * Mcap + m) * DK + tid] = k_raw;
+            if (kPerKey) a.log_lam[(sh * Mcap + m) * DK + tid] = s_lam[tid];
+            else if (tid == 0) a.log_lam[sh * Mcap + m] = s_lam[0];
         }
     }
     if (MODE != kEager && tid == 0) a.log_len[sh] = merge ? 0 : m + 1;
 
-    // ---------------------------------------------------------- merge
+    // ---- merge: base <- diag(exp Lam) base + sum_e k~_e u_e^T (base still in registers)
     if (merge) {
         __syncthreads();
         const int ne = MODE == kMergeOnly ? m : m + 1;
@@ -236,26 +289,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             const float ar = s_a[r];
             float v0 = reg[p].x * ar, v1 = reg[p].y * ar, v2 = reg[p].z * ar, v3 = reg[p].w * ar;
             for (int e = 0; e < ne; ++e) {
-                const float kt = s_kt[e * DK + r];
+                const float kt = (!kPerKey && e < m) ? s_kt[e * DK + r] * s_fac[e] : s_kt[e * DK + r];
                 const float4 ue = *reinterpret_cast<const float4 *>(s_u + e * DV + col);
                 v0 = fmaf(kt, ue.x, v0);
                 v1 = fmaf(kt, ue.y, v1);
                 v2 = fmaf(kt, ue.z, v2);
                 v3 = fmaf(kt, ue.w, v3);
             }
-            *reinterpret_cast<float4 *>(S + (size_t)r * DV + col) = make_float4(v0, v1, v2, v3);
+            store_stream(S + (size_t)r * DV + col, make_float4(v0, v1, v2, v3));
         }
     }
 }
 
 template <int D, int VAR, typename TI, typename TO, int MODE>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
-    const int nl = (MODE == kEager ? 0 : a.Mcap) + 1;
-    const size_t lds = sizeof(float) * ((size_t)2 * nl + (size_t)nl * (D + D));
     const int blocks = a.B * a.H;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<D, D, VAR, TI, TO, MODE>), dim3(blocks), dim3(kThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, D, VAR, TI, TO, MODE>), dim3(blocks), dim3(kThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

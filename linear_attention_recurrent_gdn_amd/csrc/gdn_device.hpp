@@ -51,6 +51,21 @@ __device__ __forceinline__ float wave_sum(float x) { return wave_sum_strided<1>(
 
 __device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7fc00000u); }
 
+// Streaming (non-temporal) 16-byte load / store for data touched once per
+// launch: the state tiles of the decode step. Keeps the caches for data that
+// is re-read (logs, inputs).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream(const float *p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(float *p, float4 x) {
+    f32x4 v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+
 // ---------------------------------------------------------------- launch API
 enum Variant { kScalar = 0, kKda = 1, kRwkv6 = 2 };
 enum DType { kF32 = 0, kBF16 = 1 };
