@@ -16,7 +16,7 @@
 // Sig0 (= S0^T, [d_k][d_v]), g_r = running sum of log a inside the chunk,
 // gamma_r = exp(g_r):
 //   A[r][s] = beta_r exp(g_r - g_s) <k_r, k_s>            (s < r)
-//   T = (I + A)^-1 (unit lower triangular),  T' = T diag(beta)
+//   T' = (I + A)^-1 diag(beta)
 //   P[r][s] = exp(g_r - g_s) <q_r, k_s>                    (s <= r)
 //   U = T' (V - diag(gamma) K Sig0)       the chunk's rank-1 factors u_r
 //   O = diag(gamma) Q Sig0 + P U          o_r = S_r q_r
@@ -24,16 +24,24 @@
 // Column j of U, O, Sig depends only on column j of V and Sig0, so value
 // tiles are independent.
 //
+// Every contraction runs on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16)
+// with split-bf16 operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi),
+// and a.b ~ hi.hi + hi.lo + lo.hi accumulated in fp32 -- about 2^-16
+// relative per product, where a single bf16 product (2^-9) would not meet a
+// 2e-3 end-to-end tolerance.
+//
 // Kernels:
 //   plan  -- one workgroup: per-sequence chunk offsets (prefix sum of
 //            ceil(len/C)) into the workspace, from the device offsets.
 //   prep  -- one workgroup per (chunk, head), all chunks in parallel: conv
-//            + q/k norm of the chunk, then T' and P (key-side only) to the
-//            workspace.
-//   scan  -- one workgroup per (sequence, head, value tile of 32): walks the
-//            sequence's chunks in order with the state tile resident in LDS,
-//            recomputing the chunk's conv'd q/k/v and applying the chunk
-//            form; writes o, the final state tile and (tile 0) the window.
+//            + q/k norm of the chunk rows, KK^T and QK^T on MFMA, then
+//            T = (I + A)^-1 by per-column forward substitution; writes T'
+//            and P to the workspace.
+//   scan  -- one workgroup per (sequence, head, 32-wide value tile): walks
+//            the sequence's chunks in order. Each of its 4 waves owns 16
+//            chunk rows: it forms the conv'd, normalised K and Q rows
+//            directly in MFMA operand registers, and the state tile Sig^T
+//            [32][d_k] stays in LDS across chunks.
 
 #include <type_traits>
 
@@ -45,26 +53,74 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int C = 64;        // chunk length
-constexpr int CP = C + 4;    // padded row of a transposed [d][C] tile
 constexpr int TV = 32;       // value-tile width of the scan
+constexpr int RB = 16;       // chunk rows per wave
 constexpr float kNormEps = 1e-6f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ split-bf16 MFMA
+struct Split8 {
+    bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ Split8 split8(const float (&x)[8]) {
+    Split8 s;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)x[e];
+        s.hi[e] = h;
+        s.lo[e] = (__bf16)(x[e] - (float)h);
+    }
+    return s;
+}
+
+// c += a . b for 16x16 tiles with K = 32, fp32-faithful via three products
+__device__ __forceinline__ f32x4v mma3(const Split8 &a, const Split8 &b, f32x4v c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// 8 consecutive io-dtype values as fp32 (16-byte aligned)
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16 *p, float (&x)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
 
 // ------------------------------------------------------------ workspace
 struct WsLayout {
-    size_t chunk_start_off;  // int32 [n_seq + 1]
-    size_t rec_off;          // per (chunk, head) record
-    size_t rec_floats;       // T'^T [C][C], P^T [C][C], g [C]
+    size_t rec_off;     // per (chunk, head) record: T' [C][C], P [C][C] (row-major)
+    size_t rec_floats;
     size_t max_chunks;
     size_t total;
 };
 
 __host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H) {
     WsLayout w{};
-    auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
     w.max_chunks = (size_t)n_tokens / C + (size_t)n_seq;
-    w.chunk_start_off = 0;
-    w.rec_off = align(sizeof(int32_t) * ((size_t)n_seq + 1));
-    w.rec_floats = 2 * (size_t)C * C + C;
+    w.rec_off = ((sizeof(int32_t) * ((size_t)n_seq + 1)) + 255) & ~size_t(255);
+    w.rec_floats = 2 * (size_t)C * C;
     w.total = w.rec_off + sizeof(float) * w.rec_floats * w.max_chunks * (size_t)H;
     return w;
 }
@@ -112,59 +168,6 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n
     if (tid == kThreads - 1) chunk_start[n_seq] = (int32_t)min(run, max_chunks);
 }
 
-// ------------------------------------------------------------ conv + norm
-// Conv'd inputs of one part (q, k or v) of head h for the chunk rows
-// l < L, columns [d_begin, d_begin + W) of the part (head size D), written
-// to dst[d * ld + l] (transposed) or dst[l * ld + d]; rows l >= L are zero.
-// Position p of the sequence reads x[(seq0 + p)] for p >= 0, else row 3+p
-// of the incoming window (zeros without one).
-template <typename TI, bool TRANSPOSED>
-__device__ void conv_part(const TI *x, int H, int D, int h, int d_begin, int W, int seq0, int p0,
-                          int L, const TI *win, int CC, int cbase, const float *w, float *dst,
-                          int ld) {
-    for (int idx = threadIdx.x; idx < C * W; idx += kThreads) {
-        const int d = idx % W, l = idx / W;
-        float y = 0.f;
-        if (l < L) {
-            const int c = cbase + h * D + d_begin + d;  // channel in [q | k | v]
-            const size_t col = (size_t)h * D + d_begin + d;
-            if (w) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = p0 + l - 3 + r;
-                    float xv;
-                    if (p >= 0)
-                        xv = to_f32(x[(size_t)(seq0 + p) * H * D + col]);
-                    else
-                        xv = win ? to_f32(win[(size_t)(3 + p) * CC + c]) : 0.f;
-                    y = fmaf(w[(size_t)c * 4 + r], xv, y);
-                }
-            } else {
-                y = to_f32(x[(size_t)(seq0 + p0 + l) * H * D + col]);
-            }
-        }
-        dst[TRANSPOSED ? d * ld + l : l * ld + d] = y;
-    }
-}
-
-// L2-normalise the C rows of a transposed [D][ld] tile in place.
-template <int D>
-__device__ void norm_rows_transposed(float *t, int ld, float *s_inv) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    for (int l = wave; l < C; l += kWaves) {
-        float ss = 0.f;
-        for (int d = lane; d < D; d += kWave) ss = fmaf(t[d * ld + l], t[d * ld + l], ss);
-        ss = wave_sum(ss);
-        if (lane == 0) s_inv[l] = 1.0f / sqrtf(ss + kNormEps);
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < C * D; idx += kThreads) {
-        const int d = idx / C, l = idx % C;
-        t[d * ld + l] *= s_inv[l];
-    }
-    __syncthreads();
-}
-
 __device__ __forceinline__ int find_seq(const int32_t *chunk_start, int n_seq, int gc) {
     int lo = 0, hi = n_seq;  // last s in [0, n_seq) with chunk_start[s] <= gc
     while (hi - lo > 1) {
@@ -175,12 +178,128 @@ __device__ __forceinline__ int find_seq(const int32_t *chunk_start, int n_seq, i
     return lo;
 }
 
+// ------------------------------------------------------------ chunk inputs
+// Where a chunk's tokens live: sequence start in the stream, position of the
+// chunk's first token in the sequence, live rows, incoming window.
+template <typename TI>
+struct ChunkSrc {
+    int seq0, p0, L;
+    const TI *win;  // [3][CC] or null (zeros)
+};
+
+// Running sum of log a over the chunk rows, one row per lane (rows >= L add
+// nothing): lane l returns g_l. A wave-wide inclusive scan, shared by the
+// prep and scan kernels so both see identical g.
+__device__ __forceinline__ float chunk_g(const float *log_alpha, int H, int h, int seq0, int p0,
+                                         int L) {
+    const int lane = threadIdx.x % kWave;
+    float g = lane < L ? log_alpha[(size_t)(seq0 + p0 + lane) * H + h] : 0.f;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(g, off, kWave);
+        if (lane >= off) g += o;
+    }
+    return g;
+}
+
+// Conv'd (and, for q / k, normalised) rows rb*16 .. rb*16+15 of the chunk in
+// the A-operand layout of a 16x16x32 MFMA: lane l holds row rb*16 + l%16,
+// columns ks*32 + (l/16)*8 + e for ks < D/32, e < 8. Rows >= L are zero.
+// x is the [N][H][D] stream of this part; cbase its first channel in the
+// [q | k | v] concatenation of CC channels.
+template <int D, typename TI>
+__device__ void rows_afrag(const TI *x, int H, int h, const ChunkSrc<TI> &cs, int rb, int CC,
+                           int cbase, const float *w, bool norm, float (&out)[D / 32][8]) {
+    const int lane = threadIdx.x % kWave;
+    const int row = rb * RB + lane % 16;
+    const int cq = (lane / 16) * 8;
+    const bool live = row < cs.L;
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        const int d0 = ks * 32 + cq;
+        float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            if (w) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int p = cs.p0 + row - 3 + r;
+                    float xv[8];
+                    if (p >= 0) {
+                        load8(x + (size_t)(cs.seq0 + p) * H * D + (size_t)h * D + d0, xv);
+                    } else if (cs.win) {
+                        load8(cs.win + (size_t)(3 + p) * CC + cbase + h * D + d0, xv);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) xv[e] = 0.f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        y[e] = fmaf(w[(size_t)(cbase + h * D + d0 + e) * 4 + r], xv[e], y[e]);
+                }
+            } else {
+                load8(x + (size_t)(cs.seq0 + cs.p0 + row) * H * D + (size_t)h * D + d0, y);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            out[ks][e] = y[e];
+            ss = fmaf(y[e], y[e], ss);
+        }
+    }
+    if (norm) {
+        ss += __shfl_xor(ss, 16, kWave);
+        ss += __shfl_xor(ss, 32, kWave);
+        const float inv = 1.0f / sqrtf(ss + kNormEps);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[ks][e] *= inv;
+    }
+}
+
+// Conv'd value entries of one 16-row block in the C/D layout of a 16x16 MFMA:
+// lane l holds rows rb*16 + (l/16)*4 + i (i < 4) of columns j0 + t*16 + l%16
+// for the value tiles t < TV/16.
+template <int DV, typename TI>
+__device__ void rows_dfrag_v(const TI *v, int H, int h, const ChunkSrc<TI> &cs, int rb, int j0,
+                             int CC, int cbase, const float *w, float (&out)[TV / 16][4]) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int t = 0; t < TV / 16; ++t) {
+        const int j = j0 + t * 16 + lane % 16;
+        const int c = cbase + h * DV + j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = rb * RB + (lane / 16) * 4 + i;
+            float y = 0.f;
+            if (row < cs.L) {
+                if (w) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int p = cs.p0 + row - 3 + r;
+                        float xv = 0.f;
+                        if (p >= 0) xv = to_f32(v[(size_t)(cs.seq0 + p) * H * DV + (size_t)h * DV + j]);
+                        else if (cs.win) xv = to_f32(cs.win[(size_t)(3 + p) * CC + c]);
+                        y = fmaf(w[(size_t)c * 4 + r], xv, y);
+                    }
+                } else {
+                    y = to_f32(v[(size_t)(cs.seq0 + cs.p0 + row) * H * DV + (size_t)h * DV + j]);
+                }
+            }
+            out[t][i] = y;
+        }
+    }
+}
+
 // ------------------------------------------------------------ prep
 template <int DK, int DV, typename TI>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
-    __shared__ float s_qt[DK * CP], s_kt[DK * CP];
-    __shared__ float s_A[C * (C + 1)];   // A, then T (row-major, padded)
-    __shared__ float s_g[C], s_b[C], s_inv[C];
+    constexpr int KP = DK + 4;           // padded row of the staged K rows
+    // staged K rows [C][KP], then (reused) T' [C][C + 1]
+    constexpr int SK = C * KP > C * (C + 1) ? C * KP : C * (C + 1);
+    __shared__ __attribute__((aligned(16))) float s_k[SK];
+    __shared__ __attribute__((aligned(16))) float s_A[C * (C + 1)];  // strictly lower A
 
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
     const int gc = blockIdx.x, h = blockIdx.y;
@@ -188,116 +307,122 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
     const int s = find_seq(chunk_start, a.n_seq, gc);
     const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
     const int c = gc - chunk_start[s];
-    const int p0 = c * C;
-    const int L = min(C, sp.len - p0);
     const int H = a.H;
     const int CC = H * (2 * DK + DV);
     const int src = a.parent ? a.parent[s] : s;
     const bool src_ok = src >= 0 && src < a.n_parent;
-    const TI *win = (a.win_in && src_ok) ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC
-                                         : nullptr;
-    const int tid = threadIdx.x;
+    ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C),
+                    (a.win_in && src_ok) ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC
+                                         : nullptr};
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
 
-    conv_part<TI, true>(static_cast<const TI *>(a.q), H, DK, h, 0, DK, sp.start, p0, L, win, CC, 0,
-                        a.conv_w, s_qt, CP);
-    conv_part<TI, true>(static_cast<const TI *>(a.k), H, DK, h, 0, DK, sp.start, p0, L, win, CC,
-                        H * DK, a.conv_w, s_kt, CP);
-    if (tid == 0) {
-        float g = 0.f;
-        for (int r = 0; r < C; ++r) {
-            if (r < L) g += a.log_alpha[(size_t)(sp.start + p0 + r) * H + h];
-            s_g[r] = g;
-            s_b[r] = r < L ? a.beta[(size_t)(sp.start + p0 + r) * H + h] : 0.f;
-        }
-    }
+    float kf[DK / 32][8], qf[DK / 32][8];
+    rows_afrag<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK, a.conv_w,
+                       a.qk_norm != 0, kf);
+    rows_afrag<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, 0, a.conv_w, a.qk_norm != 0,
+                       qf);
+    const float g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
+    const float b_l = lane < cs.L ? a.beta[(size_t)(cs.seq0 + cs.p0 + lane) * H + h] : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            s_k[(w * RB + lane % 16) * KP + ks * 32 + (lane / 16) * 8 + e] = kf[ks][e];
     __syncthreads();
-    if (a.qk_norm) {
-        norm_rows_transposed<DK>(s_qt, CP, s_inv);
-        norm_rows_transposed<DK>(s_kt, CP, s_inv);
-    }
 
-    // A and P: 4x4 outputs per thread
     float *rec = reinterpret_cast<float *>(static_cast<char *>(a.ws) +
                                            ws_layout(a.n_tokens, a.n_seq, H).rec_off) +
-                 ((size_t)gc * H + h) * (2 * C * C + C);
-    float *Tt = rec;            // T'^T : Tt[s][r] = T[r][s] beta_s
-    float *Pt = rec + C * C;    // P^T  : Pt[s][r] = P[r][s]
-    float *G = rec + 2 * C * C; // g
-    {
-        const int r0 = (tid / 16) * 4, c0 = (tid % 16) * 4;
-        float kk[4][4] = {}, qk[4][4] = {};
-        for (int d = 0; d < DK; ++d) {
-            const float4 kr = *reinterpret_cast<const float4 *>(s_kt + d * CP + r0);
-            const float4 qr = *reinterpret_cast<const float4 *>(s_qt + d * CP + r0);
-            const float4 kc = *reinterpret_cast<const float4 *>(s_kt + d * CP + c0);
-            const float krv[4] = {kr.x, kr.y, kr.z, kr.w}, qrv[4] = {qr.x, qr.y, qr.z, qr.w};
-            const float kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+                 ((size_t)gc * H + h) * (2 * C * C);
+    float *Tg = rec;          // T' [C][C] row-major
+    float *Pg = rec + C * C;  // P  [C][C] row-major
+
+    // KK^T and QK^T tiles (w, ct), ct <= w, on MFMA; the rest of the rows are zero
+    Split8 ka[DK / 32], qa[DK / 32];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+    for (int ks = 0; ks < DK / 32; ++ks) {
+        ka[ks] = split8(kf[ks]);
+        qa[ks] = split8(qf[ks]);
+    }
+    for (int ct = 0; ct < C / RB; ++ct) {
+        f32x4v kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+        if (ct <= w) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    kk[i][j] = fmaf(krv[i], kcv[j], kk[i][j]);
-                    qk[i][j] = fmaf(qrv[i], kcv[j], qk[i][j]);
-                }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = r0 + i, sc = c0 + j;
-                const bool live = r < L && sc < L;
-                const float dec = live && sc <= r ? expf(s_g[r] - s_g[sc]) : 0.f;
-                s_A[r * (C + 1) + sc] = (sc < r) ? s_b[r] * dec * kk[i][j] : 0.f;
-                Pt[sc * C + r] = dec * qk[i][j];
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                float bx[8];
+                lds_read8(s_k + (ct * RB + lane % 16) * KP + ks * 32 + (lane / 16) * 8, bx);
+                const Split8 bs = split8(bx);
+                kk = mma3(ka[ks], bs, kk);
+                qk = mma3(qa[ks], bs, qk);
             }
+        }
+        // D layout: rows w*16 + (l/16)*4 + i, column ct*16 + l%16
+        const int col = ct * RB + lane % 16;
+        const float g_c = __shfl(g, col, kWave);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = w * RB + (lane / 16) * 4 + i;
+            const float g_r = __shfl(g, row, kWave);
+            const float b_r = __shfl(b_l, row, kWave);
+            const bool live = row < cs.L && col < cs.L;
+            const float dec = (live && col <= row) ? expf(g_r - g_c) : 0.f;
+            s_A[row * (C + 1) + col] = col < row ? b_r * dec * kk[i] : 0.f;
+            Pg[row * C + col] = dec * qk[i];
+        }
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution, row by row; T overwrites A
-    // (row r of A is read before row r of T is written; rows < r hold T).
-    // Four lanes share one column s and split the sum over j.
+    // T = (I + A)^-1, one column per group of 4 lanes (columns are
+    // independent): lane (col, part) keeps T[j][col] for j = part (mod 4).
     {
-        const int sc = tid / 4, part = tid % 4;
-        for (int r = 1; r < C; ++r) {
+        const int col = w * 16 + lane / 4, part = lane % 4;
+        float t[C / 4];
+#pragma unroll
+        for (int q = 0; q < C / 4; ++q) t[q] = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
             float acc = 0.f;
-            if (sc < r)
-                for (int j = sc + part; j < r; j += 4)
-                    acc = fmaf(s_A[r * (C + 1) + j], (j == sc) ? 1.f : s_A[j * (C + 1) + sc], acc);
+#pragma unroll
+            for (int q = 0; q < C / 4; ++q) {
+                const int j = q * 4 + part;
+                if (j < r) acc = fmaf(s_A[r * (C + 1) + j], t[q], acc);
+            }
             acc += __shfl_xor(acc, 1, kWave);
             acc += __shfl_xor(acc, 2, kWave);
-            __syncthreads();
-            if (sc < r && part == 0) s_A[r * (C + 1) + sc] = -acc;
-            __syncthreads();
+            const float val = (r == col) ? 1.f : (r > col ? -acc : 0.f);
+            if (r % 4 == part) t[r / 4] = val;
         }
+        __syncthreads();  // every lane is done with s_A; s_k is free as well
+        // T'[j][col] = T[j][col] beta_col, staged through LDS for coalesced stores
+        const float bcol = __shfl(b_l, col, kWave);
+#pragma unroll
+        for (int q = 0; q < C / 4; ++q) s_k[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
     }
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int sc = idx / C, r = idx % C;  // Tt[sc][r] = T[r][sc] beta_sc
-        const float t = r == sc ? 1.f : (sc < r ? s_A[r * (C + 1) + sc] : 0.f);
-        Tt[idx] = t * s_b[sc];
-    }
-    if (tid < C) G[tid] = s_g[tid];
+    __syncthreads();
+    for (int idx = tid; idx < C * C; idx += kThreads)
+        Tg[idx] = s_k[(idx / C) * (C + 1) + idx % C];
 }
 
 // ------------------------------------------------------------ scan
 template <int DK, int DV, typename TI, typename TO>
 __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
-    __shared__ float s_S[DK * TV];     // state tile [DK][TV]
-    __shared__ float s_qt[DK * CP];    // conv'd, normalised q, transposed
-    __shared__ float s_kt[DK * CP];    // conv'd, normalised k, transposed
-    __shared__ float s_v[C * TV];      // V, then R
-    __shared__ float s_u[C * TV];      // U
-    __shared__ float s_tt[C * C];      // T'^T
-    __shared__ float s_pt[C * C];      // P^T
-    __shared__ float s_g[C], s_inv[C];
+    constexpr int KS = DK / 32;       // k-steps over d_k
+    constexpr int SP = DK + 4;        // padded row of Sig^T
+    constexpr int CPd = C + 4;        // padded row of K~^T, R^T, U^T
+    constexpr int NVT = TV / 16;      // 16-wide value sub-tiles
+    constexpr int NFT = NVT * (DK / 16);  // output tiles of the state update
+    __shared__ __attribute__((aligned(16))) float s_St[TV * SP];   // Sig^T tile [TV][DK]
+    __shared__ __attribute__((aligned(16))) float s_Kt[DK * CPd];  // K~^T [DK][C]
+    __shared__ __attribute__((aligned(16))) float s_Rt[TV * CPd];  // R^T  [TV][C]
+    __shared__ __attribute__((aligned(16))) float s_Ut[TV * CPd];  // U^T  [TV][C]
 
     constexpr int NT = DV / TV;
     const int tile = blockIdx.x % NT;
-    const int sh = blockIdx.x / NT;
-    const int s = sh / a.H, h = sh % a.H;
+    const int shd = blockIdx.x / NT;
+    const int s = shd / a.H, h = shd % a.H;
     const int H = a.H;
     const int CC = H * (2 * DK + DV);
     const int j0 = tile * TV;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
     const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H);
     const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
@@ -318,173 +443,182 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
 
     for (int idx = tid; idx < DK * TV; idx += kThreads) {
         const int d = idx / TV, j = idx % TV;
-        s_S[idx] = a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + j] : 0.f;
+        s_St[j * SP + d] =
+            a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + j] : 0.f;
     }
+    __syncthreads();
 
     const int nchunks = chunk_start[s + 1] - chunk_start[s];  // <= ceil(len / C)
     for (int c = 0; c < nchunks; ++c) {
-        const int p0 = c * C;
-        const int L = min(C, sp.len - p0);
-        const float *rec = reinterpret_cast<const float *>(static_cast<const char *>(a.ws) + wl.rec_off) +
+        const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
+        const float *rec = reinterpret_cast<const float *>(static_cast<const char *>(a.ws) +
+                                                           wl.rec_off) +
                            ((size_t)(chunk_start[s] + c) * H + h) * wl.rec_floats;
-        __syncthreads();  // previous chunk done with every buffer
-        conv_part<TI, true>(static_cast<const TI *>(a.q), H, DK, h, 0, DK, sp.start, p0, L, win, CC,
-                            0, a.conv_w, s_qt, CP);
-        conv_part<TI, true>(static_cast<const TI *>(a.k), H, DK, h, 0, DK, sp.start, p0, L, win, CC,
-                            H * DK, a.conv_w, s_kt, CP);
-        conv_part<TI, false>(static_cast<const TI *>(a.v), H, DV, h, j0, TV, sp.start, p0, L, win,
-                             CC, 2 * H * DK, a.conv_w, s_v, TV);
-        for (int idx = tid; idx < C * C / 4; idx += kThreads) {
-            reinterpret_cast<float4 *>(s_tt)[idx] = reinterpret_cast<const float4 *>(rec)[idx];
-            reinterpret_cast<float4 *>(s_pt)[idx] = reinterpret_cast<const float4 *>(rec + C * C)[idx];
-        }
-        if (tid < C) s_g[tid] = rec[2 * C * C + tid];
-        __syncthreads();
-        if (a.qk_norm) {
-            norm_rows_transposed<DK>(s_qt, CP, s_inv);
-            norm_rows_transposed<DK>(s_kt, CP, s_inv);
-        }
+        const float *Tg = rec, *Pg = rec + C * C;
 
-        // 4 rows x 2 columns of a [C][TV] output per thread
-        const int l0 = (tid / 16) * 4, cj = (tid % 16) * 2;
+        // this wave's 16 rows: K, Q (A operands), V (C/D layout), g
+        float kf[KS][8], qf[KS][8], vf[NVT][4];
+        rows_afrag<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK, a.conv_w,
+                           a.qk_norm != 0, kf);
+        rows_afrag<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, 0, a.conv_w,
+                           a.qk_norm != 0, qf);
+        rows_dfrag_v<DV, TI>(static_cast<const TI *>(a.v), H, h, cs, w, j0, CC, 2 * H * DK,
+                             a.conv_w, vf);
+        const float g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
+        const float gL = __shfl(g, C - 1, kWave);
+
+        // K~^T[d][row] = exp(g_L - g_row) k_row[d] for the state update
+        {
+            const int row = w * RB + lane % 16;
+            const float f = expf(gL - __shfl(g, row, kWave));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    s_Kt[(ks * 32 + (lane / 16) * 8 + e) * CPd + row] = kf[ks][e] * f;
+        }
+        Split8 ka[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = split8(kf[ks]);
+
+        // R = V - diag(gamma) K Sig0 : rows w*16.., all value columns
         float gam[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gam[i] = expf(s_g[l0 + i]);
+        for (int i = 0; i < 4; ++i) gam[i] = expf(__shfl(g, w * RB + (lane / 16) * 4 + i, kWave));
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                float bx[8];
+                lds_read8(s_St + (t * 16 + lane % 16) * SP + ks * 32 + (lane / 16) * 8, bx);
+                acc = mma3(ka[ks], split8(bx), acc);
+            }
+            float4 r4;
+            r4.x = vf[t][0] - gam[0] * acc[0];
+            r4.y = vf[t][1] - gam[1] * acc[1];
+            r4.z = vf[t][2] - gam[2] * acc[2];
+            r4.w = vf[t][3] - gam[3] * acc[3];
+            *reinterpret_cast<float4 *>(s_Rt + (t * 16 + lane % 16) * CPd + w * RB + (lane / 16) * 4) = r4;
+        }
+        __syncthreads();
 
-        // R = V - diag(gamma) K Sig0
-        {
-            float acc[4][2] = {};
-            for (int d = 0; d < DK; ++d) {
-                const float4 kr = *reinterpret_cast<const float4 *>(s_kt + d * CP + l0);
-                const float2 sv = *reinterpret_cast<const float2 *>(s_S + d * TV + cj);
-                const float kv[4] = {kr.x, kr.y, kr.z, kr.w};
+        // U = T' R (T' lower triangular: k-steps up to this wave's rows)
+        const int kmax = (w * RB + RB - 1) / 32;
+        Split8 ta[2];
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+            if (kq <= kmax) {
+                float tx[8];
+                load8(Tg + (w * RB + lane % 16) * C + kq * 32 + (lane / 16) * 8, tx);
+                ta[kq] = split8(tx);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                if (kq <= kmax) {
+                    float bx[8];
+                    lds_read8(s_Rt + (t * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, bx);
+                    acc = mma3(ta[kq], split8(bx), acc);
+                }
+            }
+            *reinterpret_cast<float4 *>(s_Ut + (t * 16 + lane % 16) * CPd + w * RB + (lane / 16) * 4) =
+                make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+        __syncthreads();
+
+        // O = diag(gamma) Q Sig0 + P U
+        if (a.o) {
+            Split8 qa[KS], pa[2];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[ks] = split8(qf[ks]);
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                if (kq <= kmax) {
+                    float px[8];
+                    load8(Pg + (w * RB + lane % 16) * C + kq * 32 + (lane / 16) * 8, px);
+                    pa[kq] = split8(px);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) {
+                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    float bx[8];
+                    lds_read8(s_St + (t * 16 + lane % 16) * SP + ks * 32 + (lane / 16) * 8, bx);
+                    acc = mma3(qa[ks], split8(bx), acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] *= gam[i];
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) {
+                    if (kq <= kmax) {
+                        float bx[8];
+                        lds_read8(s_Ut + (t * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, bx);
+                        acc = mma3(pa[kq], split8(bx), acc);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    acc[i][0] = fmaf(kv[i], sv.x, acc[i][0]);
-                    acc[i][1] = fmaf(kv[i], sv.y, acc[i][1]);
+                    const int row = w * RB + (lane / 16) * 4 + i;
+                    if (row < cs.L)
+                        static_cast<TO *>(a.o)[((size_t)(cs.seq0 + cs.p0 + row) * H + h) * DV + j0 +
+                                               t * 16 + lane % 16] = from_f32<TO>(acc[i]);
                 }
+            }
+        }
+        __syncthreads();  // Sig^T fully read before it is rewritten
+
+        // Sig^T <- gamma_L Sig^T + U^T K~   (tiles: value sub-tile x 16 keys)
+        const float gamL = expf(gL);
+        for (int ft = w; ft < NFT; ft += kWaves) {
+            const int t = ft % NVT, dt = ft / NVT;
+            f32x4v acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = gamL * s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16];
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                float ax[8], bx[8];
+                lds_read8(s_Ut + (t * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, ax);
+                lds_read8(s_Kt + (dt * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, bx);
+                acc = mma3(split8(ax), split8(bx), acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float *vv = s_v + (l0 + i) * TV + cj + j;
-                    *vv = *vv - gam[i] * acc[i][j];
-                }
+                s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16] = acc[i];
         }
         __syncthreads();
-        // U = T' R
-        {
-            float acc[4][2] = {};
-            const int smax = min(l0 + 4, C);
-            for (int sc = 0; sc < smax; ++sc) {
-                const float4 tr = *reinterpret_cast<const float4 *>(s_tt + sc * C + l0);
-                const float2 rv = *reinterpret_cast<const float2 *>(s_v + sc * TV + cj);
-                const float tv[4] = {tr.x, tr.y, tr.z, tr.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[i][0] = fmaf(tv[i], rv.x, acc[i][0]);
-                    acc[i][1] = fmaf(tv[i], rv.y, acc[i][1]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s_u[(l0 + i) * TV + cj] = acc[i][0];
-                s_u[(l0 + i) * TV + cj + 1] = acc[i][1];
-            }
-        }
-        __syncthreads();
-        // O = diag(gamma) Q Sig0 + P U
-        if (a.o) {
-            float acc[4][2] = {}, pu[4][2] = {};
-            for (int d = 0; d < DK; ++d) {
-                const float4 qr = *reinterpret_cast<const float4 *>(s_qt + d * CP + l0);
-                const float2 sv = *reinterpret_cast<const float2 *>(s_S + d * TV + cj);
-                const float qv[4] = {qr.x, qr.y, qr.z, qr.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[i][0] = fmaf(qv[i], sv.x, acc[i][0]);
-                    acc[i][1] = fmaf(qv[i], sv.y, acc[i][1]);
-                }
-            }
-            const int smax = min(l0 + 4, C);
-            for (int sc = 0; sc < smax; ++sc) {
-                const float4 pr = *reinterpret_cast<const float4 *>(s_pt + sc * C + l0);
-                const float2 uv = *reinterpret_cast<const float2 *>(s_u + sc * TV + cj);
-                const float pv[4] = {pr.x, pr.y, pr.z, pr.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pu[i][0] = fmaf(pv[i], uv.x, pu[i][0]);
-                    pu[i][1] = fmaf(pv[i], uv.y, pu[i][1]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int l = l0 + i;
-                if (l < L) {
-                    TO *orow = static_cast<TO *>(a.o) + ((size_t)(sp.start + p0 + l) * H + h) * DV + j0 + cj;
-                    orow[0] = from_f32<TO>(fmaf(gam[i], acc[i][0], pu[i][0]));
-                    orow[1] = from_f32<TO>(fmaf(gam[i], acc[i][1], pu[i][1]));
-                }
-            }
-        }
-        __syncthreads();  // O read the old state
-        // Sig <- gamma_L Sig + K~^T U,  K~_l = exp(g_L - g_l) k_l
-        {
-            const float gL = s_g[C - 1];  // rows >= L add nothing to g
-            const float gamL = expf(gL);
-            for (int idx = tid; idx < C * TV; idx += kThreads) {
-                const int l = idx / TV;
-                s_u[idx] *= (l < L) ? expf(gL - s_g[l]) : 0.f;
-            }
-            __syncthreads();
-            const int d0 = (tid / 8) * 4, c0 = (tid % 8) * 4;  // DK <= 128 rows
-            float acc[4][4] = {};
-            if (d0 < DK)
-            for (int l = 0; l < L; ++l) {
-                const float4 uv = *reinterpret_cast<const float4 *>(s_u + l * TV + c0);
-                const float uu[4] = {uv.x, uv.y, uv.z, uv.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float kd = s_kt[(d0 + i) * CP + l];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(kd, uu[j], acc[i][j]);
-                }
-            }
-            if (d0 < DK)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float4 *sp4 = reinterpret_cast<float4 *>(s_S + (d0 + i) * TV + c0);
-                const float4 old = *sp4;
-                *sp4 = make_float4(fmaf(gamL, old.x, acc[i][0]), fmaf(gamL, old.y, acc[i][1]),
-                                   fmaf(gamL, old.z, acc[i][2]), fmaf(gamL, old.w, acc[i][3]));
-            }
-        }
     }
-    __syncthreads();
+
     if (a.state_out)
         for (int idx = tid; idx < DK * TV; idx += kThreads) {
             const int d = idx / TV, j = idx % TV;
-            a.state_out[(((size_t)s * H + h) * DK + d) * DV + j0 + j] = s_S[idx];
+            a.state_out[(((size_t)s * H + h) * DK + d) * DV + j0 + j] = s_St[j * SP + d];
         }
     // window out (tile 0): the last 3 raw inputs of the head's channels
     if (a.win_out && tile == 0) {
         TI *wo = static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC;
         const int W = 2 * DK + DV;
         for (int idx = tid; idx < 3 * W; idx += kThreads) {
-            const int r = idx / W, w = idx % W;
+            const int r = idx / W, wc = idx % W;
             const int p = sp.len - 3 + r;
             int cch;
             const TI *xs;
             size_t col, stride;
-            if (w < DK) {
-                cch = h * DK + w; xs = static_cast<const TI *>(a.q); col = (size_t)h * DK + w; stride = (size_t)H * DK;
-            } else if (w < 2 * DK) {
-                cch = H * DK + h * DK + (w - DK); xs = static_cast<const TI *>(a.k);
-                col = (size_t)h * DK + (w - DK); stride = (size_t)H * DK;
+            if (wc < DK) {
+                cch = h * DK + wc; xs = static_cast<const TI *>(a.q);
+                col = (size_t)h * DK + wc; stride = (size_t)H * DK;
+            } else if (wc < 2 * DK) {
+                cch = H * DK + h * DK + (wc - DK); xs = static_cast<const TI *>(a.k);
+                col = (size_t)h * DK + (wc - DK); stride = (size_t)H * DK;
             } else {
-                cch = 2 * H * DK + h * DV + (w - 2 * DK); xs = static_cast<const TI *>(a.v);
-                col = (size_t)h * DV + (w - 2 * DK); stride = (size_t)H * DV;
+                cch = 2 * H * DK + h * DV + (wc - 2 * DK); xs = static_cast<const TI *>(a.v);
+                col = (size_t)h * DV + (wc - 2 * DK); stride = (size_t)H * DV;
             }
             TI val;
             if (p >= 0) val = xs[(size_t)(sp.start + p) * stride + col];
@@ -505,8 +639,8 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wl.max_chunks > 0) {
-        hipLaunchKernelGGL((prep_kernel<D, D, TI>), dim3((unsigned)wl.max_chunks, a.H), dim3(kThreads),
-                           0, stream, a);
+        hipLaunchKernelGGL((prep_kernel<D, D, TI>), dim3((unsigned)wl.max_chunks, a.H),
+                           dim3(kThreads), 0, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
