@@ -84,6 +84,19 @@ __device__ __forceinline__ f32x4v mma3(const Split8 &a, const Split8 &b, f32x4v 
     return c;
 }
 
+// 8 consecutive bf16 of a hi plane and the matching lo plane (16-byte aligned)
+__device__ __forceinline__ Split8 read_split8(const __bf16 *hi, const __bf16 *lo) {
+    Split8 s;
+    s.hi = *reinterpret_cast<const bf16x8 *>(hi);
+    s.lo = *reinterpret_cast<const bf16x8 *>(lo);
+    return s;
+}
+
+__device__ __forceinline__ void split1(float x, __bf16 &hi, __bf16 &lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
 __device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
     const float4 b = *reinterpret_cast<const float4 *>(p + 4);
@@ -109,19 +122,42 @@ __device__ __forceinline__ void load8(const bf16 *p, float (&x)[8]) {
 }
 
 // ------------------------------------------------------------ workspace
+// Per (chunk, head) record of bf16 hi / lo planes, split once by the prep
+// kernel for the scan:
+//   T'  [C][C], P [C][C]              row-major (A operands)
+//   K, Q [C][d_k]                     the conv'd, normalised chunk rows (A operands)
+//   K~^T [d_k][C]                     exp(g_L - g_r) k_r, transposed (B operand)
+struct RecLayout {
+    size_t thi, tlo, phi, plo, khi, klo, qhi, qlo, kthi, ktlo, elems;
+};
+
+__host__ __device__ constexpr RecLayout rec_layout(int dk) {
+    return RecLayout{0,
+                     (size_t)C * C,
+                     2 * (size_t)C * C,
+                     3 * (size_t)C * C,
+                     4 * (size_t)C * C,
+                     4 * (size_t)C * C + (size_t)C * dk,
+                     4 * (size_t)C * C + 2 * (size_t)C * dk,
+                     4 * (size_t)C * C + 3 * (size_t)C * dk,
+                     4 * (size_t)C * C + 4 * (size_t)C * dk,
+                     4 * (size_t)C * C + 5 * (size_t)C * dk,
+                     4 * (size_t)C * C + 6 * (size_t)C * dk};
+}
+
 struct WsLayout {
-    size_t rec_off;     // per (chunk, head) record: T' [C][C], P [C][C] (row-major)
-    size_t rec_floats;
+    size_t rec_off;
+    size_t rec_elems;   // bf16 elements per record
     size_t max_chunks;
     size_t total;
 };
 
-__host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H) {
+__host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H, int dk) {
     WsLayout w{};
     w.max_chunks = (size_t)n_tokens / C + (size_t)n_seq;
     w.rec_off = ((sizeof(int32_t) * ((size_t)n_seq + 1)) + 255) & ~size_t(255);
-    w.rec_floats = 2 * (size_t)C * C;
-    w.total = w.rec_off + sizeof(float) * w.rec_floats * w.max_chunks * (size_t)H;
+    w.rec_elems = rec_layout(dk).elems;
+    w.total = w.rec_off + sizeof(__bf16) * w.rec_elems * w.max_chunks * (size_t)H;
     return w;
 }
 
@@ -193,7 +229,9 @@ struct ChunkSrc {
 __device__ __forceinline__ float chunk_g(const float *log_alpha, int H, int h, int seq0, int p0,
                                          int L) {
     const int lane = threadIdx.x % kWave;
-    float g = lane < L ? log_alpha[(size_t)(seq0 + p0 + lane) * H + h] : 0.f;
+    const int r = min(lane, L - 1);  // clamped: the load is unconditional
+    float g = log_alpha[(size_t)(seq0 + p0 + r) * H + h];
+    g = lane < L ? g : 0.f;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const float o = __shfl_up(g, off, kWave);
@@ -202,49 +240,119 @@ __device__ __forceinline__ float chunk_g(const float *log_alpha, int H, int h, i
     return g;
 }
 
+// Raw io-dtype words of 8 consecutive values: 4 words for bf16, 8 for fp32.
+template <typename TI>
+struct Raw8 {
+    static constexpr int W = 8 * (int)sizeof(TI) / 4;
+    uint32_t w[W];
+};
+
+template <typename TI>
+__device__ __forceinline__ void raw_load(const TI *p, Raw8<TI> &r) {
+#pragma unroll
+    for (int i = 0; i < Raw8<TI>::W / 4; ++i) {
+        const uint4 u = reinterpret_cast<const uint4 *>(p)[i];
+        r.w[4 * i] = u.x;
+        r.w[4 * i + 1] = u.y;
+        r.w[4 * i + 2] = u.z;
+        r.w[4 * i + 3] = u.w;
+    }
+}
+
+__device__ __forceinline__ void raw_unpack(const Raw8<float> &r, float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(r.w[e]);
+}
+__device__ __forceinline__ void raw_unpack(const Raw8<bf16> &r, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(r.w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
+    }
+}
+
+// lane i <- lane (i - N) mod 16 of its 16-lane DPP row (row_ror:N)
+template <int N>
+__device__ __forceinline__ uint32_t ror16(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + N, 0xf, 0xf, false);
+}
+
 // Conv'd (and, for q / k, normalised) rows rb*16 .. rb*16+15 of the chunk in
 // the A-operand layout of a 16x16x32 MFMA: lane l holds row rb*16 + l%16,
 // columns ks*32 + (l/16)*8 + e for ks < D/32, e < 8. Rows >= L are zero.
-// x is the [N][H][D] stream of this part; cbase its first channel in the
-// [q | k | v] concatenation of CC channels.
+// x is the [N][H][D] stream of this part, cwin the part's first channel of
+// head h in the [q | k | v] window rows, s_w the part's taps [D][4] in LDS
+// (null: no convolution). Each lane loads only its own raw row; lanes 13-15
+// also load the 3 rows before the block (from the stream or the incoming
+// window). The three earlier taps of a row then come from the lanes 1-3 rows
+// up through DPP row rotations, which match the 16-row layout exactly.
 template <int D, typename TI>
 __device__ void rows_afrag(const TI *x, int H, int h, const ChunkSrc<TI> &cs, int rb, int CC,
-                           int cbase, const float *w, bool norm, float (&out)[D / 32][8]) {
+                           int cwin, const float *s_w, bool norm, float (&out)[D / 32][8]) {
+    constexpr int KS = D / 32;
     const int lane = threadIdx.x % kWave;
-    const int row = rb * RB + lane % 16;
+    const int i = lane % 16;
     const int cq = (lane / 16) * 8;
+    const int row = rb * RB + i;
     const bool live = row < cs.L;
+    // Every load is unconditional from a clamped, in-bounds address (validity
+    // is applied afterwards) and all of them are issued before any use, so
+    // they travel as one batch.
+    const TI *own_p = x + (size_t)(cs.seq0 + cs.p0 + min(row, cs.L - 1)) * H * D + (size_t)h * D;
+    Raw8<TI> own[KS], halo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw_load(own_p + ks * 32 + cq, own[ks]);
+    const bool conv = s_w != nullptr;
+    if (conv) {
+        // halo rows (lanes 13..15): stream position ph, or window row 3 + ph.
+        // A block with no live row may put ph past the sequence: clamp it (a
+        // block with a live row has its halo inside the sequence).
+        const int ph = cs.p0 + rb * RB + i - RB;
+        const bool hvalid = i >= RB - 3 && (ph >= 0 || cs.win != nullptr);
+        const TI *hp = own_p;
+        if (i >= RB - 3) {
+            if (ph >= 0)
+                hp = x + (size_t)(cs.seq0 + min(ph, cs.p0 + cs.L - 1)) * H * D + (size_t)h * D;
+            else if (cs.win)
+                hp = cs.win + (size_t)(3 + max(ph, -3)) * CC + cwin;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) raw_load(hp + ks * 32 + cq, halo[ks]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int q = 0; q < Raw8<TI>::W; ++q) halo[ks].w[q] = hvalid ? halo[ks].w[q] : 0u;
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         const int d0 = ks * 32 + cq;
-        float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (live) {
-            if (w) {
+        float y[8];
+        raw_unpack(own[ks], y);
+        if (conv) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = cs.p0 + row - 3 + r;
-                    float xv[8];
-                    if (p >= 0) {
-                        load8(x + (size_t)(cs.seq0 + p) * H * D + (size_t)h * D + d0, xv);
-                    } else if (cs.win) {
-                        load8(cs.win + (size_t)(3 + p) * CC + cbase + h * D + d0, xv);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) xv[e] = 0.f;
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        y[e] = fmaf(w[(size_t)(cbase + h * D + d0 + e) * 4 + r], xv[e], y[e]);
-                }
-            } else {
-                load8(x + (size_t)(cs.seq0 + cs.p0 + row) * H * D + (size_t)h * D + d0, y);
-            }
+            for (int e = 0; e < 8; ++e) y[e] *= s_w[(d0 + e) * 4 + 3];
+            // taps n = 1, 2, 3 rows up: source lane j = i - n (mod 16) offers
+            // its own row if j <= 15 - n, else its halo row
+#define GDN_TAP(N)                                                                       \
+    {                                                                                    \
+        Raw8<TI> t;                                                                      \
+        _Pragma("unroll") for (int q = 0; q < Raw8<TI>::W; ++q)                          \
+            t.w[q] = ror16<N>(i <= 15 - (N) ? own[ks].w[q] : halo[ks].w[q]);             \
+        float xt[8];                                                                     \
+        raw_unpack(t, xt);                                                               \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e)                                    \
+            y[e] = fmaf(s_w[(d0 + e) * 4 + 3 - (N)], xt[e], y[e]);                       \
+    }
+            GDN_TAP(1)
+            GDN_TAP(2)
+            GDN_TAP(3)
+#undef GDN_TAP
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            out[ks][e] = y[e];
-            ss = fmaf(y[e], y[e], ss);
+            out[ks][e] = live ? y[e] : 0.f;
+            ss = fmaf(out[ks][e], out[ks][e], ss);
         }
     }
     if (norm) {
@@ -252,7 +360,7 @@ __device__ void rows_afrag(const TI *x, int H, int h, const ChunkSrc<TI> &cs, in
         ss += __shfl_xor(ss, 32, kWave);
         const float inv = 1.0f / sqrtf(ss + kNormEps);
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[ks][e] *= inv;
     }
@@ -260,46 +368,63 @@ __device__ void rows_afrag(const TI *x, int H, int h, const ChunkSrc<TI> &cs, in
 
 // Conv'd value entries of one 16-row block in the C/D layout of a 16x16 MFMA:
 // lane l holds rows rb*16 + (l/16)*4 + i (i < 4) of columns j0 + t*16 + l%16
-// for the value tiles t < TV/16.
+// for the value tiles t < TV/16. s_w: taps [TV][4] of the tile's v channels
+// in LDS (null: no convolution); cwin: first v channel of head h.
 template <int DV, typename TI>
 __device__ void rows_dfrag_v(const TI *v, int H, int h, const ChunkSrc<TI> &cs, int rb, int j0,
-                             int CC, int cbase, const float *w, float (&out)[TV / 16][4]) {
+                             int CC, int cwin, const float *s_w, float (&out)[TV / 16][4]) {
     const int lane = threadIdx.x % kWave;
+    const int r0 = rb * RB + (lane / 16) * 4;
 #pragma unroll
     for (int t = 0; t < TV / 16; ++t) {
-        const int j = j0 + t * 16 + lane % 16;
-        const int c = cbase + h * DV + j;
+        const int jt = t * 16 + lane % 16;  // column inside the tile
+        const int j = j0 + jt;
+        float xr[7];                         // raw rows r0 - 3 .. r0 + 3
+#pragma unroll
+        for (int q = 0; q < 7; ++q) {
+            const int row = r0 - 3 + q;
+            const int p = cs.p0 + row;          // >= -3
+            const bool inseq = row < cs.L && p >= 0;
+            const bool inwin = p < 0 && cs.win != nullptr;
+            const bool need = s_w != nullptr || q >= 3;
+            // unconditional load from a clamped in-bounds address
+            const TI *ptr = inwin ? cs.win + (size_t)(3 + p) * CC + cwin + j
+                                  : v + (size_t)(cs.seq0 + min(max(p, 0), cs.p0 + cs.L - 1)) * H * DV +
+                                        (size_t)h * DV + j;
+            const float xv = to_f32(*ptr);
+            xr[q] = (need && (inseq || inwin)) ? xv : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = rb * RB + (lane / 16) * 4 + i;
-            float y = 0.f;
-            if (row < cs.L) {
-                if (w) {
+            float y;
+            if (s_w) {
+                y = 0.f;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int p = cs.p0 + row - 3 + r;
-                        float xv = 0.f;
-                        if (p >= 0) xv = to_f32(v[(size_t)(cs.seq0 + p) * H * DV + (size_t)h * DV + j]);
-                        else if (cs.win) xv = to_f32(cs.win[(size_t)(3 + p) * CC + c]);
-                        y = fmaf(w[(size_t)c * 4 + r], xv, y);
-                    }
-                } else {
-                    y = to_f32(v[(size_t)(cs.seq0 + cs.p0 + row) * H * DV + (size_t)h * DV + j]);
-                }
+                for (int r = 0; r < 4; ++r) y = fmaf(s_w[jt * 4 + r], xr[i + r], y);
+            } else {
+                y = xr[i + 3];
             }
-            out[t][i] = y;
+            out[t][i] = r0 + i < cs.L ? y : 0.f;
         }
     }
+}
+
+// Stage the conv taps of `n` channels starting at channel c0 into LDS [n][4].
+__device__ __forceinline__ void stage_taps(const float *conv_w, int c0, int n, float *s_w) {
+    for (int idx = threadIdx.x; idx < n; idx += kThreads)
+        reinterpret_cast<float4 *>(s_w)[idx] = reinterpret_cast<const float4 *>(conv_w)[c0 + idx];
 }
 
 // ------------------------------------------------------------ prep
 template <int DK, int DV, typename TI>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
-    constexpr int KP = DK + 4;           // padded row of the staged K rows
-    // staged K rows [C][KP], then (reused) T' [C][C + 1]
-    constexpr int SK = C * KP > C * (C + 1) ? C * KP : C * (C + 1);
+    constexpr int KP = DK + 4;  // padded row of the staged K rows
+    // staged K rows [C][KP]; then K~^T [DK][C + 1]; then T' [C][C + 1]
+    constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
+    constexpr int SK = SK0 > C * (C + 1) ? SK0 : C * (C + 1);
     __shared__ __attribute__((aligned(16))) float s_k[SK];
     __shared__ __attribute__((aligned(16))) float s_A[C * (C + 1)];  // strictly lower A
+    __shared__ __attribute__((aligned(16))) float s_wq[DK * 4], s_wk[DK * 4];
 
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
     const int gc = blockIdx.x, h = blockIdx.y;
@@ -315,41 +440,60 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
                     (a.win_in && src_ok) ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC
                                          : nullptr};
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK);
+    constexpr RecLayout RL = rec_layout(DK);
+    __bf16 *rec = reinterpret_cast<__bf16 *>(static_cast<char *>(a.ws) + wl.rec_off) +
+                  ((size_t)gc * H + h) * wl.rec_elems;
 
-    float kf[DK / 32][8], qf[DK / 32][8];
-    rows_afrag<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK, a.conv_w,
-                       a.qk_norm != 0, kf);
-    rows_afrag<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, 0, a.conv_w, a.qk_norm != 0,
-                       qf);
-    const float g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
-    const float b_l = lane < cs.L ? a.beta[(size_t)(cs.seq0 + cs.p0 + lane) * H + h] : 0.f;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            s_k[(w * RB + lane % 16) * KP + ks * 32 + (lane / 16) * 8 + e] = kf[ks][e];
+    const bool conv = a.conv_w != nullptr;
+    if (conv) {
+        stage_taps(a.conv_w, h * DK, DK, s_wq);
+        stage_taps(a.conv_w, H * DK + h * DK, DK, s_wk);
+    }
     __syncthreads();
+    const float g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
+    const float gL = __shfl(g, C - 1, kWave);
+    float b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
+    b_l = lane < cs.L ? b_l : 0.f;
+    const int row = w * RB + lane % 16;  // this lane's row in the A layout
+    const int cq = (lane / 16) * 8;
 
-    float *rec = reinterpret_cast<float *>(static_cast<char *>(a.ws) +
-                                           ws_layout(a.n_tokens, a.n_seq, H).rec_off) +
-                 ((size_t)gc * H + h) * (2 * C * C);
-    float *Tg = rec;          // T' [C][C] row-major
-    float *Pg = rec + C * C;  // P  [C][C] row-major
-
-    // KK^T and QK^T tiles (w, ct), ct <= w, on MFMA; the rest of the rows are zero
-    Split8 ka[DK / 32], qa[DK / 32];
+    // conv'd, normalised Q and K rows; their split A operands go to the record
+    Split8 qa[DK / 32], ka[DK / 32];
+    {
+        float qf[DK / 32][8];
+        rows_afrag<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, h * DK,
+                           conv ? s_wq : nullptr, a.qk_norm != 0, qf);
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+            qa[ks] = split8(qf[ks]);
+            const size_t off = (size_t)row * DK + ks * 32 + cq;
+            *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
+            *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = qa[ks].lo;
+        }
+    }
+    float kf[DK / 32][8];
+    rows_afrag<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK + h * DK,
+                       conv ? s_wk : nullptr, a.qk_norm != 0, kf);
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
         ka[ks] = split8(kf[ks]);
-        qa[ks] = split8(qf[ks]);
+        const size_t off = (size_t)row * DK + ks * 32 + cq;
+        *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
+        *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_k[row * KP + ks * 32 + cq + e] = kf[ks][e];
     }
+    __syncthreads();
+
+    // KK^T and QK^T tiles (w, ct), ct <= w, on MFMA; A and P from them
     for (int ct = 0; ct < C / RB; ++ct) {
         f32x4v kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
         if (ct <= w) {
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
                 float bx[8];
-                lds_read8(s_k + (ct * RB + lane % 16) * KP + ks * 32 + (lane / 16) * 8, bx);
+                lds_read8(s_k + (ct * RB + lane % 16) * KP + ks * 32 + cq, bx);
                 const Split8 bs = split8(bx);
                 kk = mma3(ka[ks], bs, kk);
                 qk = mma3(qa[ks], bs, qk);
@@ -360,16 +504,28 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
         const float g_c = __shfl(g, col, kWave);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = w * RB + (lane / 16) * 4 + i;
-            const float g_r = __shfl(g, row, kWave);
-            const float b_r = __shfl(b_l, row, kWave);
-            const bool live = row < cs.L && col < cs.L;
-            const float dec = (live && col <= row) ? expf(g_r - g_c) : 0.f;
-            s_A[row * (C + 1) + col] = col < row ? b_r * dec * kk[i] : 0.f;
-            Pg[row * C + col] = dec * qk[i];
+            const int r = w * RB + (lane / 16) * 4 + i;
+            const float g_r = __shfl(g, r, kWave);
+            const float b_r = __shfl(b_l, r, kWave);
+            const bool live = r < cs.L && col < cs.L;
+            const float dec = (live && col <= r) ? expf(g_r - g_c) : 0.f;
+            s_A[r * (C + 1) + col] = col < r ? b_r * dec * kk[i] : 0.f;
+            split1(dec * qk[i], rec[RL.phi + r * C + col], rec[RL.plo + r * C + col]);
         }
     }
+    __syncthreads();  // s_A complete; the K rows in s_k are no longer needed
+
+    // K~^T[d][r] = exp(g_L - g_r) k_r[d], staged transposed for coalesced stores
+    {
+        const float f = expf(gL - __shfl(g, row, kWave));
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_k[(ks * 32 + cq + e) * (C + 1) + row] = kf[ks][e] * f;
+    }
     __syncthreads();
+    for (int idx = tid; idx < DK * C; idx += kThreads)
+        split1(s_k[(idx / C) * (C + 1) + idx % C], rec[RL.kthi + idx], rec[RL.ktlo + idx]);
 
     // T = (I + A)^-1, one column per group of 4 lanes (columns are
     // independent): lane (col, part) keeps T[j][col] for j = part (mod 4).
@@ -391,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
             const float val = (r == col) ? 1.f : (r > col ? -acc : 0.f);
             if (r % 4 == part) t[r / 4] = val;
         }
-        __syncthreads();  // every lane is done with s_A; s_k is free as well
+        __syncthreads();  // every lane is done with s_A and with the K~^T copy-out
         // T'[j][col] = T[j][col] beta_col, staged through LDS for coalesced stores
         const float bcol = __shfl(b_l, col, kWave);
 #pragma unroll
@@ -399,32 +555,71 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
     }
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += kThreads)
-        Tg[idx] = s_k[(idx / C) * (C + 1) + idx % C];
+        split1(s_k[(idx / C) * (C + 1) + idx % C], rec[RL.thi + idx], rec[RL.tlo + idx]);
 }
 
 // ------------------------------------------------------------ scan
+// Workgroup -> (sequence-head, value tile): the NT value tiles of one
+// sequence-head get block indices congruent modulo 8, so they are dispatched
+// to the same XCD and share its L2 for the chunk records they all read.
+__device__ __forceinline__ void scan_unit(int b, int NT, int &sh, int &tile) {
+    const int xcd = b % 8, local = b / 8;
+    tile = local % NT;
+    sh = (local / NT) * 8 + xcd;
+}
+
+// Offset (in bf16 elements) of 16-byte chunk `ch` of row `r` in an LDS
+// plane of rows of C bf16 (128 bytes): the chunk index is XOR-swizzled by
+// the row so that 16 lanes reading one chunk of 16 consecutive rows spread
+// over all banks.
+__device__ __forceinline__ int kt_swz(int r, int ch) { return r * C + ((ch ^ (r & 7)) << 3); }
+
+// Registers a chunk step needs from memory, loaded ahead of use: only loads
+// go in here (no arithmetic on the results), so the loads can stay in
+// flight until the step consumes them.
+
+// 16-byte direct-to-LDS load (lane l lands at lds + 8 l elements). Kept out
+// of the kernel templates: with the builtin inside a template the host pass
+// drops the kernel's launch stub without a diagnostic.
+__device__ __forceinline__ void lds_dma16(const __bf16 *g, __bf16 *lds) {
+    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+template <int KS, int NVT, typename TI>
+struct ChunkRegs {
+    Split8 ka[KS], qa[KS], ta[2], pa[2];
+    TI vraw[NVT][7];  // raw V rows r0-3 .. r0+3 of this lane's columns
+    float la;         // log a of row `lane` (clamped)
+};
+
 template <int DK, int DV, typename TI, typename TO>
 __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
-    constexpr int KS = DK / 32;       // k-steps over d_k
-    constexpr int SP = DK + 4;        // padded row of Sig^T
-    constexpr int CPd = C + 4;        // padded row of K~^T, R^T, U^T
-    constexpr int NVT = TV / 16;      // 16-wide value sub-tiles
-    constexpr int NFT = NVT * (DK / 16);  // output tiles of the state update
-    __shared__ __attribute__((aligned(16))) float s_St[TV * SP];   // Sig^T tile [TV][DK]
-    __shared__ __attribute__((aligned(16))) float s_Kt[DK * CPd];  // K~^T [DK][C]
-    __shared__ __attribute__((aligned(16))) float s_Rt[TV * CPd];  // R^T  [TV][C]
-    __shared__ __attribute__((aligned(16))) float s_Ut[TV * CPd];  // U^T  [TV][C]
+    constexpr int KS = DK / 32;          // k-steps over d_k
+    constexpr int SP = DK + 4;           // padded row of Sig^T (fp32)
+    constexpr int CB = C + 8;            // padded row of the R^T / U^T planes
+    constexpr int NVT = TV / 16;         // 16-wide value sub-tiles
+    constexpr int NFT = NVT * (DK / 16); // output tiles of the state update
+    constexpr RecLayout RL = rec_layout(DK);
+    // Sig^T tile [TV][DK] in fp32; R^T and U^T [TV][C] as hi / lo bf16
+    // planes (split once when written); K~^T [DK][C] hi / lo planes copied
+    // from the chunk record by direct-to-LDS loads (swizzled rows).
+    __shared__ __attribute__((aligned(16))) float s_St[TV * SP];
+    __shared__ __attribute__((aligned(16))) __bf16 s_Rh[TV * CB], s_Rl[TV * CB];
+    __shared__ __attribute__((aligned(16))) __bf16 s_Uh[TV * CB], s_Ul[TV * CB];
+    __shared__ __attribute__((aligned(16))) __bf16 s_Kh[DK * C], s_Kl[DK * C];
+    __shared__ __attribute__((aligned(16))) float s_wv[TV * 4];
 
     constexpr int NT = DV / TV;
-    const int tile = blockIdx.x % NT;
-    const int shd = blockIdx.x / NT;
+    int shd, tile;
+    scan_unit(blockIdx.x, NT, shd, tile);
+    if (shd >= a.n_seq * a.H) return;
     const int s = shd / a.H, h = shd % a.H;
     const int H = a.H;
     const int CC = H * (2 * DK + DV);
     const int j0 = tile * TV;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H);
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK);
     const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
     const int src = a.parent ? a.parent[s] : s;
     const bool src_ok = src >= 0 && src < a.n_parent;
@@ -441,6 +636,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     }
     const TI *win = a.win_in ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC : nullptr;
 
+    const bool conv = a.conv_w != nullptr;
+    if (conv) stage_taps(a.conv_w, 2 * H * DK + h * DV + j0, TV, s_wv);
     for (int idx = tid; idx < DK * TV; idx += kThreads) {
         const int d = idx / TV, j = idx % TV;
         s_St[j * SP + d] =
@@ -448,130 +645,186 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
-    const int nchunks = chunk_start[s + 1] - chunk_start[s];  // <= ceil(len / C)
+    const bool want_o = a.o != nullptr;
+    const int kmax = (w * RB + RB - 1) / 32;  // T', P lower triangular: k-steps to use
+    const int arow = w * RB + lane % 16;       // this lane's row in the A layout
+    const int acol = (lane / 16) * 8;
+    const int r0v = w * RB + (lane / 16) * 4;  // first of this lane's rows in the C/D layout
+    // read once: inside the loop the compiler could not prove these unchanged
+    // across the o stores and would reload them behind a full wait
+    const int cs0 = chunk_start[s];
+    const int nchunks = chunk_start[s + 1] - cs0;  // <= ceil(len / C)
+    const TI *vs = static_cast<const TI *>(a.v);
+    const int cwin_v = 2 * H * DK + h * DV;
+
+    auto record = [&](int c) {
+        return reinterpret_cast<const __bf16 *>(static_cast<const char *>(a.ws) + wl.rec_off) +
+               ((size_t)(cs0 + c) * H + h) * wl.rec_elems;
+    };
+    // loads only: every address is clamped in bounds, nothing is consumed here
+    auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI> &r) {
+        const __bf16 *rec = record(c);
+        const int p0 = c * C, L = min(C, sp.len - p0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const size_t off = (size_t)arow * DK + ks * 32 + acol;
+            r.ka[ks] = read_split8(rec + RL.khi + off, rec + RL.klo + off);
+            if (want_o) r.qa[ks] = read_split8(rec + RL.qhi + off, rec + RL.qlo + off);
+        }
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+            if (kq <= kmax) {
+                const int off = arow * C + kq * 32 + acol;
+                r.ta[kq] = read_split8(rec + RL.thi + off, rec + RL.tlo + off);
+                if (want_o) r.pa[kq] = read_split8(rec + RL.phi + off, rec + RL.plo + off);
+            }
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const int j = j0 + t * 16 + lane % 16;
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                const int p = p0 + r0v - 3 + q;  // >= -3
+                const TI *ptr = (p < 0 && win) ? win + (size_t)(3 + p) * CC + cwin_v + j
+                                               : vs + (size_t)(sp.start + min(max(p, 0), p0 + L - 1)) *
+                                                          H * DV + (size_t)h * DV + j;
+                r.vraw[t][q] = *ptr;
+            }
+        }
+        r.la = a.log_alpha[(size_t)(sp.start + p0 + min(lane, L - 1)) * H + h];
+    };
+    // K~^T hi / lo planes of chunk c into LDS (direct-to-LDS, 16 B per lane;
+    // the LDS position of a lane's bytes is fixed, so the swizzle is applied
+    // by choosing which global chunk each lane fetches)
+    auto load_kt = [&](int c) {
+        const __bf16 *rec = record(c);
+        constexpr int PER_WAVE = DK * C * 2 / 16 / kThreads;  // 16-byte pieces per lane, per plane
+#pragma unroll
+        for (int q = 0; q < PER_WAVE; ++q) {
+            const int piece = (q * kWaves + w) * kWave + lane;  // 16-byte piece of the plane
+            const int r = piece / 8, chl = piece % 8;           // LDS row, LDS chunk slot
+            const int chg = chl ^ (r & 7);                      // global chunk stored there
+            const int lds0 = (q * kWaves + w) * kWave * 8;      // wave-uniform LDS element offset
+            lds_dma16(rec + RL.kthi + r * C + chg * 8, s_Kh + lds0);
+            lds_dma16(rec + RL.ktlo + r * C + chg * 8, s_Kl + lds0);
+        }
+    };
+
+    ChunkRegs<KS, NVT, TI> nxt;
+    if (nchunks > 0) load_regs(0, nxt);
     for (int c = 0; c < nchunks; ++c) {
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
-        const float *rec = reinterpret_cast<const float *>(static_cast<const char *>(a.ws) +
-                                                           wl.rec_off) +
-                           ((size_t)(chunk_start[s] + c) * H + h) * wl.rec_floats;
-        const float *Tg = rec, *Pg = rec + C * C;
+        const ChunkRegs<KS, NVT, TI> cur = nxt;
+        load_kt(c);
 
-        // this wave's 16 rows: K, Q (A operands), V (C/D layout), g
-        float kf[KS][8], qf[KS][8], vf[NVT][4];
-        rows_afrag<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK, a.conv_w,
-                           a.qk_norm != 0, kf);
-        rows_afrag<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, 0, a.conv_w,
-                           a.qk_norm != 0, qf);
-        rows_dfrag_v<DV, TI>(static_cast<const TI *>(a.v), H, h, cs, w, j0, CC, 2 * H * DK,
-                             a.conv_w, vf);
-        const float g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
-        const float gL = __shfl(g, C - 1, kWave);
-
-        // K~^T[d][row] = exp(g_L - g_row) k_row[d] for the state update
-        {
-            const int row = w * RB + lane % 16;
-            const float f = expf(gL - __shfl(g, row, kWave));
+        // g (running log a over the chunk rows; rows >= L add nothing)
+        float g = lane < cs.L ? cur.la : 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    s_Kt[(ks * 32 + (lane / 16) * 8 + e) * CPd + row] = kf[ks][e] * f;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float o = __shfl_up(g, off, kWave);
+            if (lane >= off) g += o;
         }
-        Split8 ka[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[ks] = split8(kf[ks]);
-
-        // R = V - diag(gamma) K Sig0 : rows w*16.., all value columns
+        const float gL = __shfl(g, C - 1, kWave);
         float gam[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gam[i] = expf(__shfl(g, w * RB + (lane / 16) * 4 + i, kWave));
+        for (int i = 0; i < 4; ++i) gam[i] = expf(__shfl(g, r0v + i, kWave));
+
+        // conv'd V entries of this lane (C/D layout), from the raw rows
+        float vf[NVT][4];
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const int jt = t * 16 + lane % 16;
+            float xr[7];
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                const int row = r0v - 3 + q, p = cs.p0 + row;
+                const bool ok = (conv || q >= 3) && ((row < cs.L && p >= 0) || (p < 0 && win));
+                xr[q] = ok ? to_f32(cur.vraw[t][q]) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float y = xr[i + 3];
+                if (conv) {
+                    y = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) y = fmaf(s_wv[jt * 4 + r], xr[i + r], y);
+                }
+                vf[t][i] = r0v + i < cs.L ? y : 0.f;
+            }
+        }
+
+        // K Sig0 and Q Sig0 share the split Sig^T fragments;
+        // R = V - diag(gamma) K Sig0 goes to LDS, Q Sig0 stays in registers
+        f32x4v acc_o[NVT];
 #pragma unroll
         for (int t = 0; t < NVT; ++t) {
             f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+            acc_o[t] = acc;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 float bx[8];
-                lds_read8(s_St + (t * 16 + lane % 16) * SP + ks * 32 + (lane / 16) * 8, bx);
-                acc = mma3(ka[ks], split8(bx), acc);
+                lds_read8(s_St + (t * 16 + lane % 16) * SP + ks * 32 + acol, bx);
+                const Split8 bs = split8(bx);
+                acc = mma3(cur.ka[ks], bs, acc);
+                if (want_o) acc_o[t] = mma3(cur.qa[ks], bs, acc_o[t]);
             }
-            float4 r4;
-            r4.x = vf[t][0] - gam[0] * acc[0];
-            r4.y = vf[t][1] - gam[1] * acc[1];
-            r4.z = vf[t][2] - gam[2] * acc[2];
-            r4.w = vf[t][3] - gam[3] * acc[3];
-            *reinterpret_cast<float4 *>(s_Rt + (t * 16 + lane % 16) * CPd + w * RB + (lane / 16) * 4) = r4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = t * 16 + lane % 16, r = r0v + i;
+                split1(vf[t][i] - gam[i] * acc[i], s_Rh[col * CB + r], s_Rl[col * CB + r]);
+            }
         }
         __syncthreads();
 
-        // U = T' R (T' lower triangular: k-steps up to this wave's rows)
-        const int kmax = (w * RB + RB - 1) / 32;
-        Split8 ta[2];
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-            if (kq <= kmax) {
-                float tx[8];
-                load8(Tg + (w * RB + lane % 16) * C + kq * 32 + (lane / 16) * 8, tx);
-                ta[kq] = split8(tx);
-            }
-        }
+        // U = T' R
 #pragma unroll
         for (int t = 0; t < NVT; ++t) {
             f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kq = 0; kq < 2; ++kq) {
+            for (int kq = 0; kq < 2; ++kq)
                 if (kq <= kmax) {
-                    float bx[8];
-                    lds_read8(s_Rt + (t * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, bx);
-                    acc = mma3(ta[kq], split8(bx), acc);
+                    const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                    acc = mma3(cur.ta[kq], read_split8(s_Rh + off, s_Rl + off), acc);
                 }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = t * 16 + lane % 16, r = r0v + i;
+                split1(acc[i], s_Uh[col * CB + r], s_Ul[col * CB + r]);
             }
-            *reinterpret_cast<float4 *>(s_Ut + (t * 16 + lane % 16) * CPd + w * RB + (lane / 16) * 4) =
-                make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
         __syncthreads();
 
-        // O = diag(gamma) Q Sig0 + P U
-        if (a.o) {
-            Split8 qa[KS], pa[2];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qa[ks] = split8(qf[ks]);
-#pragma unroll
-            for (int kq = 0; kq < 2; ++kq) {
-                if (kq <= kmax) {
-                    float px[8];
-                    load8(Pg + (w * RB + lane % 16) * C + kq * 32 + (lane / 16) * 8, px);
-                    pa[kq] = split8(px);
-                }
-            }
+        // O = diag(gamma) Q Sig0 + P U (stored after the next barrier)
+        if (want_o) {
 #pragma unroll
             for (int t = 0; t < NVT; ++t) {
-                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    float bx[8];
-                    lds_read8(s_St + (t * 16 + lane % 16) * SP + ks * 32 + (lane / 16) * 8, bx);
-                    acc = mma3(qa[ks], split8(bx), acc);
-                }
+                for (int i = 0; i < 4; ++i) acc_o[t][i] *= gam[i];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= gam[i];
-#pragma unroll
-                for (int kq = 0; kq < 2; ++kq) {
+                for (int kq = 0; kq < 2; ++kq)
                     if (kq <= kmax) {
-                        float bx[8];
-                        lds_read8(s_Ut + (t * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, bx);
-                        acc = mma3(pa[kq], split8(bx), acc);
+                        const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                        acc_o[t] = mma3(cur.pa[kq], read_split8(s_Uh + off, s_Ul + off), acc_o[t]);
                     }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = w * RB + (lane / 16) * 4 + i;
-                    if (row < cs.L)
-                        static_cast<TO *>(a.o)[((size_t)(cs.seq0 + cs.p0 + row) * H + h) * DV + j0 +
-                                               t * 16 + lane % 16] = from_f32<TO>(acc[i]);
-                }
             }
         }
-        __syncthreads();  // Sig^T fully read before it is rewritten
+        // This wave's direct-to-LDS copies of K~^T are the only memory
+        // operations in flight here; finish them before the barrier so the
+        // whole plane is visible to every wave after it.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();  // K~^T complete; Sig^T fully read before it is rewritten
+
+        if (c + 1 < nchunks) load_regs(c + 1, nxt);  // prefetch the next step
+        if (want_o) {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = r0v + i;
+                    if (r < cs.L)
+                        static_cast<TO *>(a.o)[((size_t)(cs.seq0 + cs.p0 + r) * H + h) * DV + j0 +
+                                               t * 16 + lane % 16] = from_f32<TO>(acc_o[t][i]);
+                }
+        }
 
         // Sig^T <- gamma_L Sig^T + U^T K~   (tiles: value sub-tile x 16 keys)
         const float gamL = expf(gL);
@@ -583,10 +836,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
                 acc[i] = gamL * s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16];
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
-                float ax[8], bx[8];
-                lds_read8(s_Ut + (t * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, ax);
-                lds_read8(s_Kt + (dt * 16 + lane % 16) * CPd + kq * 32 + (lane / 16) * 8, bx);
-                acc = mma3(split8(ax), split8(bx), acc);
+                const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                const int ok = kt_swz(dt * 16 + lane % 16, kq * 4 + lane / 16);
+                acc = mma3(read_split8(s_Uh + ou, s_Ul + ou), read_split8(s_Kh + ok, s_Kl + ok), acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -632,7 +884,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
 template <int D, typename TI, typename TO>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     if (a.n_seq == 0) return hipSuccess;
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H);
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, D);
     int32_t *chunk_start = static_cast<int32_t *>(a.ws);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq, a.n_tokens,
                        (long long)wl.max_chunks, chunk_start);
@@ -644,7 +896,8 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const unsigned blocks = (unsigned)((size_t)a.n_seq * a.H * (D / TV));
+    const size_t n_sh = (size_t)a.n_seq * a.H;
+    const unsigned blocks = (unsigned)(((n_sh + 7) / 8) * 8 * (D / TV));  // see scan_unit
     hipLaunchKernelGGL((scan_kernel<D, D, TI, TO>), dim3(blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -652,10 +905,9 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv, int chunk) {
-    (void)dk;
-    (void)dv;
     (void)chunk;
-    return ws_layout(n_tokens, n_seq, H).total;
+    (void)dv;
+    return ws_layout(n_tokens, n_seq, H, dk).total;
 }
 
 hipError_t launch_prefill(int dk, int dv, int io, int out, const PrefillArgs &a,
