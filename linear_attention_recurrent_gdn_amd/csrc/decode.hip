@@ -68,9 +68,45 @@ struct TileMap {
     static_assert(P >= 1 && DK % RPP == 0, "tile must cover the rows");
 };
 
-template <int DK, int DV, int VAR, typename TI, typename TO, int MODE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+// Row-gathered position of key row i: the thread owning rows r0 + p*RPP
+// (p < P) finds them at r0*P .. r0*P + P - 1.
+template <int DK, int DV>
+__device__ __forceinline__ int row_gather(int i) {
     using Map = TileMap<DK, DV>;
+    return (i % Map::RPP) * Map::P + i / Map::RPP;
+}
+
+// N consecutive floats from LDS (16-byte aligned when N >= 4).
+template <int N>
+__device__ __forceinline__ void lds_gather(const float *p, float (&x)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const float4 v = reinterpret_cast<const float4 *>(p)[i];
+            x[4 * i] = v.x;
+            x[4 * i + 1] = v.y;
+            x[4 * i + 2] = v.z;
+            x[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = p[i];
+    }
+}
+
+// Write-back of a materialised base row piece. The eager step rewrites every
+// tile (a copy-like stream: non-temporal stores); the deferred steps write
+// the few merging slots, whose lines are read again at the next step.
+template <bool NT>
+__device__ __forceinline__ void store_base(float *p, float4 x) {
+    if (NT) store_stream(p, x);
+    else *reinterpret_cast<float4 *>(p) = x;
+}
+
+template <int DK, int DV, int VAR, typename TI, typename TO, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
+    using Map = TileMap<DK, DV>;
+    const auto rg = [](int i) { return row_gather<DK, DV>(i); };
     constexpr bool kPerKey = VAR != kScalar;
     constexpr bool kDelta = VAR != kRwkv6;
     constexpr int LS = kPerKey ? DK : 1;                 // log-decay values per log entry
@@ -80,12 +116,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     constexpr int SEG = DK < kWave ? DK : kWave;         // lanes summing one key range
     constexpr int NSEG = DK / SEG;                       // partial sums per key vector
 
-    __shared__ float s_k[DK], s_q[DK], s_a[DK], s_lam[DK];
-    __shared__ float s_red[kWaves][2][DV];
-    __shared__ float s_cpart[ML + 1][NSEG], s_dpart[ML + 1][NSEG], s_dtpart[NSEG];
-    __shared__ float s_kt[(ML + 1) * DK];  // k~_e (per-key decay) or k_e (scalar), merging steps
-    __shared__ float s_u[(ML + 1) * DV];   // u_e
-    __shared__ float s_fac[ML + 1];        // scalar decay: exp(Lam_t - Lam_e)
+    // LDS. Per-row vectors of the key side are kept in "row-gathered" order
+    // (rg(i): the P rows a thread owns are consecutive), so a thread fetches
+    // its rows with P/4 float4 reads.
+    __shared__ __attribute__((aligned(16))) float s_k[DK], s_q[DK], s_lam[DK];
+    __shared__ __attribute__((aligned(16))) float s_khg[DK], s_qhg[DK], s_ag[DK];  // a.k, a.q, a
+    __shared__ __attribute__((aligned(16))) float s_red[kWaves][2][DV];
+    __shared__ __attribute__((aligned(16))) float s_cd[ML + 1][4];  // c_e, d_e partial sums
+    __shared__ float s_dtpart[NSEG];
+    __shared__ __attribute__((aligned(16))) float s_ktg[(ML + 1) * DK];  // k~_e / k_e, row-gathered
+    __shared__ __attribute__((aligned(16))) float s_u[(ML + 1) * DV];    // u_e
+    __shared__ float s_fac[ML + 1];  // scalar decay: exp(Lam_t - Lam_e)
+    static_assert(NSEG <= 2, "two partial sums per key vector at most");
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -114,10 +156,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // entries that depend on it are issued while the base is in flight.
     const int col = (tid % Map::TPR) * 4;
     const int r0 = tid / Map::TPR;
+    // 32-bit element offsets from the uniform tile base keep the addresses
+    // of the 16 loads and stores in single VGPRs (scalar base + vector offset)
+    const auto tile_off = [&](int p) { return (uint32_t)((r0 + p * Map::RPP) * DV + col); };
     float4 reg[Map::P];
 #pragma unroll
     for (int p = 0; p < Map::P; ++p)
-        reg[p] = load_stream(S + (size_t)(r0 + p * Map::RPP) * DV + col);
+        reg[p] = load_stream(S + tile_off(p));
 
     int m_raw = 0;
     if (MODE != kEager) m_raw = a.log_len[sh];
@@ -137,7 +182,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (MODE == kAppend) merge = (a.merge_at > 0 && m + 1 >= a.merge_at) || m >= Mcap;
     if (MODE == kMergeOnly) merge = m > 0 && m >= a.min_len;
     if (!merge && MODE == kMergeOnly) return;
-
     const int e_last = max(m - 1, 0);  // a valid entry index for clamped loads
     float lam_prev = 0.f, lam_e_s = 0.f;
     TI kl_raw[NKE];
@@ -163,10 +207,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // ---- ReplayPrep (key side, once per slot-head)
     if (tid < DK) {
         const float lam = MODE == kMergeOnly ? lam_prev : lam_prev + lax;
+        const float ai = expf(lam);
+        const int g = rg(tid);
         s_lam[tid] = lam;
-        s_a[tid] = expf(lam);
         s_k[tid] = kx;
         s_q[tid] = qx;
+        s_ag[g] = ai;
+        s_khg[g] = ai * kx;
+        s_qhg[g] = ai * qx;
     }
     if (!kPerKey && tid < m) s_fac[tid] = lam_e_s;  // Lam_e, turned into a factor below
     if (MODE != kMergeOnly) {  // k . q
@@ -174,6 +222,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         if (tid < DK && lane % SEG == 0) s_dtpart[tid / SEG] = p;
     }
     __syncthreads();
+    // No barrier closes this part: what it writes (s_fac, s_cd, s_ktg, s_u)
+    // is read only after the reduction barrier or the merge barrier below.
     if (!kPerKey && tid < m) s_fac[tid] = expf(s_lam[0] - s_fac[tid]);  // exp(Lam_t - Lam_e)
     if (ML > 0) {
 #pragma unroll
@@ -187,14 +237,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
                 const float kt = kPerKey ? kl * expf(s_lam[i] - ll[r]) : kl;
                 pc = kt * s_k[i];
                 pd = kt * s_q[i];
-                if (merge) s_kt[e * DK + i] = kt;
+                if (merge) s_ktg[e * DK + rg(i)] = kt;
             }
             if (MODE != kMergeOnly) {
                 pc = wave_sum_seg<SEG>(pc);
                 pd = wave_sum_seg<SEG>(pd);
                 if (e < m && lane % SEG == 0) {
-                    s_cpart[e][i / SEG] = pc;
-                    s_dpart[e][i / SEG] = pd;
+                    s_cd[e][i / SEG] = pc;
+                    s_cd[e][2 + i / SEG] = pd;
+                    if (NSEG == 1) {
+                        s_cd[e][1] = 0.f;
+                        s_cd[e][3] = 0.f;
+                    }
                 }
             }
         }
@@ -204,22 +258,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             if (e < m) s_u[idx] = ul[r];
         }
     }
-    if (MODE != kMergeOnly && merge && tid < DK) s_kt[m * DK + tid] = kx;
-    if (!kPerKey) __syncthreads();  // s_fac ready for the value columns and the merge
+    if (MODE != kMergeOnly && merge && tid < DK) s_ktg[m * DK + rg(tid)] = kx;
 
     // ---- AppendDecode: S^T k^ and S^T q^ over the key rows
     if (MODE != kMergeOnly) {
         float ax[4] = {0.f, 0.f, 0.f, 0.f}, ao[4] = {0.f, 0.f, 0.f, 0.f};
+        constexpr int G = Map::P < 4 ? Map::P : 4;  // rows per LDS fetch
 #pragma unroll
-        for (int p = 0; p < Map::P; ++p) {
-            const int r = r0 + p * Map::RPP;
-            const float kh = s_a[r] * s_k[r];
-            const float qh = s_a[r] * s_q[r];
-            const float x4[4] = {reg[p].x, reg[p].y, reg[p].z, reg[p].w};
+        for (int p0 = 0; p0 < Map::P; p0 += G) {
+            float kh[G], qh[G];
+            lds_gather<G>(s_khg + r0 * Map::P + p0, kh);
+            lds_gather<G>(s_qhg + r0 * Map::P + p0, qh);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (kDelta) ax[c] = fmaf(x4[c], kh, ax[c]);
-                ao[c] = fmaf(x4[c], qh, ao[c]);
+            for (int pp = 0; pp < G; ++pp) {
+                const float4 xv = reg[p0 + pp];
+                const float x4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (kDelta) ax[c] = fmaf(x4[c], kh[pp], ax[c]);
+                    ao[c] = fmaf(x4[c], qh[pp], ao[c]);
+                }
             }
         }
 #pragma unroll
@@ -245,20 +303,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
                 x += s_red[w][0][j];
                 oo += s_red[w][1][j];
             }
-            for (int e = 0; e < m; ++e) {
-                float c = 0.f, d = 0.f;
+            // groups of 4 entries, unrolled and predicated (m is uniform), so
+            // the LDS reads of a group are issued together
 #pragma unroll
-                for (int g = 0; g < NSEG; ++g) {
-                    c += s_cpart[e][g];
-                    d += s_dpart[e][g];
+            for (int e0 = 0; e0 < ML; e0 += 4) {
+                if (e0 >= m) break;
+#pragma unroll
+                for (int e = e0; e < e0 + 4; ++e) {
+                if (e < m) {
+                    const float4 cd = *reinterpret_cast<const float4 *>(&s_cd[e][0]);
+                    float c = cd.x + cd.y, d = cd.z + cd.w;
+                    if (!kPerKey) {
+                        c *= s_fac[e];
+                        d *= s_fac[e];
+                    }
+                    const float ue = s_u[e * DV + j];
+                    x = fmaf(c, ue, x);
+                    oo = fmaf(d, ue, oo);
                 }
-                if (!kPerKey) {
-                    c *= s_fac[e];
-                    d *= s_fac[e];
                 }
-                const float ue = s_u[e * DV + j];
-                x = fmaf(c, ue, x);
-                oo = fmaf(d, ue, oo);
             }
             float dt = 0.f;
 #pragma unroll
@@ -283,20 +346,72 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (merge) {
         __syncthreads();
         const int ne = MODE == kMergeOnly ? m : m + 1;
+        constexpr int G = Map::P < 4 ? Map::P : 4;  // rows per LDS fetch
+        // The thread's offset passes through an empty asm statement so the
+        // store addresses are formed at the stores (scalar base + one vector
+        // offset) instead of being kept live as 64-bit VGPR pairs from the loads.
+        uint32_t off0 = tile_off(0);
+        asm volatile("" : "+v"(off0));
+        auto decay = [&](int p0) {  // rows p0 .. p0+G-1 of the thread
+            float ar[G];
+            lds_gather<G>(s_ag + r0 * Map::P + p0, ar);
 #pragma unroll
-        for (int p = 0; p < Map::P; ++p) {
-            const int r = r0 + p * Map::RPP;
-            const float ar = s_a[r];
-            float v0 = reg[p].x * ar, v1 = reg[p].y * ar, v2 = reg[p].z * ar, v3 = reg[p].w * ar;
-            for (int e = 0; e < ne; ++e) {
-                const float kt = (!kPerKey && e < m) ? s_kt[e * DK + r] * s_fac[e] : s_kt[e * DK + r];
-                const float4 ue = *reinterpret_cast<const float4 *>(s_u + e * DV + col);
-                v0 = fmaf(kt, ue.x, v0);
-                v1 = fmaf(kt, ue.y, v1);
-                v2 = fmaf(kt, ue.z, v2);
-                v3 = fmaf(kt, ue.w, v3);
+            for (int pp = 0; pp < G; ++pp) {
+                float4 &x = reg[p0 + pp];
+                x.x *= ar[pp];
+                x.y *= ar[pp];
+                x.z *= ar[pp];
+                x.w *= ar[pp];
             }
-            store_stream(S + (size_t)r * DV + col, make_float4(v0, v1, v2, v3));
+        };
+        auto entry_u = [&](int e) {  // u_e, times the scalar decay factor of a logged entry
+            float4 ue = *reinterpret_cast<const float4 *>(s_u + e * DV + col);
+            if (!kPerKey && e < m) {
+                const float f = s_fac[e];
+                ue = make_float4(ue.x * f, ue.y * f, ue.z * f, ue.w * f);
+            }
+            return ue;
+        };
+        auto rank1 = [&](int e, float4 ue, int p0) {  // rows p0.. += k~_e[row] u_e
+            float kt[G];
+            lds_gather<G>(s_ktg + e * DK + r0 * Map::P + p0, kt);
+#pragma unroll
+            for (int pp = 0; pp < G; ++pp) {
+                float4 &x = reg[p0 + pp];
+                x.x = fmaf(kt[pp], ue.x, x.x);
+                x.y = fmaf(kt[pp], ue.y, x.y);
+                x.z = fmaf(kt[pp], ue.z, x.z);
+                x.w = fmaf(kt[pp], ue.w, x.w);
+            }
+        };
+        auto store = [&](int p) {
+            store_base<MODE == kEager>(S + (off0 + (uint32_t)(p * Map::RPP * DV)), reg[p]);
+        };
+        if constexpr (MODE == kEager) {
+            // every tile is written, a copy-like stream: each group of rows is
+            // stored as soon as it is done, so the writes start early
+#pragma unroll
+            for (int p0 = 0; p0 < Map::P; p0 += G) {
+                decay(p0);
+                rank1(0, entry_u(0), p0);
+#pragma unroll
+                for (int pp = 0; pp < G; ++pp) store(p0 + pp);
+            }
+        } else {
+            // few merging tiles: the whole update (entries in order, each u_e
+            // read once), then the stores
+#pragma unroll
+            for (int p0 = 0; p0 < Map::P; p0 += G) decay(p0);
+#pragma unroll
+            for (int e = 0; e < ML + 1; ++e) {
+                if (e < ne) {
+                    const float4 ue = entry_u(e);
+#pragma unroll
+                    for (int p0 = 0; p0 < Map::P; p0 += G) rank1(e, ue, p0);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < Map::P; ++p) store(p);
         }
     }
 }
