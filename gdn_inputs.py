@@ -166,7 +166,7 @@ class SeqInputs:
 
 
 def seq_inputs(prefix_lens, branch_lens, branch_parent, H, dk, dv, *,
-               io="bf16", la_range=(-0.1, -0.001), conv=True, seed=0):
+               io="bf16", la_range=(-0.1, -0.001), conv=True, per_key=False, seed=0):
     rng = np.random.default_rng(seed)
     prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
     branch_lens = np.asarray(branch_lens, dtype=np.int64)
@@ -175,7 +175,8 @@ def seq_inputs(prefix_lens, branch_lens, branch_parent, H, dk, dv, *,
     q = unit_rows(rng.standard_normal((N, H, dk), dtype=np.float32))
     k = unit_rows(rng.standard_normal((N, H, dk), dtype=np.float32))
     v = rng.standard_normal((N, H, dv), dtype=np.float32)
-    log_alpha = rng.uniform(la_range[0], la_range[1], (N, H)).astype(np.float32)
+    la_shape = (N, H, dk) if per_key else (N, H)
+    log_alpha = rng.uniform(la_range[0], la_range[1], la_shape).astype(np.float32)
     beta = _sigmoid(rng.standard_normal((N, H)))
     conv_w = None
     if conv:

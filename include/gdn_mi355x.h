@@ -94,13 +94,21 @@ size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k,
  *     positions before the first token read init_window; no bias, no
  *     activation;
  *  2. if qk_l2norm: q, k <- y / sqrt(sum y^2 + 1e-6) per (token, head);
- *  3. the recurrence S_t = S_{t-1} a_t (I - b_t k_t k_t^T) + b_t v_t k_t^T
- *     ([GD]) from init_state, o_t = S_t q_t, in chunks of `chunk` tokens.
+ *  3. the recurrence from init_state, o_t = S_t q_t, in chunks of `chunk`
+ *     tokens: GDN_SCALAR S_t = S_{t-1} a_t (I - b_t k_t k_t^T) + b_t v_t k_t^T
+ *     ([GD]); GDN_KDA the same delta rule with a per-key decay,
+ *     S_t = S_{t-1} diag(a_t) (I - b_t k_t k_t^T) + b_t v_t k_t^T; GDN_RWKV6
+ *     the raw value update S_t = S_{t-1} diag(a_t) + v_t k_t^T ([DL] "커널
+ *     구현": the KDA and RWKV6 operators). a_t = exp(log_alpha).
+ *     Per-key decay is formed inside each chunk as exp(+-running sum of
+ *     log_alpha), so a chunk's total log-decay per key must stay above
+ *     about -80 (fp32 range).
  *
  *  q, k         [n_tokens, H, d_k]   io_dtype
  *  v            [n_tokens, H, d_v]   io_dtype
- *  log_alpha    [n_tokens, H]        fp32 (GDN_SCALAR only)
- *  beta         [n_tokens, H]        fp32
+ *  log_alpha    [n_tokens, H] fp32 (GDN_SCALAR) or [n_tokens, H, d_k] fp32
+ *               (GDN_KDA, GDN_RWKV6)
+ *  beta         [n_tokens, H]        fp32 (NULL allowed for GDN_RWKV6)
  *  cu_seqlens   [n_seq + 1]          int32, device; cu[0] = 0, non-decreasing,
  *                                    cu[n_seq] <= n_tokens
  *  conv_w       [CC, 4] fp32 or NULL (no convolution)
@@ -112,9 +120,10 @@ size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k,
  *                                    inputs (from init_window when the
  *                                    sequence is shorter than 3)
  *  chunk        64
+ *  variant      GDN_SCALAR, GDN_KDA or GDN_RWKV6
  *  workspace    >= gdn_prefill_workspace_bytes(n_tokens, n_seq, ...) bytes
  * Errors: INVALID_ARG (NULL required pointer, n_seq < 0, n_tokens < 0,
- * H < 1, bad dtype), UNSUPPORTED (d_k/d_v, chunk, variant), WORKSPACE.
+ * H < 1, bad dtype or variant), UNSUPPORTED (d_k/d_v, chunk), WORKSPACE.
  */
 int gdn_prefill_shared(const void *q, const void *k, const void *v,
                        const float *log_alpha, const float *beta,
@@ -123,7 +132,7 @@ int gdn_prefill_shared(const void *q, const void *k, const void *v,
                        const float *conv_w, int qk_l2norm,
                        const float *init_state, const void *init_window,
                        void *o, float *final_state, void *final_window,
-                       int io_dtype, int o_dtype, void *workspace,
+                       int variant, int io_dtype, int o_dtype, void *workspace,
                        size_t ws_bytes, void *stream);
 
 /*
@@ -153,8 +162,9 @@ int gdn_fork_branches(const void *q, const void *k, const void *v,
                       int d_k, int d_v, int chunk, const float *conv_w,
                       int qk_l2norm, const float *parent_state,
                       const void *parent_window, void *o, float *branch_state,
-                      void *branch_window, int io_dtype, int o_dtype,
-                      void *workspace, size_t ws_bytes, void *stream);
+                      void *branch_window, int variant, int io_dtype,
+                      int o_dtype, void *workspace, size_t ws_bytes,
+                      void *stream);
 
 /* ------------------------------------------------------------------ decode
  * gdn_decode_eager -- one decode step, materialised eagerly: the whole

@@ -29,9 +29,9 @@ SIGNATURES = {
     "gdn_max_log_capacity": (_I, []),
     "gdn_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "gdn_prefill_shared": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P,
-                                _P, _P, _P, _I, _I, _P, _S, _P]),
+                                _P, _P, _P, _I, _I, _I, _P, _S, _P]),
     "gdn_fork_branches": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I,
-                               _P, _P, _P, _P, _P, _I, _I, _P, _S, _P]),
+                               _P, _P, _P, _P, _P, _I, _I, _I, _P, _S, _P]),
     "gdn_decode_eager": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                               _P]),
     "deltalog_append_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
@@ -186,10 +186,17 @@ def _workspace(n_tokens, n_seq, H, dk, dv, chunk, device, workspace):
     return workspace, need
 
 
+def _la_shape(variant, N, H, dk):
+    return (N, H) if _variant(variant) == VARIANTS["gdn"] else (N, H, dk)
+
+
 def gdn_prefill_shared(q, k, v, log_alpha, beta, cu_seqlens, final_state, o=None,
                        conv_w=None, qk_l2norm=False, init_state=None, init_window=None,
-                       final_window=None, chunk=64, workspace=None, stream=None):
-    """Call 1 of the two-call fork: the shared contexts of a flat stream."""
+                       final_window=None, chunk=64, workspace=None, variant="gdn",
+                       stream=None):
+    """Call 1 of the two-call fork: the shared contexts of a flat stream.
+    variant "gdn" (scalar log_alpha [N,H]), "kda" or "rwkv6" (per-key
+    log_alpha [N,H,dk]; beta may be None for rwkv6)."""
     N, H, dk = q.shape
     dv = v.shape[-1]
     R = cu_seqlens.shape[0] - 1
@@ -198,8 +205,10 @@ def gdn_prefill_shared(q, k, v, log_alpha, beta, cu_seqlens, final_state, o=None
     ws, _ = _workspace(N, R, H, dk, dv, chunk, q.device, workspace)
     st = load().gdn_prefill_shared(
         _dev(q, "q", q.dtype, (N, H, dk)), _dev(k, "k", q.dtype, (N, H, dk)),
-        _dev(v, "v", q.dtype, (N, H, dv)), _dev(log_alpha, "log_alpha", _F32, (N, H)),
-        _dev(beta, "beta", _F32, (N, H)), _dev(cu_seqlens, "cu_seqlens", _I32, (R + 1,)),
+        _dev(v, "v", q.dtype, (N, H, dv)),
+        _dev(log_alpha, "log_alpha", _F32, _la_shape(variant, N, H, dk)),
+        _dev(beta, "beta", _F32, (N, H), optional=True),
+        _dev(cu_seqlens, "cu_seqlens", _I32, (R + 1,)),
         R, N, H, dk, dv, chunk, _dev(conv_w, "conv_w", _F32, (cc, 4), optional=True),
         int(bool(qk_l2norm)),
         _dev(init_state, "init_state", _F32, (R, H, dk, dv), optional=True),
@@ -207,15 +216,16 @@ def gdn_prefill_shared(q, k, v, log_alpha, beta, cu_seqlens, final_state, o=None
         _dev(o, "o", _IO, (N, H, dv), optional=True),
         _dev(final_state, "final_state", _F32, (R, H, dk, dv)),
         _dev(final_window, "final_window", q.dtype, (R, 3, cc), optional=True),
-        io, _io_code(o) if o is not None else GDN_F32, ws.data_ptr(), ws.numel(),
-        _stream(stream))
+        _variant(variant), io, _io_code(o) if o is not None else GDN_F32, ws.data_ptr(),
+        ws.numel(), _stream(stream))
     _check("gdn_prefill_shared", st)
 
 
 def gdn_fork_branches(q, k, v, log_alpha, beta, branch_cu, branch_parent, parent_state, o,
                       parent_window=None, branch_state=None, branch_window=None, conv_w=None,
-                      qk_l2norm=False, chunk=64, workspace=None, stream=None):
-    """Call 2 of the two-call fork: every branch from its request's saved state."""
+                      qk_l2norm=False, chunk=64, workspace=None, variant="gdn", stream=None):
+    """Call 2 of the two-call fork: every branch from its request's saved state
+    (variants as gdn_prefill_shared)."""
     N, H, dk = q.shape
     dv = v.shape[-1]
     NB = branch_cu.shape[0] - 1
@@ -225,8 +235,10 @@ def gdn_fork_branches(q, k, v, log_alpha, beta, branch_cu, branch_parent, parent
     ws, _ = _workspace(N, NB, H, dk, dv, chunk, q.device, workspace)
     st = load().gdn_fork_branches(
         _dev(q, "q", q.dtype, (N, H, dk)), _dev(k, "k", q.dtype, (N, H, dk)),
-        _dev(v, "v", q.dtype, (N, H, dv)), _dev(log_alpha, "log_alpha", _F32, (N, H)),
-        _dev(beta, "beta", _F32, (N, H)), _dev(branch_cu, "branch_cu", _I32, (NB + 1,)),
+        _dev(v, "v", q.dtype, (N, H, dv)),
+        _dev(log_alpha, "log_alpha", _F32, _la_shape(variant, N, H, dk)),
+        _dev(beta, "beta", _F32, (N, H), optional=True),
+        _dev(branch_cu, "branch_cu", _I32, (NB + 1,)),
         _dev(branch_parent, "branch_parent", _I32, (NB,)), NB, R, N, H, dk, dv, chunk,
         _dev(conv_w, "conv_w", _F32, (cc, 4), optional=True), int(bool(qk_l2norm)),
         _dev(parent_state, "parent_state", _F32, (R, H, dk, dv)),
@@ -234,5 +246,5 @@ def gdn_fork_branches(q, k, v, log_alpha, beta, branch_cu, branch_parent, parent
         _dev(o, "o", _IO, (N, H, dv)),
         _dev(branch_state, "branch_state", _F32, (NB, H, dk, dv), optional=True),
         _dev(branch_window, "branch_window", q.dtype, (NB, 3, cc), optional=True),
-        io, _io_code(o), ws.data_ptr(), ws.numel(), _stream(stream))
+        _variant(variant), io, _io_code(o), ws.data_ptr(), ws.numel(), _stream(stream))
     _check("gdn_fork_branches", st)

@@ -150,10 +150,12 @@ static int prefill_common(const void *q, const void *k, const void *v, const flo
                           int n_parent, int n_tokens, int H, int d_k, int d_v, int chunk,
                           const float *conv_w, int qk_l2norm, const float *state_in,
                           const void *win_in, void *o, float *state_out, void *win_out,
-                          int io_dtype, int o_dtype, void *workspace, size_t ws_bytes,
-                          void *stream) {
-    if (!q || !k || !v || !log_alpha || !beta || !cu) return GDN_ERR_INVALID_ARG;
-    if (!dtype_ok(io_dtype) || !dtype_ok(o_dtype)) return GDN_ERR_INVALID_ARG;
+                          int variant, int io_dtype, int o_dtype, void *workspace,
+                          size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !log_alpha || !cu) return GDN_ERR_INVALID_ARG;
+    if (!variant_ok(variant) || !dtype_ok(io_dtype) || !dtype_ok(o_dtype))
+        return GDN_ERR_INVALID_ARG;
+    if (variant != GDN_RWKV6 && !beta) return GDN_ERR_INVALID_ARG;
     if (n_seq < 0 || n_tokens < 0 || H < 1 || n_parent < 0) return GDN_ERR_INVALID_ARG;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || d_k != d_v) return GDN_ERR_UNSUPPORTED;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
@@ -181,6 +183,7 @@ static int prefill_common(const void *q, const void *k, const void *v, const flo
     a.H = H;
     a.qk_norm = qk_l2norm ? 1 : 0;
     a.chunk = chunk;
+    a.variant = variant;
     return from_hip(
         gdn::launch_prefill(d_k, d_v, io_dtype, o_dtype, a, static_cast<hipStream_t>(stream)));
 }
@@ -189,13 +192,13 @@ int gdn_prefill_shared(const void *q, const void *k, const void *v, const float 
                        const float *beta, const int32_t *cu_seqlens, int n_seq, int n_tokens,
                        int H, int d_k, int d_v, int chunk, const float *conv_w, int qk_l2norm,
                        const float *init_state, const void *init_window, void *o,
-                       float *final_state, void *final_window, int io_dtype, int o_dtype,
-                       void *workspace, size_t ws_bytes, void *stream) {
+                       float *final_state, void *final_window, int variant, int io_dtype,
+                       int o_dtype, void *workspace, size_t ws_bytes, void *stream) {
     if (!final_state) return GDN_ERR_INVALID_ARG;
     return prefill_common(q, k, v, log_alpha, beta, cu_seqlens, nullptr, n_seq, n_seq, n_tokens,
                           H, d_k, d_v, chunk, conv_w, qk_l2norm, init_state, init_window, o,
-                          final_state, final_window, io_dtype, o_dtype, workspace, ws_bytes,
-                          stream);
+                          final_state, final_window, variant, io_dtype, o_dtype, workspace,
+                          ws_bytes, stream);
 }
 
 int gdn_fork_branches(const void *q, const void *k, const void *v, const float *log_alpha,
@@ -203,13 +206,13 @@ int gdn_fork_branches(const void *q, const void *k, const void *v, const float *
                       int n_branch, int n_parent, int n_tokens, int H, int d_k, int d_v,
                       int chunk, const float *conv_w, int qk_l2norm, const float *parent_state,
                       const void *parent_window, void *o, float *branch_state,
-                      void *branch_window, int io_dtype, int o_dtype, void *workspace,
-                      size_t ws_bytes, void *stream) {
+                      void *branch_window, int variant, int io_dtype, int o_dtype,
+                      void *workspace, size_t ws_bytes, void *stream) {
     if (!branch_parent || !parent_state || !o) return GDN_ERR_INVALID_ARG;
     return prefill_common(q, k, v, log_alpha, beta, branch_cu, branch_parent, n_branch,
                           n_parent, n_tokens, H, d_k, d_v, chunk, conv_w, qk_l2norm,
-                          parent_state, parent_window, o, branch_state, branch_window, io_dtype,
-                          o_dtype, workspace, ws_bytes, stream);
+                          parent_state, parent_window, o, branch_state, branch_window, variant,
+                          io_dtype, o_dtype, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

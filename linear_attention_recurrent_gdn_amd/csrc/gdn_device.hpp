@@ -102,6 +102,7 @@ struct PrefillArgs {
     void *ws;
     size_t ws_bytes;
     int n_seq, n_parent, n_tokens, H, qk_norm, chunk;
+    int variant;            // Variant: scalar log a [N, H], or per-key [N, H, dk]
 };
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,

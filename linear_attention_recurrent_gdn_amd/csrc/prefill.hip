@@ -128,7 +128,7 @@ __device__ __forceinline__ void load8(const bf16 *p, float (&x)[8]) {
 //   K, Q [C][d_k]                     the conv'd, normalised chunk rows (A operands)
 //   K~^T [d_k][C]                     exp(g_L - g_r) k_r, transposed (B operand)
 struct RecLayout {
-    size_t thi, tlo, phi, plo, khi, klo, qhi, qlo, kthi, ktlo, elems;
+    size_t thi, tlo, phi, plo, khi, klo, qhi, qlo, kthi, ktlo, egl, elems;
 };
 
 __host__ __device__ constexpr RecLayout rec_layout(int dk) {
@@ -142,7 +142,8 @@ __host__ __device__ constexpr RecLayout rec_layout(int dk) {
                      4 * (size_t)C * C + 3 * (size_t)C * dk,
                      4 * (size_t)C * C + 4 * (size_t)C * dk,
                      4 * (size_t)C * C + 5 * (size_t)C * dk,
-                     4 * (size_t)C * C + 6 * (size_t)C * dk};
+                     4 * (size_t)C * C + 6 * (size_t)C * dk,
+                     4 * (size_t)C * C + 6 * (size_t)C * dk + 2 * (size_t)dk};
 }
 
 struct WsLayout {
@@ -416,8 +417,27 @@ __device__ __forceinline__ void stage_taps(const float *conv_w, int c0, int n, f
 }
 
 // ------------------------------------------------------------ prep
-template <int DK, int DV, typename TI>
+// DPP row shift within each 16-lane row: lane i gets lane i - N of its row,
+// lanes i < N get 0 (row_shr:N with bound_ctrl).
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+
+// VAR: the decay / update rule. kScalar: log a [N, H], the gated delta rule.
+// kKda: per-key log a [N, H, d_k], delta rule. kRwkv6: per-key log a, raw
+// value update (u = v: no A, T' = I, no K Sig term, beta unused).
+// Per-key chunk form (g_r[d] running sums per key): with K^ = K . e^{g},
+// K- = K . e^{-g}, Q^ = Q . e^{g}:
+//   A[r][s] = beta_r <K^_r, K-_s> (s < r),  P[r][s] = <Q^_r, K-_s> (s <= r),
+//   U = T' (V - K^ Sig0),  O = Q^ Sig0 + P U,
+//   Sig_L = diag(e^{g_L}) Sig0 + sum_r (k_r . e^{g_L - g_r}) u_r^T,
+// which the scan runs with gamma = 1 and a per-key state decay.
+template <int DK, int DV, typename TI, int VAR>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
+    constexpr bool kPerKey = VAR != kScalar;
+    constexpr bool kDelta = VAR != kRwkv6;
+    constexpr int KS = DK / 32;
     constexpr int KP = DK + 4;  // padded row of the staged K rows
     // staged K rows [C][KP]; then K~^T [DK][C + 1]; then T' [C][C + 1]
     constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
@@ -425,6 +445,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) float s_k[SK];
     __shared__ __attribute__((aligned(16))) float s_A[C * (C + 1)];  // strictly lower A
     __shared__ __attribute__((aligned(16))) float s_wq[DK * 4], s_wk[DK * 4];
+    __shared__ float s_gt[kPerKey ? kWaves * DK : 1];  // per-key: each wave's row-block sums
 
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
     const int gc = blockIdx.x, h = blockIdx.y;
@@ -451,12 +472,69 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
         stage_taps(a.conv_w, H * DK + h * DK, DK, s_wk);
     }
     __syncthreads();
-    const float g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
-    const float gL = __shfl(g, C - 1, kWave);
-    float b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
-    b_l = lane < cs.L ? b_l : 0.f;
     const int row = w * RB + lane % 16;  // this lane's row in the A layout
     const int cq = (lane / 16) * 8;
+    // scalar decay: g of row `lane`; per key: the factors of this lane's row
+    // and columns (A layout), e^{g}, e^{-g} and e^{g_L - g}
+    float g = 0.f, gL = 0.f;
+    float eg[KS][8], eng[KS][8], ekt[KS][8];
+    if constexpr (!kPerKey) {
+        g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
+        gL = __shfl(g, C - 1, kWave);
+    } else {
+        // log a of this lane's row (rows >= L add nothing), then an inclusive
+        // scan over the wave's 16 rows (DPP within 16-lane rows) plus the
+        // sums of the earlier waves' row blocks
+        const float *lap =
+            a.log_alpha + ((size_t)(cs.seq0 + cs.p0 + min(row, cs.L - 1)) * H + h) * DK;
+        float gk[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load8(lap + ks * 32 + cq, gk[ks]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = row < cs.L ? gk[ks][e] : 0.f;
+                x += row_shr<1>(x);
+                x += row_shr<2>(x);
+                x += row_shr<4>(x);
+                x += row_shr<8>(x);
+                gk[ks][e] = x;
+            }
+        if (lane % 16 == 15)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_gt[w * DK + ks * 32 + cq + e] = gk[ks][e];
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = ks * 32 + cq + e;
+                float before = 0.f, total = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    const float t = s_gt[ww * DK + d];
+                    before += ww < w ? t : 0.f;
+                    total += t;
+                }
+                const float gr = gk[ks][e] + before;
+                eg[ks][e] = expf(gr);
+                eng[ks][e] = expf(-gr);
+                ekt[ks][e] = expf(total - gr);
+            }
+        // e^{g_L} per key for the scan's state decay
+        if (tid < DK) {
+            float total = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) total += s_gt[ww * DK + tid];
+            reinterpret_cast<float *>(rec + RL.egl)[tid] = expf(total);
+        }
+    }
+    float b_l = 1.f;
+    if constexpr (kDelta) b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
+    b_l = lane < cs.L ? b_l : 0.f;
 
     // conv'd, normalised Q and K rows; their split A operands go to the record
     Split8 qa[DK / 32], ka[DK / 32];
@@ -466,6 +544,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
                            conv ? s_wq : nullptr, a.qk_norm != 0, qf);
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks) {
+            if constexpr (kPerKey)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[ks][e] *= eg[ks][e];  // Q^
             qa[ks] = split8(qf[ks]);
             const size_t off = (size_t)row * DK + ks * 32 + cq;
             *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
@@ -477,12 +558,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
                        conv ? s_wk : nullptr, a.qk_norm != 0, kf);
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-        ka[ks] = split8(kf[ks]);
+        // A operand of KK^T and the scan's K Sig term: K (scalar decay), K^
+        // (per key), nothing (raw value update: the record row is zero)
+        float ak[8], bk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ak[e] = kPerKey ? (kDelta ? kf[ks][e] * eg[ks][e] : 0.f) : kf[ks][e];
+            bk[e] = kPerKey ? kf[ks][e] * eng[ks][e] : kf[ks][e];  // B operand rows: K or K-
+        }
+        ka[ks] = split8(ak);
         const size_t off = (size_t)row * DK + ks * 32 + cq;
         *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
         *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_k[row * KP + ks * 32 + cq + e] = kf[ks][e];
+        for (int e = 0; e < 8; ++e) s_k[row * KP + ks * 32 + cq + e] = bk[e];
     }
     __syncthreads();
 
@@ -508,8 +597,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
             const float g_r = __shfl(g, r, kWave);
             const float b_r = __shfl(b_l, r, kWave);
             const bool live = r < cs.L && col < cs.L;
-            const float dec = (live && col <= r) ? expf(g_r - g_c) : 0.f;
-            s_A[r * (C + 1) + col] = col < r ? b_r * dec * kk[i] : 0.f;
+            // the decay between rows: a factor here (scalar), inside the
+            // products already (per key)
+            const float dec = (live && col <= r) ? (kPerKey ? 1.f : expf(g_r - g_c)) : 0.f;
+            s_A[r * (C + 1) + col] = (kDelta && col < r) ? b_r * dec * kk[i] : 0.f;
             split1(dec * qk[i], rec[RL.phi + r * C + col], rec[RL.plo + r * C + col]);
         }
     }
@@ -517,11 +608,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
 
     // K~^T[d][r] = exp(g_L - g_r) k_r[d], staged transposed for coalesced stores
     {
-        const float f = expf(gL - __shfl(g, row, kWave));
+        const float f = kPerKey ? 1.f : expf(gL - __shfl(g, row, kWave));
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_k[(ks * 32 + cq + e) * (C + 1) + row] = kf[ks][e] * f;
+            for (int e = 0; e < 8; ++e)
+                s_k[(ks * 32 + cq + e) * (C + 1) + row] = kf[ks][e] * (kPerKey ? ekt[ks][e] : f);
     }
     __syncthreads();
     for (int idx = tid; idx < DK * C; idx += kThreads)
@@ -585,20 +677,25 @@ __device__ __forceinline__ void lds_dma16(const __bf16 *g, __bf16 *lds) {
     __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
-template <int KS, int NVT, typename TI>
+template <int KS, int NVT, typename TI, int NEG>
 struct ChunkRegs {
     Split8 ka[KS], qa[KS], ta[2], pa[2];
     TI vraw[NVT][7];  // raw V rows r0-3 .. r0+3 of this lane's columns
-    float la;         // log a of row `lane` (clamped)
+    float la;         // scalar decay: log a of row `lane` (clamped)
+    float egl[NEG];   // per-key decay: e^{g_L} of this lane's state columns
 };
 
-template <int DK, int DV, typename TI, typename TO>
+// PK: per-key decay (K and Q arrive pre-scaled, gamma = 1; the state decays
+// by e^{g_L} per key column).
+template <int DK, int DV, typename TI, typename TO, bool PK>
 __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     constexpr int KS = DK / 32;          // k-steps over d_k
     constexpr int SP = DK + 4;           // padded row of Sig^T (fp32)
     constexpr int CB = C + 8;            // padded row of the R^T / U^T planes
     constexpr int NVT = TV / 16;         // 16-wide value sub-tiles
     constexpr int NFT = NVT * (DK / 16); // output tiles of the state update
+    constexpr int NEG = NFT / kWaves;    // state-update tiles per wave
+    static_assert(NFT % kWaves == 0, "state-update tiles split evenly over the waves");
     constexpr RecLayout RL = rec_layout(DK);
     // Sig^T tile [TV][DK] in fp32; R^T and U^T [TV][C] as hi / lo bf16
     // planes (split once when written); K~^T [DK][C] hi / lo planes copied
@@ -662,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
                ((size_t)(cs0 + c) * H + h) * wl.rec_elems;
     };
     // loads only: every address is clamped in bounds, nothing is consumed here
-    auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI> &r) {
+    auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI, NEG> &r) {
         const __bf16 *rec = record(c);
         const int p0 = c * C, L = min(C, sp.len - p0);
 #pragma unroll
@@ -690,7 +787,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
                 r.vraw[t][q] = *ptr;
             }
         }
-        r.la = a.log_alpha[(size_t)(sp.start + p0 + min(lane, L - 1)) * H + h];
+        if constexpr (PK) {
+            const float *egl = reinterpret_cast<const float *>(rec + RL.egl);
+#pragma unroll
+            for (int m = 0; m < NEG; ++m)
+                r.egl[m] = egl[((w + m * kWaves) / NVT) * 16 + lane % 16];
+            r.la = 0.f;
+        } else {
+            r.la = a.log_alpha[(size_t)(sp.start + p0 + min(lane, L - 1)) * H + h];
+        }
     };
     // K~^T hi / lo planes of chunk c into LDS (direct-to-LDS, 16 B per lane;
     // the LDS position of a lane's bytes is fixed, so the swizzle is applied
@@ -709,11 +814,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
         }
     };
 
-    ChunkRegs<KS, NVT, TI> nxt;
+    ChunkRegs<KS, NVT, TI, NEG> nxt;
     if (nchunks > 0) load_regs(0, nxt);
     for (int c = 0; c < nchunks; ++c) {
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
-        const ChunkRegs<KS, NVT, TI> cur = nxt;
+        const ChunkRegs<KS, NVT, TI, NEG> cur = nxt;
         load_kt(c);
 
         // g (running log a over the chunk rows; rows >= L add nothing)
@@ -726,7 +831,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
         const float gL = __shfl(g, C - 1, kWave);
         float gam[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gam[i] = expf(__shfl(g, r0v + i, kWave));
+        for (int i = 0; i < 4; ++i) gam[i] = PK ? 1.f : expf(__shfl(g, r0v + i, kWave));
 
         // conv'd V entries of this lane (C/D layout), from the raw rows
         float vf[NVT][4];
@@ -828,12 +933,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
 
         // Sig^T <- gamma_L Sig^T + U^T K~   (tiles: value sub-tile x 16 keys)
         const float gamL = expf(gL);
-        for (int ft = w; ft < NFT; ft += kWaves) {
+#pragma unroll
+        for (int m = 0; m < NEG; ++m) {
+            const int ft = w + m * kWaves;
             const int t = ft % NVT, dt = ft / NVT;
+            const float dec = PK ? cur.egl[m] : gamL;  // per key: e^{g_L} of column dt*16 + lane%16
             f32x4v acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                acc[i] = gamL * s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16];
+                acc[i] = dec * s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16];
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
                 const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
@@ -883,6 +991,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
 
 template <int D, typename TI, typename TO>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
+    auto prep = [&](auto vtag) {
+        constexpr int VAR = decltype(vtag)::value;
+        return prep_kernel<D, D, TI, VAR>;
+    };
     if (a.n_seq == 0) return hipSuccess;
     const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, D);
     int32_t *chunk_start = static_cast<int32_t *>(a.ws);
@@ -891,14 +1003,27 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wl.max_chunks > 0) {
-        hipLaunchKernelGGL((prep_kernel<D, D, TI>), dim3((unsigned)wl.max_chunks, a.H),
-                           dim3(kThreads), 0, stream, a);
+        const dim3 grid((unsigned)wl.max_chunks, a.H);
+        if (a.variant == kKda)
+            hipLaunchKernelGGL(prep(std::integral_constant<int, kKda>{}), grid, dim3(kThreads), 0,
+                               stream, a);
+        else if (a.variant == kRwkv6)
+            hipLaunchKernelGGL(prep(std::integral_constant<int, kRwkv6>{}), grid, dim3(kThreads),
+                               0, stream, a);
+        else
+            hipLaunchKernelGGL(prep(std::integral_constant<int, kScalar>{}), grid, dim3(kThreads),
+                               0, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const size_t n_sh = (size_t)a.n_seq * a.H;
     const unsigned blocks = (unsigned)(((n_sh + 7) / 8) * 8 * (D / TV));  // see scan_unit
-    hipLaunchKernelGGL((scan_kernel<D, D, TI, TO>), dim3(blocks), dim3(kThreads), 0, stream, a);
+    if (a.variant == kScalar)
+        hipLaunchKernelGGL((scan_kernel<D, D, TI, TO, false>), dim3(blocks), dim3(kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((scan_kernel<D, D, TI, TO, true>), dim3(blocks), dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -102,17 +102,23 @@ def test_prefill_validation_and_workspace(lib):
     need = lib.gdn_prefill_workspace_bytes(1000, 3, 4, 128, 128, 64)
     assert need > 0
 
-    def call(ws=FAKE, ws_bytes=need, chunk=64, final=FAKE, cu=FAKE, d=128):
-        return lib.gdn_prefill_shared(FAKE, FAKE, FAKE, FAKE, FAKE, cu, 3, 1000, 4, d, d, chunk,
-                                      NULL, 0, NULL, NULL, FAKE, final, NULL, 1, 0, ws, ws_bytes,
-                                      NULL)
+    def call(ws=FAKE, ws_bytes=need, chunk=64, final=FAKE, cu=FAKE, d=128, beta=FAKE,
+             variant=0):
+        return lib.gdn_prefill_shared(FAKE, FAKE, FAKE, FAKE, beta, cu, 3, 1000, 4, d, d, chunk,
+                                      NULL, 0, NULL, NULL, FAKE, final, NULL, variant, 1, 0, ws,
+                                      ws_bytes, NULL)
     assert call(final=NULL) == INVALID
     assert call(cu=NULL) == INVALID
+    assert call(variant=3) == INVALID
+    assert call(variant=-1) == INVALID
+    # beta is required by the delta-rule variants (may be NULL only for RWKV6)
+    assert call(beta=NULL, variant=0) == INVALID
+    assert call(beta=NULL, variant=1) == INVALID
     assert call(chunk=48) == UNSUPPORTED
     assert call(d=80) == UNSUPPORTED
     assert call(ws=NULL) == WORKSPACE
     assert call(ws_bytes=need - 1) == WORKSPACE
     # fork: the parent state and o are required
     assert lib.gdn_fork_branches(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 100, 4, 128, 128,
-                                 64, NULL, 0, NULL, NULL, FAKE, NULL, NULL, 1, 0, FAKE, need,
+                                 64, NULL, 0, NULL, NULL, FAKE, NULL, NULL, 0, 1, 0, FAKE, need,
                                  NULL) == INVALID

@@ -57,45 +57,49 @@ def window_ref(win64, io):
     return win64.astype(np.float32)
 
 
-def run_fork(inp, *, init_state=None, init_window=None, o_dtype=torch.float32):
+def run_fork(inp, *, init_state=None, init_window=None, o_dtype=torch.float32, variant="gdn"):
     """Both calls on the GPU; returns host copies of every output."""
     H, dk, dv, Np = inp.H, inp.dk, inp.dv, inp.Np
     R, NB = len(inp.cu_seqlens) - 1, len(inp.branch_cu) - 1
     cc = H * (2 * dk + dv)
     io_dtype = torch.bfloat16 if inp.io == "bf16" else torch.float32
     q, k, v = (dev_io(getattr(inp, n), getattr(inp, n + "_bits")) for n in "qkv")
-    la, beta = f32(inp.log_alpha), f32(inp.beta)
+    la = f32(inp.log_alpha)
+    beta = None if variant == "rwkv6" else f32(inp.beta)  # beta may be NULL for RWKV6
+    pick = lambda x, sl: None if x is None else x[sl]  # noqa: E731
     conv_w = None if inp.conv_w is None else f32(inp.conv_w)
     o_p = torch.full((Np, H, dv), float("nan"), device=DEV, dtype=o_dtype)
     st = torch.full((R, H, dk, dv), float("nan"), device=DEV)
     win = torch.zeros((R, 3, cc), device=DEV, dtype=io_dtype)
-    gdn.gdn_prefill_shared(q[:Np], k[:Np], v[:Np], la[:Np], beta[:Np], i32(inp.cu_seqlens), st,
-                           o=o_p, conv_w=conv_w, qk_l2norm=conv_w is not None,
+    gdn.gdn_prefill_shared(q[:Np], k[:Np], v[:Np], la[:Np], pick(beta, slice(None, Np)),
+                           i32(inp.cu_seqlens), st, o=o_p, conv_w=conv_w,
+                           qk_l2norm=conv_w is not None,
                            init_state=None if init_state is None else f32(init_state),
-                           init_window=init_window, final_window=win)
+                           init_window=init_window, final_window=win, variant=variant)
     Nb = inp.Nb
     o_b = torch.full((Nb, H, dv), float("nan"), device=DEV, dtype=o_dtype)
     st_b = torch.full((NB, H, dk, dv), float("nan"), device=DEV)
     win_b = torch.zeros((NB, 3, cc), device=DEV, dtype=io_dtype)
     if NB > 0:
-        gdn.gdn_fork_branches(q[Np:], k[Np:], v[Np:], la[Np:], beta[Np:], i32(inp.branch_cu),
-                              i32(inp.branch_parent), st, o_b, parent_window=win,
-                              branch_state=st_b, branch_window=win_b, conv_w=conv_w,
-                              qk_l2norm=conv_w is not None)
+        gdn.gdn_fork_branches(q[Np:], k[Np:], v[Np:], la[Np:], pick(beta, slice(Np, None)),
+                              i32(inp.branch_cu), i32(inp.branch_parent), st, o_b,
+                              parent_window=win, branch_state=st_b, branch_window=win_b,
+                              conv_w=conv_w, qk_l2norm=conv_w is not None, variant=variant)
     torch.cuda.synchronize()
     return dict(o_p=o_p.float().cpu().numpy(), st=st.cpu().numpy(), win=win,
                 o_b=o_b.float().cpu().numpy(), st_b=st_b.cpu().numpy(), win_b=win_b)
 
 
-def run_oracle(inp, *, init_state=None, init_window=None):
+def run_oracle(inp, *, init_state=None, init_window=None, variant="gdn"):
     Np = inp.Np
     conv = inp.conv_w is not None
     o_p, st, win = oracle.prefill(inp.q[:Np], inp.k[:Np], inp.v[:Np], inp.log_alpha[:Np],
                                   inp.beta[:Np], inp.cu_seqlens, conv_w=inp.conv_w,
-                                  qk_norm=conv, state_in=init_state, win_in=init_window)
+                                  qk_norm=conv, state_in=init_state, win_in=init_window,
+                                  variant=variant)
     o_b, st_b, win_b = oracle.fork(inp.q[Np:], inp.k[Np:], inp.v[Np:], inp.log_alpha[Np:],
                                    inp.beta[Np:], inp.branch_cu, inp.branch_parent, st, win,
-                                   conv_w=inp.conv_w, qk_norm=conv)
+                                   conv_w=inp.conv_w, qk_norm=conv, variant=variant)
     return dict(o_p=o_p, st=st, win=win, o_b=o_b, st_b=st_b, win_b=win_b)
 
 
@@ -147,6 +151,47 @@ def test_ragged_fork_with_conv(d, io):
     g = run_fork(inp, init_state=s0, init_window=w0_dev)
     r = run_oracle(inp, init_state=s0, init_window=w0)
     compare(g, r, inp, TOL if io == "bf16" else TOL_F32)
+
+
+@pytest.mark.parametrize("variant", ["kda", "rwkv6"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_ragged_fork_per_key(variant, d, io):
+    """Per-key decay (KDA delta rule, RWKV6-style raw value update): the
+    ragged layout of test_ragged_fork_with_conv, per-key log a ~ U(-0.1,
+    -0.001), random initial states and windows, conv + q/k norm; RWKV6 runs
+    with beta = NULL."""
+    prefix = [0, 1, 2, 3, 64, 65, 130, 200]
+    branches = [5, 0, 1, 2, 64, 70, 3, 9, 1, 128]
+    parent = [0, 1, 2, 3, 4, 5, 6, 7, 7, 4]
+    H = 2
+    inp = gi.seq_inputs(prefix, branches, parent, H, d, d, io=io, conv=True, per_key=True,
+                        seed=d + 7)
+    rng = np.random.default_rng(d + 8)
+    R = len(prefix)
+    cc = H * 3 * d
+    s0 = (rng.standard_normal((R, H, d, d)) * 0.1).astype(np.float32)
+    w0 = rng.standard_normal((R, 3, cc)).astype(np.float32)
+    if io == "bf16":
+        wbits, w0 = gi.bf16_round(w0)
+        w0_dev = torch.from_numpy(wbits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        w0_dev = f32(w0)
+    g = run_fork(inp, init_state=s0, init_window=w0_dev, variant=variant)
+    r = run_oracle(inp, init_state=s0, init_window=w0, variant=variant)
+    compare(g, r, inp, TOL if io == "bf16" else TOL_F32)
+
+
+@pytest.mark.parametrize("variant", ["kda", "rwkv6"])
+def test_long_context_per_key(variant):
+    """Per-key decay over long contexts (16+ chunks per sequence), H=4,
+    d=128, bf16, conv: errors must not grow with the number of chunks."""
+    prefix = [1100, 1024, 64]
+    branches = [64, 64, 33, 64]
+    parent = [0, 1, 2, 0]
+    inp = gi.seq_inputs(prefix, branches, parent, 4, 128, 128, io="bf16", conv=True,
+                        per_key=True, seed=11)
+    compare(run_fork(inp, variant=variant), run_oracle(inp, variant=variant), inp, TOL)
 
 
 def test_fork_is_bitwise_the_full_run_at_chunk_boundaries():
