@@ -149,11 +149,11 @@ def schedule_bytes(phase, H, M, first, K):
 
 
 # ---------------------------------------------------------------- fork
-def bench_fork(torch, gdn, gi, reps):
+def bench_fork(torch, gdn, gi, reps, variant="gdn"):
     w = gi.WORKLOADS["fork_prefill"]
     R, H, d = w["R"], w["H"], w["d"]
     pl, bl, par = gi.fork_layout(R, w["prefix"], w["branches_per_req"], w["branch_len"])
-    t = gi.torch_seq_inputs(pl, bl, par, H, d, d, conv=True, seed=0)
+    t = gi.torch_seq_inputs(pl, bl, par, H, d, d, conv=True, per_key=variant != "gdn", seed=0)
     Np, Nb, NB = t["Np"], t["Nb"], len(bl)
     cc = H * 3 * d
     dev = "cuda"
@@ -168,13 +168,13 @@ def bench_fork(torch, gdn, gi, reps):
     def prefill():
         gdn.gdn_prefill_shared(t["q"][:Np], t["k"][:Np], t["v"][:Np], t["log_alpha"][:Np],
                                t["beta"][:Np], t["cu_seqlens"], st, o=o_p, conv_w=t["conv_w"],
-                               qk_l2norm=True, final_window=win, workspace=ws)
+                               qk_l2norm=True, final_window=win, workspace=ws, variant=variant)
 
     def fork():
         gdn.gdn_fork_branches(t["q"][Np:], t["k"][Np:], t["v"][Np:], t["log_alpha"][Np:],
                               t["beta"][Np:], t["branch_cu"], t["branch_parent"], st, o_b,
                               parent_window=win, conv_w=t["conv_w"], qk_l2norm=True,
-                              workspace=ws)
+                              workspace=ws, variant=variant)
 
     prefill()
     fork()
@@ -304,10 +304,12 @@ def main():
     eager_gbps = eager_bytes() * head_steps / (te.ms / 1e3) / 1e9
     eager_writes = STATE_B * head_steps
 
-    fork = None
+    fork = fork_kda = None
     if not args.no_fork:
         log("two-call fork ...")
         fork = bench_fork(torch, gdn, gi, args.fork_reps)
+        log("two-call fork, per-key decay (KDA) ...")
+        fork_kda = bench_fork(torch, gdn, gi, args.fork_reps, variant="kda")
 
     probe = hbm_probe(torch, stream)
 
@@ -356,6 +358,7 @@ def main():
             "deferred": state_writes / head_steps, "eager": eager_writes / head_steps,
             "ratio": eager_writes / state_writes},
         "fork": fork,
+        "fork_kda": fork_kda,
         "hbm_probe": probe,
         "cpu_baseline": cpu,
     }

@@ -252,7 +252,7 @@ def torch_decode_inputs(B, H, dk, dv, steps, *, per_key=False, device="cuda",
 
 
 def torch_seq_inputs(prefix_lens, branch_lens, branch_parent, H, dk, dv, *, conv=True,
-                     device="cuda", la_range=(-0.1, -0.001), seed=0):
+                     device="cuda", la_range=(-0.1, -0.001), per_key=False, seed=0):
     """Full-size flat-stream inputs drawn on the device (same distributions
     and draw order as `seq_inputs`; q/k/v bf16, the rest float32)."""
     import torch
@@ -271,7 +271,8 @@ def torch_seq_inputs(prefix_lens, branch_lens, branch_parent, H, dk, dv, *, conv
     k = unit((N, H, dk))
     v = torch.randn((N, H, dv), generator=g, device=device, dtype=f32).to(torch.bfloat16)
     lo, hi = la_range
-    log_alpha = torch.rand((N, H), generator=g, device=device, dtype=f32) * (hi - lo) + lo
+    la_shape = (N, H, dk) if per_key else (N, H)
+    log_alpha = torch.rand(la_shape, generator=g, device=device, dtype=f32) * (hi - lo) + lo
     beta = torch.sigmoid(torch.randn((N, H), generator=g, device=device, dtype=f32))
     conv_w = None
     if conv:
