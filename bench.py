@@ -193,6 +193,55 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
                 prefix_token_heads_per_s=Np * H / (tp_ms / 1e3))
 
 
+# ---------------------------------------------------------------- decode_small
+def bench_decode_small(torch, gdn, gi, reps=5):
+    """The small decode workload (B=64, H=16, d=128: a 64 MiB state that the
+    256 MB last-level cache holds), deferred M=8 over 256 steps, launched one
+    call at a time and as one captured HIP graph replayed; the steps are
+    short enough that launch gaps matter."""
+    w = gi.WORKLOADS["decode_small"]
+    B, H, d, T, M = w["B"], w["H"], w["d"], w["steps"], 8
+    t = gi.torch_decode_inputs(B, H, d, d, T, seed=0)
+    base = t["state0"].clone()
+    logs = dict(log_u=torch.zeros((B, H, M, d), device="cuda"),
+                log_k=torch.zeros((B, H, M, d), device="cuda", dtype=torch.bfloat16),
+                log_lam=torch.zeros((B, H, M), device="cuda"),
+                log_len=torch.zeros((B, H), device="cuda", dtype=torch.int32))
+    o = torch.empty((B, H, d), device="cuda")
+
+    def steps():
+        run_deferred(torch, gdn, t, logs, base, o, M, range(T))
+
+    stream = torch.cuda.current_stream()
+    steps()
+    plain = []
+    for _ in range(reps):
+        with Timer(torch, stream) as a:
+            steps()
+        plain.append(a.ms)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        steps()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    graph.replay()
+    graphed = []
+    for _ in range(reps):
+        with Timer(torch, stream) as a:
+            graph.replay()
+        graphed.append(a.ms)
+    hs = B * H * T
+    p_ms, g_ms = float(np.median(plain)), float(np.median(graphed))
+    return dict(workload="decode_small: deferred M=8, B=64, H=16, d=128, 256 steps "
+                         "(64 MiB state, cache-resident)",
+                plain_head_steps_per_s=hs / (p_ms / 1e3), plain_us_per_step=p_ms * 1e3 / T,
+                graph_head_steps_per_s=hs / (g_ms / 1e3), graph_us_per_step=g_ms * 1e3 / T)
+
+
 # ---------------------------------------------------------------- HBM probe
 def hbm_probe(torch, stream, nbytes=4 << 30, reps=5):
     """Attainable HBM bandwidth on this GPU: a plain device copy (read +
@@ -311,6 +360,9 @@ def main():
         log("two-call fork, per-key decay (KDA) ...")
         fork_kda = bench_fork(torch, gdn, gi, args.fork_reps, variant="kda")
 
+    log("decode_small, plain launches and one captured graph ...")
+    small = bench_decode_small(torch, gdn, gi)
+
     probe = hbm_probe(torch, stream)
 
     cpu = None
@@ -359,6 +411,7 @@ def main():
             "ratio": eager_writes / state_writes},
         "fork": fork,
         "fork_kda": fork_kda,
+        "decode_small": small,
         "hbm_probe": probe,
         "cpu_baseline": cpu,
     }
