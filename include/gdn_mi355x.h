@@ -136,6 +136,36 @@ int gdn_prefill_shared(const void *q, const void *k, const void *v,
                        size_t ws_bytes, void *stream);
 
 /*
+ * gdn_prefill_checkpointed -- gdn_prefill_shared that also keeps the state
+ * and convolution window at internal positions of every sequence ([FL]
+ * "연구방법을 단계별로": incremental checkpoints within a long history, so a
+ * later request sharing a prefix of it resumes from the nearest one -- by
+ * passing the checkpoint as init_state / init_window of a new call).
+ * Checkpoint j (0 <= j < ckpt_cap) of sequence r is the state and window
+ * after its first (j + 1) * ckpt_every * chunk tokens; it is written when
+ * that position is inside the sequence or at its end, and left untouched
+ * otherwise.
+ *
+ *  ckpt_every  chunks between checkpoints, >= 1
+ *  ckpt_cap    checkpoints per sequence the buffers hold, >= 0
+ *  ckpt_state  [n_seq, ckpt_cap, H, d_k, d_v] fp32 (required when ckpt_cap > 0)
+ *  ckpt_window [n_seq, ckpt_cap, 3, CC] io_dtype, or NULL (not written)
+ * Everything else as gdn_prefill_shared. Errors as gdn_prefill_shared, and
+ * INVALID_ARG for ckpt_every < 1, ckpt_cap < 0 or a missing ckpt_state.
+ */
+int gdn_prefill_checkpointed(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta,
+                             const int32_t *cu_seqlens, int n_seq, int n_tokens,
+                             int H, int d_k, int d_v, int chunk,
+                             const float *conv_w, int qk_l2norm,
+                             const float *init_state, const void *init_window,
+                             void *o, float *final_state, void *final_window,
+                             int ckpt_every, int ckpt_cap, float *ckpt_state,
+                             void *ckpt_window, int variant, int io_dtype,
+                             int o_dtype, void *workspace, size_t ws_bytes,
+                             void *stream);
+
+/*
  * gdn_fork_branches -- call 2 of the two-call fork ([FL] method step 2;
  * glossary "ForkAttention": in GDN layers each branch forks exactly from
  * the shared state by a second call plus state indexing). Branch b

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     deltalog_merge,
     gdn_decode_eager,
     gdn_fork_branches,
+    gdn_prefill_checkpointed,
     gdn_prefill_shared,
     load,
     prefill_workspace_bytes,

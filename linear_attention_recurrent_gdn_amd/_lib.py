@@ -30,6 +30,9 @@ SIGNATURES = {
     "gdn_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "gdn_prefill_shared": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P,
                                 _P, _P, _P, _I, _I, _I, _P, _S, _P]),
+    "gdn_prefill_checkpointed": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I,
+                                      _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _S,
+                                      _P]),
     "gdn_fork_branches": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I,
                                _P, _P, _P, _P, _P, _I, _I, _I, _P, _S, _P]),
     "gdn_decode_eager": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -219,6 +222,40 @@ def gdn_prefill_shared(q, k, v, log_alpha, beta, cu_seqlens, final_state, o=None
         _variant(variant), io, _io_code(o) if o is not None else GDN_F32, ws.data_ptr(),
         ws.numel(), _stream(stream))
     _check("gdn_prefill_shared", st)
+
+
+def gdn_prefill_checkpointed(q, k, v, log_alpha, beta, cu_seqlens, final_state, ckpt_every,
+                             ckpt_state, o=None, ckpt_window=None, conv_w=None, qk_l2norm=False,
+                             init_state=None, init_window=None, final_window=None, chunk=64,
+                             workspace=None, variant="gdn", stream=None):
+    """Call 1 that also keeps checkpoints: ckpt_state[r, j] (and ckpt_window)
+    = the state (window) after (j + 1) * ckpt_every * chunk tokens of
+    sequence r, when that is inside the sequence or its end."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    R = cu_seqlens.shape[0] - 1
+    cap = ckpt_state.shape[1]
+    cc = H * (2 * dk + dv)
+    io = _io_code(q)
+    ws, _ = _workspace(N, R, H, dk, dv, chunk, q.device, workspace)
+    st = load().gdn_prefill_checkpointed(
+        _dev(q, "q", q.dtype, (N, H, dk)), _dev(k, "k", q.dtype, (N, H, dk)),
+        _dev(v, "v", q.dtype, (N, H, dv)),
+        _dev(log_alpha, "log_alpha", _F32, _la_shape(variant, N, H, dk)),
+        _dev(beta, "beta", _F32, (N, H), optional=True),
+        _dev(cu_seqlens, "cu_seqlens", _I32, (R + 1,)),
+        R, N, H, dk, dv, chunk, _dev(conv_w, "conv_w", _F32, (cc, 4), optional=True),
+        int(bool(qk_l2norm)),
+        _dev(init_state, "init_state", _F32, (R, H, dk, dv), optional=True),
+        _dev(init_window, "init_window", q.dtype, (R, 3, cc), optional=True),
+        _dev(o, "o", _IO, (N, H, dv), optional=True),
+        _dev(final_state, "final_state", _F32, (R, H, dk, dv)),
+        _dev(final_window, "final_window", q.dtype, (R, 3, cc), optional=True),
+        int(ckpt_every), cap, _dev(ckpt_state, "ckpt_state", _F32, (R, cap, H, dk, dv)),
+        _dev(ckpt_window, "ckpt_window", q.dtype, (R, cap, 3, cc), optional=True),
+        _variant(variant), io, _io_code(o) if o is not None else GDN_F32, ws.data_ptr(),
+        ws.numel(), _stream(stream))
+    _check("gdn_prefill_checkpointed", st)
 
 
 def gdn_fork_branches(q, k, v, log_alpha, beta, branch_cu, branch_parent, parent_state, o,

@@ -151,7 +151,8 @@ static int prefill_common(const void *q, const void *k, const void *v, const flo
                           const float *conv_w, int qk_l2norm, const float *state_in,
                           const void *win_in, void *o, float *state_out, void *win_out,
                           int variant, int io_dtype, int o_dtype, void *workspace,
-                          size_t ws_bytes, void *stream) {
+                          size_t ws_bytes, void *stream, int ckpt_every = 0, int ckpt_cap = 0,
+                          float *ckpt_state = nullptr, void *ckpt_window = nullptr) {
     if (!q || !k || !v || !log_alpha || !cu) return GDN_ERR_INVALID_ARG;
     if (!variant_ok(variant) || !dtype_ok(io_dtype) || !dtype_ok(o_dtype))
         return GDN_ERR_INVALID_ARG;
@@ -184,6 +185,10 @@ static int prefill_common(const void *q, const void *k, const void *v, const flo
     a.qk_norm = qk_l2norm ? 1 : 0;
     a.chunk = chunk;
     a.variant = variant;
+    a.ckpt_every = ckpt_every;
+    a.ckpt_cap = ckpt_cap;
+    a.ckpt_state = ckpt_state;
+    a.ckpt_window = ckpt_window;
     return from_hip(
         gdn::launch_prefill(d_k, d_v, io_dtype, o_dtype, a, static_cast<hipStream_t>(stream)));
 }
@@ -201,6 +206,22 @@ int gdn_prefill_shared(const void *q, const void *k, const void *v, const float 
                           ws_bytes, stream);
 }
 
+int gdn_prefill_checkpointed(const void *q, const void *k, const void *v, const float *log_alpha,
+                             const float *beta, const int32_t *cu_seqlens, int n_seq,
+                             int n_tokens, int H, int d_k, int d_v, int chunk,
+                             const float *conv_w, int qk_l2norm, const float *init_state,
+                             const void *init_window, void *o, float *final_state,
+                             void *final_window, int ckpt_every, int ckpt_cap,
+                             float *ckpt_state, void *ckpt_window, int variant, int io_dtype,
+                             int o_dtype, void *workspace, size_t ws_bytes, void *stream) {
+    if (!final_state) return GDN_ERR_INVALID_ARG;
+    if (ckpt_every < 1 || ckpt_cap < 0 || (ckpt_cap > 0 && !ckpt_state))
+        return GDN_ERR_INVALID_ARG;
+    return prefill_common(q, k, v, log_alpha, beta, cu_seqlens, nullptr, n_seq, n_seq, n_tokens,
+                          H, d_k, d_v, chunk, conv_w, qk_l2norm, init_state, init_window, o,
+                          final_state, final_window, variant, io_dtype, o_dtype, workspace,
+                          ws_bytes, stream, ckpt_every, ckpt_cap, ckpt_state, ckpt_window);
+}
 int gdn_fork_branches(const void *q, const void *k, const void *v, const float *log_alpha,
                       const float *beta, const int32_t *branch_cu, const int32_t *branch_parent,
                       int n_branch, int n_parent, int n_tokens, int H, int d_k, int d_v,

@@ -103,6 +103,11 @@ struct PrefillArgs {
     size_t ws_bytes;
     int n_seq, n_parent, n_tokens, H, qk_norm, chunk;
     int variant;            // Variant: scalar log a [N, H], or per-key [N, H, dk]
+    // checkpoints: state / window after every ckpt_every chunks, at most
+    // ckpt_cap per sequence ([n_seq, ckpt_cap, H, dk, dv] / [n_seq, ckpt_cap, 3, CC])
+    float *ckpt_state;      // or null
+    void *ckpt_window;      // or null
+    int ckpt_every, ckpt_cap;
 };
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,

@@ -754,6 +754,55 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     const TI *vs = static_cast<const TI *>(a.v);
     const int cwin_v = 2 * H * DK + h * DV;
 
+    // the state tile [DK][TV] of this workgroup (Sig^T in s_St) into a
+    // [DK][DV] state at dst; valid at a chunk boundary (after the barrier
+    // that closes the previous state update)
+    auto put_state = [&](float *dst) {
+        for (int idx = tid; idx < DK * TV; idx += kThreads) {
+            const int d = idx / TV, j = idx % TV;
+            dst[(size_t)d * DV + j0 + j] = s_St[j * SP + d];
+        }
+    };
+    // conv window after position `end` of the sequence: its last 3 raw
+    // inputs (from the incoming window where end < 3), head h's channels
+    auto put_window = [&](TI *wo, int end) {
+        const int W = 2 * DK + DV;
+        for (int idx = tid; idx < 3 * W; idx += kThreads) {
+            const int r = idx / W, wc = idx % W;
+            const int p = end - 3 + r;
+            int cch;
+            const TI *xs;
+            size_t col, stride;
+            if (wc < DK) {
+                cch = h * DK + wc; xs = static_cast<const TI *>(a.q);
+                col = (size_t)h * DK + wc; stride = (size_t)H * DK;
+            } else if (wc < 2 * DK) {
+                cch = H * DK + h * DK + (wc - DK); xs = static_cast<const TI *>(a.k);
+                col = (size_t)h * DK + (wc - DK); stride = (size_t)H * DK;
+            } else {
+                cch = 2 * H * DK + h * DV + (wc - 2 * DK); xs = static_cast<const TI *>(a.v);
+                col = (size_t)h * DV + (wc - 2 * DK); stride = (size_t)H * DV;
+            }
+            TI val;
+            if (p >= 0) val = xs[(size_t)(sp.start + p) * stride + col];
+            else if (win) val = win[(size_t)(3 + p) * CC + cch];
+            else val = from_f32<TI>(0.f);
+            wo[(size_t)r * CC + cch] = val;
+        }
+    };
+    // checkpoint k of the sequence: the state and window after
+    // (k + 1) * ckpt_every chunks; `ckpt_at(c)` says whether the boundary
+    // before chunk c is one (k < ckpt_cap)
+    auto ckpt_at = [&](int c) {
+        return a.ckpt_state && a.ckpt_every > 0 && c > 0 && c % a.ckpt_every == 0 &&
+               c / a.ckpt_every - 1 < a.ckpt_cap;
+    };
+    auto put_checkpoint = [&](int c) {
+        const size_t k = (size_t)s * a.ckpt_cap + (c / a.ckpt_every - 1);
+        put_state(a.ckpt_state + (k * H + h) * DK * DV);
+        if (a.ckpt_window && tile == 0) put_window(static_cast<TI *>(a.ckpt_window) + k * 3 * CC, c * C);
+    };
+
     auto record = [&](int c) {
         return reinterpret_cast<const __bf16 *>(static_cast<const char *>(a.ws) + wl.rec_off) +
                ((size_t)(cs0 + c) * H + h) * wl.rec_elems;
@@ -817,6 +866,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     ChunkRegs<KS, NVT, TI, NEG> nxt;
     if (nchunks > 0) load_regs(0, nxt);
     for (int c = 0; c < nchunks; ++c) {
+        if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
         const ChunkRegs<KS, NVT, TI, NEG> cur = nxt;
         load_kt(c);
@@ -955,38 +1005,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
-    if (a.state_out)
-        for (int idx = tid; idx < DK * TV; idx += kThreads) {
-            const int d = idx / TV, j = idx % TV;
-            a.state_out[(((size_t)s * H + h) * DK + d) * DV + j0 + j] = s_St[j * SP + d];
-        }
-    // window out (tile 0): the last 3 raw inputs of the head's channels
-    if (a.win_out && tile == 0) {
-        TI *wo = static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC;
-        const int W = 2 * DK + DV;
-        for (int idx = tid; idx < 3 * W; idx += kThreads) {
-            const int r = idx / W, wc = idx % W;
-            const int p = sp.len - 3 + r;
-            int cch;
-            const TI *xs;
-            size_t col, stride;
-            if (wc < DK) {
-                cch = h * DK + wc; xs = static_cast<const TI *>(a.q);
-                col = (size_t)h * DK + wc; stride = (size_t)H * DK;
-            } else if (wc < 2 * DK) {
-                cch = H * DK + h * DK + (wc - DK); xs = static_cast<const TI *>(a.k);
-                col = (size_t)h * DK + (wc - DK); stride = (size_t)H * DK;
-            } else {
-                cch = 2 * H * DK + h * DV + (wc - 2 * DK); xs = static_cast<const TI *>(a.v);
-                col = (size_t)h * DV + (wc - 2 * DK); stride = (size_t)H * DV;
-            }
-            TI val;
-            if (p >= 0) val = xs[(size_t)(sp.start + p) * stride + col];
-            else if (win) val = win[(size_t)(3 + p) * CC + cch];
-            else val = from_f32<TI>(0.f);
-            wo[(size_t)r * CC + cch] = val;
-        }
-    }
+    if (a.state_out) put_state(a.state_out + ((size_t)s * H + h) * DK * DV);
+    if (a.win_out && tile == 0) put_window(static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
+    // a checkpoint at the end of the sequence (its length a multiple of the
+    // checkpoint spacing)
+    if (ckpt_at(nchunks) && nchunks * C == sp.len) put_checkpoint(nchunks);
 }
 
 template <int D, typename TI, typename TO>

@@ -118,6 +118,14 @@ def test_prefill_validation_and_workspace(lib):
     assert call(d=80) == UNSUPPORTED
     assert call(ws=NULL) == WORKSPACE
     assert call(ws_bytes=need - 1) == WORKSPACE
+    # checkpoints: spacing >= 1, capacity >= 0, a state buffer when capacity > 0
+    def ck(every=1, cap=2, buf=FAKE):
+        return lib.gdn_prefill_checkpointed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1000, 4, 128,
+                                            128, 64, NULL, 0, NULL, NULL, FAKE, FAKE, NULL,
+                                            every, cap, buf, NULL, 0, 1, 0, FAKE, need, NULL)
+    assert ck(every=0) == INVALID
+    assert ck(cap=-1) == INVALID
+    assert ck(buf=NULL) == INVALID
     # fork: the parent state and o are required
     assert lib.gdn_fork_branches(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 100, 4, 128, 128,
                                  64, NULL, 0, NULL, NULL, FAKE, NULL, NULL, 0, 1, 0, FAKE, need,

@@ -194,6 +194,58 @@ def test_long_context_per_key(variant):
     compare(run_fork(inp, variant=variant), run_oracle(inp, variant=variant), inp, TOL)
 
 
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+def test_checkpoints_match_truncated_runs_and_resume(variant):
+    """Checkpoints every 2 chunks (128 tokens): each equals the oracle's
+    final state / window of the sequence cut at that position; positions
+    past a sequence (or past the capacity) are left untouched; and resuming
+    from a checkpoint reproduces the rest of the sequence."""
+    d, H, every, cap = 64, 2, 2, 3
+    prefix = [300, 128, 64, 520, 0]
+    inp = gi.seq_inputs(prefix, [], [], H, d, d, io="bf16", conv=True,
+                        per_key=variant != "gdn", seed=21)
+    R, Np, cc = len(prefix), inp.Np, H * 3 * d
+    q, k, v = (dev_io(getattr(inp, n), getattr(inp, n + "_bits")) for n in "qkv")
+    la, beta, conv_w = f32(inp.log_alpha), f32(inp.beta), f32(inp.conv_w)
+    st = torch.empty((R, H, d, d), device=DEV)
+    ck = torch.full((R, cap, H, d, d), 7.0, device=DEV)
+    ckw = torch.zeros((R, cap, 3, cc), device=DEV, dtype=torch.bfloat16)
+    o = torch.empty((Np, H, d), device=DEV)
+    gdn.gdn_prefill_checkpointed(q, k, v, la, beta, i32(inp.cu_seqlens), st, every, ck, o=o,
+                                 ckpt_window=ckw, conv_w=conv_w, qk_l2norm=True, variant=variant)
+    torch.cuda.synchronize()
+    ck_h, ckw_bits = ck.cpu().numpy(), window_to_bits(ckw)
+    step = every * 64
+    for r, n in enumerate(prefix):
+        a = int(inp.cu_seqlens[r])
+        for j in range(cap):
+            pos = (j + 1) * step
+            if pos > n:
+                assert (ck_h[r, j] == 7.0).all(), (r, j)  # untouched
+                continue
+            sl = slice(a, a + pos)
+            _, st_ref, win_ref = oracle.prefill(inp.q[sl], inp.k[sl], inp.v[sl], inp.log_alpha[sl],
+                                                inp.beta[sl], np.array([0, pos]),
+                                                conv_w=inp.conv_w, qk_norm=True, variant=variant)
+            e = oracle.rel_err(ck_h[r, j][None], st_ref, axes=(2, 3))
+            assert e <= TOL, (r, j, e)
+            assert np.array_equal(ckw_bits[r, j], window_ref(win_ref[0], "bf16")), (r, j)
+    # resume sequence 3 from its second checkpoint (256 tokens in)
+    r, j = 3, 1
+    pos, a, n = (j + 1) * step, int(inp.cu_seqlens[3]), prefix[3]
+    sl = slice(a + pos, a + n)
+    st2 = torch.empty((1, H, d, d), device=DEV)
+    o2 = torch.empty((n - pos, H, d), device=DEV)
+    gdn.gdn_prefill_shared(q[sl], k[sl], v[sl], la[sl], beta[sl], i32([0, n - pos]), st2, o=o2,
+                           conv_w=conv_w, qk_l2norm=True, init_state=ck[r, j][None].contiguous(),
+                           init_window=ckw[r, j][None].contiguous(), variant=variant)
+    torch.cuda.synchronize()
+    e_o = oracle.rel_err(o2.cpu().numpy().astype(np.float64),
+                         o.cpu().numpy()[a + pos:a + n].astype(np.float64), axes=(0, 2))
+    e_s = oracle.rel_err(st2.cpu().numpy(), st.cpu().numpy()[r:r + 1], axes=(2, 3))
+    assert e_o <= TOL and e_s <= TOL, (e_o, e_s)
+
+
 def test_fork_is_bitwise_the_full_run_at_chunk_boundaries():
     """Flide page, method step 2: forking from the saved state computes the
     same function as the independent prompt. When the shared context is a
