@@ -14,8 +14,11 @@ through them. `value` is head-steps per second.
 Alongside: the eager step on the same workload (state-write ratio and
 speedup), the two-call fork (8 requests x 8192-token contexts, 20 branches
 of 64 tokens each, H=16, d=128, conv width 4) as branches per second, the
-roofline of the deferred kernel from HIP events on its stream, and the fp64
-CPU oracle timed on a bounded sample of the same decode workload.
+per-key decode workload (KDA and the RWKV6-style update, B=128, H=32,
+M=8), the small decode workload launched plainly and as one replayed HIP
+graph, the roofline of the deferred kernel from HIP events on its stream,
+and the fp64 CPU oracle timed on a bounded sample of the same decode
+workload.
 """
 
 from __future__ import annotations
@@ -43,21 +46,29 @@ LEN_B = 4 + 4                      # log length read + write
 ENTRY_B = 4 * D + 2 * D + 4        # one log entry: u (fp32), k (bf16), Lambda (fp32)
 
 
-def deferred_bytes(m, merges):
+def entry_bytes(per_key=False):
+    """One log entry; a per-key entry keeps a d_k-vector of cumulative
+    log-decay in place of the scalar."""
+    return ENTRY_B + (4 * D - 4 if per_key else 0)
+
+
+def deferred_bytes(m, merges, per_key=False, has_beta=True):
     """Bytes one head-step moves under the deferred schedule with m logged
     entries: base read, inputs, replay of m entries, o, and either a base
-    write (merging step) or one appended entry."""
-    return (STATE_B + QKV_B + SCAL_B + O_B + LEN_B + ENTRY_B * m
-            + (STATE_B if merges else ENTRY_B))
+    write (merging step) or one appended entry. Per-key decay reads a
+    d_k-vector of log a per step; the RWKV6-style update reads no beta."""
+    e = entry_bytes(per_key)
+    scal = (4 * D if per_key else 4) + (4 if has_beta else 0)
+    return STATE_B + QKV_B + scal + O_B + LEN_B + e * m + (STATE_B if merges else e)
 
 
 def eager_bytes():
     return 2 * STATE_B + QKV_B + SCAL_B + O_B
 
 
-def state_write_bytes(merges):
+def state_write_bytes(merges, per_key=False):
     """Bytes of recurrent state written per head-step: base and log."""
-    return STATE_B if merges else ENTRY_B
+    return STATE_B if merges else entry_bytes(per_key)
 
 
 def parse():
@@ -98,30 +109,31 @@ class Timer:
 
 
 # ---------------------------------------------------------------- decode
-def setup_decode(torch, gdn, gi, B=256, H=32, steps=512, M=8, seed=0):
+def setup_decode(torch, gdn, gi, B=256, H=32, steps=512, M=8, seed=0, per_key=False):
     dev = "cuda"
-    t = gi.torch_decode_inputs(B, H, D, D, steps, seed=seed)
+    t = gi.torch_decode_inputs(B, H, D, D, steps, per_key=per_key, seed=seed)
     rng = np.random.default_rng(seed + 1)
     phase = rng.integers(0, M, size=B)
     lengths = np.repeat(phase, H)
-    ent = gi.log_entries(rng, B * H, M, D, D, lengths, io="bf16")
+    ent = gi.log_entries(rng, B * H, M, D, D, lengths, per_key=per_key, io="bf16")
     logs = dict(
         log_u=torch.from_numpy(ent["u"]).to(dev).view(B, H, M, D),
         log_k=torch.from_numpy(ent["k_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
         .view(B, H, M, D),
-        log_lam=torch.from_numpy(ent["lam"]).to(dev).view(B, H, M),
+        log_lam=torch.from_numpy(ent["lam"]).to(dev).view((B, H, M, D) if per_key else (B, H, M)),
         log_len=torch.from_numpy(lengths.astype(np.int32)).to(dev).view(B, H),
     )
     return t, logs, phase
 
 
-def run_deferred(torch, gdn, t, logs, base, o, M, steps_range):
+def run_deferred(torch, gdn, t, logs, base, o, M, steps_range, variant="gdn"):
     S = t["q"].shape[0]
     for i in steps_range:
         s = i % S
         gdn.deltalog_append_decode(t["q"][s], t["k"][s], t["v"][s], t["log_alpha"][s],
-                                   t["beta"][s], base, logs["log_u"], logs["log_k"],
-                                   logs["log_lam"], logs["log_len"], o, merge_at=M)
+                                   None if variant == "rwkv6" else t["beta"][s], base,
+                                   logs["log_u"], logs["log_k"], logs["log_lam"],
+                                   logs["log_len"], o, merge_at=M, variant=variant)
 
 
 def run_eager(torch, gdn, t, state, o, steps_range):
@@ -132,7 +144,7 @@ def run_eager(torch, gdn, t, state, o, steps_range):
                              state, o)
 
 
-def schedule_bytes(phase, H, M, first, K):
+def schedule_bytes(phase, H, M, first, K, per_key=False, has_beta=True):
     """Exact algorithmic bytes of K deferred steps starting at step `first`,
     from the deterministic per-slot log lengths; plus state-write bytes."""
     m = np.asarray(phase, dtype=np.int64).copy()
@@ -142,8 +154,9 @@ def schedule_bytes(phase, H, M, first, K):
     writes = 0
     for _ in range(K):
         merges = m + 1 >= M
-        total += int(sum(deferred_bytes(int(mi), bool(mg)) for mi, mg in zip(m, merges))) * H
-        writes += int(sum(state_write_bytes(bool(mg)) for mg in merges)) * H
+        total += int(sum(deferred_bytes(int(mi), bool(mg), per_key, has_beta)
+                         for mi, mg in zip(m, merges))) * H
+        writes += int(sum(state_write_bytes(bool(mg), per_key) for mg in merges)) * H
         m = np.where(merges, 0, m + 1)
     return total, writes
 
@@ -191,6 +204,27 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
                 branches_per_s=NB / ((tp_ms + tf_ms) / 1e3),
                 branch_phase_branches_per_s=NB / (tf_ms / 1e3),
                 prefix_token_heads_per_s=Np * H / (tp_ms / 1e3))
+
+
+# ---------------------------------------------------------------- per-key decode
+def bench_decode_perkey(torch, gdn, gi, variant, K=64, W=16):
+    """The per-key decode workload (B=128, H=32, d=128, per-key log a, M=8
+    with per-slot log phases): deferred steps of the KDA delta rule or of
+    the RWKV6-style raw value update, head-steps/s and algorithmic GB/s."""
+    w = gi.WORKLOADS["perkey"]
+    B, H, T, M = w["B"], w["H"], w["steps"], w["M"]
+    t, logs, phase = setup_decode(torch, gdn, gi, B, H, T, M, per_key=True)
+    base = t["state0"].clone()
+    o = torch.empty((B, H, D), device="cuda")
+    stream = torch.cuda.current_stream()
+    run_deferred(torch, gdn, t, logs, base, o, M, range(W), variant)
+    with Timer(torch, stream) as tm:
+        run_deferred(torch, gdn, t, logs, base, o, M, range(W, W + K), variant)
+    alg, _ = schedule_bytes(phase, H, M, W, K, per_key=True, has_beta=variant != "rwkv6")
+    return dict(workload=f"perkey {variant}: deferred M=8, B={B}, H={H}, d=128, per-key "
+                         "log a, per-slot log phases",
+                value=B * H * K / (tm.ms / 1e3), unit="head-steps/s",
+                us_per_step=tm.ms * 1e3 / K, hbm_gbps_effective=alg / (tm.ms / 1e3) / 1e9)
 
 
 # ---------------------------------------------------------------- decode_small
@@ -360,6 +394,10 @@ def main():
         log("two-call fork, per-key decay (KDA) ...")
         fork_kda = bench_fork(torch, gdn, gi, args.fork_reps, variant="kda")
 
+    log("per-key decode (KDA, RWKV6-style) ...")
+    perkey = {v: bench_decode_perkey(torch, gdn, gi, v) for v in ("kda", "rwkv6")}
+    torch.cuda.empty_cache()
+
     log("decode_small, plain launches and one captured graph ...")
     small = bench_decode_small(torch, gdn, gi)
 
@@ -411,6 +449,7 @@ def main():
             "ratio": eager_writes / state_writes},
         "fork": fork,
         "fork_kda": fork_kda,
+        "decode_perkey": perkey,
         "decode_small": small,
         "hbm_probe": probe,
         "cpu_baseline": cpu,

@@ -434,7 +434,7 @@ __device__ __forceinline__ float row_shr(float x) {
 //   Sig_L = diag(e^{g_L}) Sig0 + sum_r (k_r . e^{g_L - g_r}) u_r^T,
 // which the scan runs with gamma = 1 and a per-key state decay.
 template <int DK, int DV, typename TI, int VAR>
-__global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr bool kPerKey = VAR != kScalar;
     constexpr bool kDelta = VAR != kRwkv6;
     constexpr int KS = DK / 32;
@@ -446,6 +446,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) float s_A[C * (C + 1)];  // strictly lower A
     __shared__ __attribute__((aligned(16))) float s_wq[DK * 4], s_wk[DK * 4];
     __shared__ float s_gt[kPerKey ? kWaves * DK : 1];  // per-key: each wave's row-block sums
+    __shared__ __attribute__((aligned(16))) float s_gl[kPerKey ? DK : 4];  // per-key: g_L
 
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
     const int gc = blockIdx.x, h = blockIdx.y;
@@ -474,10 +475,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
     __syncthreads();
     const int row = w * RB + lane % 16;  // this lane's row in the A layout
     const int cq = (lane / 16) * 8;
-    // scalar decay: g of row `lane`; per key: the factors of this lane's row
-    // and columns (A layout), e^{g}, e^{-g} and e^{g_L - g}
+    // scalar decay: g of row `lane`; per key: g of this lane's row and
+    // columns (A layout), the factors e^{g}, e^{-g}, e^{g_L - g} taken where
+    // they are used (few registers stay live across the loads)
     float g = 0.f, gL = 0.f;
-    float eg[KS][8], eng[KS][8], ekt[KS][8];
+    float gr[KS][8];
     if constexpr (!kPerKey) {
         g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
         gL = __shfl(g, C - 1, kWave);
@@ -512,25 +514,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int d = ks * 32 + cq + e;
-                float before = 0.f, total = 0.f;
+                float before = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < kWaves; ++ww) {
-                    const float t = s_gt[ww * DK + d];
-                    before += ww < w ? t : 0.f;
-                    total += t;
-                }
-                const float gr = gk[ks][e] + before;
-                eg[ks][e] = expf(gr);
-                eng[ks][e] = expf(-gr);
-                ekt[ks][e] = expf(total - gr);
+                for (int ww = 0; ww < kWaves; ++ww) before += ww < w ? s_gt[ww * DK + d] : 0.f;
+                gr[ks][e] = gk[ks][e] + before;
             }
-        // e^{g_L} per key for the scan's state decay
+        // g_L per key; e^{g_L} for the scan's state decay
         if (tid < DK) {
             float total = 0.f;
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww) total += s_gt[ww * DK + tid];
+            s_gl[tid] = total;
             reinterpret_cast<float *>(rec + RL.egl)[tid] = expf(total);
         }
+        __syncthreads();
     }
     float b_l = 1.f;
     if constexpr (kDelta) b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
@@ -546,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
         for (int ks = 0; ks < DK / 32; ++ks) {
             if constexpr (kPerKey)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qf[ks][e] *= eg[ks][e];  // Q^
+                for (int e = 0; e < 8; ++e) qf[ks][e] *= expf(gr[ks][e]);  // Q^
             qa[ks] = split8(qf[ks]);
             const size_t off = (size_t)row * DK + ks * 32 + cq;
             *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
@@ -560,11 +557,18 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
     for (int ks = 0; ks < DK / 32; ++ks) {
         // A operand of KK^T and the scan's K Sig term: K (scalar decay), K^
         // (per key), nothing (raw value update: the record row is zero)
-        float ak[8], bk[8];
+        // per key, kf becomes this row's K~^T column entries k e^{g_L - g}
+        float ak[8], bk[8], glv[8];
+        if constexpr (kPerKey) lds_read8(s_gl + ks * 32 + cq, glv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            ak[e] = kPerKey ? (kDelta ? kf[ks][e] * eg[ks][e] : 0.f) : kf[ks][e];
-            bk[e] = kPerKey ? kf[ks][e] * eng[ks][e] : kf[ks][e];  // B operand rows: K or K-
+            if constexpr (kPerKey) {
+                ak[e] = kDelta ? kf[ks][e] * expf(gr[ks][e]) : 0.f;
+                bk[e] = kf[ks][e] * expf(-gr[ks][e]);  // B operand rows: K-
+                kf[ks][e] *= expf(glv[e] - gr[ks][e]);
+            } else {
+                ak[e] = bk[e] = kf[ks][e];
+            }
         }
         ka[ks] = split8(ak);
         const size_t off = (size_t)row * DK + ks * 32 + cq;
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
         for (int ks = 0; ks < DK / 32; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                s_k[(ks * 32 + cq + e) * (C + 1) + row] = kf[ks][e] * (kPerKey ? ekt[ks][e] : f);
+                s_k[(ks * 32 + cq + e) * (C + 1) + row] = kPerKey ? kf[ks][e] : kf[ks][e] * f;
     }
     __syncthreads();
     for (int idx = tid; idx < DK * C; idx += kThreads)
@@ -650,6 +654,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
         split1(s_k[(idx / C) * (C + 1) + idx % C], rec[RL.thi + idx], rec[RL.tlo + idx]);
 }
 
+template <int DK, int DV, typename TI>
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
+    prep_body<DK, DV, TI, kScalar>(a);
+}
+
+// Per key the decay factors add registers; capped so two workgroups of the
+// largest head size still share a compute unit (measured faster than one,
+// while the scalar form runs best at its natural allocation).
+template <int DK, int DV, typename TI, int VAR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prep_kernel_pk(
+    PrefillArgs a) {
+    prep_body<DK, DV, TI, VAR>(a);
+}
+
 // ------------------------------------------------------------ scan
 // Workgroup -> (sequence-head, value tile): the NT value tiles of one
 // sequence-head get block indices congruent modulo 8, so they are dispatched
@@ -677,18 +695,19 @@ __device__ __forceinline__ void lds_dma16(const __bf16 *g, __bf16 *lds) {
     __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
-template <int KS, int NVT, typename TI, int NEG>
+template <int KS, int NVT, typename TI>
 struct ChunkRegs {
     Split8 ka[KS], qa[KS], ta[2], pa[2];
     TI vraw[NVT][7];  // raw V rows r0-3 .. r0+3 of this lane's columns
     float la;         // scalar decay: log a of row `lane` (clamped)
-    float egl[NEG];   // per-key decay: e^{g_L} of this lane's state columns
 };
 
 // PK: per-key decay (K and Q arrive pre-scaled, gamma = 1; the state decays
-// by e^{g_L} per key column).
-template <int DK, int DV, typename TI, typename TO, bool PK>
-__global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
+// by e^{g_L} per key column, staged in LDS with the chunk's K~^T planes).
+// CK: also write checkpoints (state and window every ckpt_every chunks);
+// a separate instance so the plain scan keeps its register budget.
+template <int DK, int DV, typename TI, typename TO, bool PK, bool CK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void scan_kernel(PrefillArgs a) {
     constexpr int KS = DK / 32;          // k-steps over d_k
     constexpr int SP = DK + 4;           // padded row of Sig^T (fp32)
     constexpr int CB = C + 8;            // padded row of the R^T / U^T planes
@@ -696,6 +715,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     constexpr int NFT = NVT * (DK / 16); // output tiles of the state update
     constexpr int NEG = NFT / kWaves;    // state-update tiles per wave
     static_assert(NFT % kWaves == 0, "state-update tiles split evenly over the waves");
+    static_assert(DK / 4 <= kWave, "e^{g_L} row fits one wave's 16-byte copies");
     constexpr RecLayout RL = rec_layout(DK);
     // Sig^T tile [TV][DK] in fp32; R^T and U^T [TV][C] as hi / lo bf16
     // planes (split once when written); K~^T [DK][C] hi / lo planes copied
@@ -705,6 +725,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_Uh[TV * CB], s_Ul[TV * CB];
     __shared__ __attribute__((aligned(16))) __bf16 s_Kh[DK * C], s_Kl[DK * C];
     __shared__ __attribute__((aligned(16))) float s_wv[TV * 4];
+    __shared__ __attribute__((aligned(16))) __bf16 s_eg[PK ? 2 * DK : 8];  // e^{g_L}, fp32 bits
 
     constexpr int NT = DV / TV;
     int shd, tile;
@@ -808,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
                ((size_t)(cs0 + c) * H + h) * wl.rec_elems;
     };
     // loads only: every address is clamped in bounds, nothing is consumed here
-    auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI, NEG> &r) {
+    auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI> &r) {
         const __bf16 *rec = record(c);
         const int p0 = c * C, L = min(C, sp.len - p0);
 #pragma unroll
@@ -837,10 +858,6 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
             }
         }
         if constexpr (PK) {
-            const float *egl = reinterpret_cast<const float *>(rec + RL.egl);
-#pragma unroll
-            for (int m = 0; m < NEG; ++m)
-                r.egl[m] = egl[((w + m * kWaves) / NVT) * 16 + lane % 16];
             r.la = 0.f;
         } else {
             r.la = a.log_alpha[(size_t)(sp.start + p0 + min(lane, L - 1)) * H + h];
@@ -861,14 +878,17 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
             lds_dma16(rec + RL.kthi + r * C + chg * 8, s_Kh + lds0);
             lds_dma16(rec + RL.ktlo + r * C + chg * 8, s_Kl + lds0);
         }
+        if constexpr (PK)  // DK floats: one 16-byte piece per lane of wave 0
+            if (w == 0 && lane < DK / 4) lds_dma16(rec + RL.egl + lane * 8, s_eg);
     };
 
-    ChunkRegs<KS, NVT, TI, NEG> nxt;
+    ChunkRegs<KS, NVT, TI> nxt;
     if (nchunks > 0) load_regs(0, nxt);
     for (int c = 0; c < nchunks; ++c) {
-        if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
+        if constexpr (CK)
+            if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
-        const ChunkRegs<KS, NVT, TI, NEG> cur = nxt;
+        const ChunkRegs<KS, NVT, TI> cur = nxt;
         load_kt(c);
 
         // g (running log a over the chunk rows; rows >= L add nothing)
@@ -987,7 +1007,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
         for (int m = 0; m < NEG; ++m) {
             const int ft = w + m * kWaves;
             const int t = ft % NVT, dt = ft / NVT;
-            const float dec = PK ? cur.egl[m] : gamL;  // per key: e^{g_L} of column dt*16 + lane%16
+            // per key: e^{g_L} of column dt*16 + lane%16
+            const float dec = PK ? reinterpret_cast<const float *>(s_eg)[dt * 16 + lane % 16] : gamL;
             f32x4v acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -1009,14 +1030,16 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(PrefillArgs a) {
     if (a.win_out && tile == 0) put_window(static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
     // a checkpoint at the end of the sequence (its length a multiple of the
     // checkpoint spacing)
-    if (ckpt_at(nchunks) && nchunks * C == sp.len) put_checkpoint(nchunks);
+    if constexpr (CK)
+        if (ckpt_at(nchunks) && nchunks * C == sp.len) put_checkpoint(nchunks);
 }
 
 template <int D, typename TI, typename TO>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     auto prep = [&](auto vtag) {
         constexpr int VAR = decltype(vtag)::value;
-        return prep_kernel<D, D, TI, VAR>;
+        if constexpr (VAR == kScalar) return prep_kernel<D, D, TI>;
+        else return prep_kernel_pk<D, D, TI, VAR>;
     };
     if (a.n_seq == 0) return hipSuccess;
     const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, D);
@@ -1041,12 +1064,17 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     }
     const size_t n_sh = (size_t)a.n_seq * a.H;
     const unsigned blocks = (unsigned)(((n_sh + 7) / 8) * 8 * (D / TV));  // see scan_unit
-    if (a.variant == kScalar)
-        hipLaunchKernelGGL((scan_kernel<D, D, TI, TO, false>), dim3(blocks), dim3(kThreads), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((scan_kernel<D, D, TI, TO, true>), dim3(blocks), dim3(kThreads), 0,
-                           stream, a);
+    const bool pk = a.variant != kScalar;
+    const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
+    auto scan = [&](auto pk_tag, auto ck_tag) {
+        hipLaunchKernelGGL((scan_kernel<D, D, TI, TO, decltype(pk_tag)::value,
+                                        decltype(ck_tag)::value>),
+                           dim3(blocks), dim3(kThreads), 0, stream, a);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (pk) ck ? scan(T_{}, T_{}) : scan(T_{}, F_{});
+    else ck ? scan(F_{}, T_{}) : scan(F_{}, F_{});
     return hipGetLastError();
 }
 

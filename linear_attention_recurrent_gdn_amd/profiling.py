@@ -1,12 +1,14 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-    python -m linear_attention_recurrent_gdn_amd.profiling trace <kernel_stats.csv> <out.md> "<command>"
+    python -m linear_attention_recurrent_gdn_amd.profiling trace <kernel_trace.csv> <out.md> "<command>"
     python -m linear_attention_recurrent_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
-        <out.md> "<command>" <kernel-substring> [copy_bytes]
+        <out.md> "<command>" <kernel-substring> [--grid N] [--copy-bytes B] [--sources decode|prefill]
 
-`trace` keeps the per-kernel call count and average / min / max duration.
-`traffic` turns two --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per
-dispatch) into HBM bytes per dispatch of the named kernel, each counter
+`trace` keeps, per kernel and launch grid, the call count and the average /
+min / max duration (one kernel serves workloads of different sizes, told
+apart by their grids). `traffic` turns two --pmc passes (FETCH_SIZE, then
+WRITE_SIZE, KiB per dispatch) into HBM bytes per dispatch of the named
+kernel (optionally only its dispatches of one grid size), each counter
 scaled by what it reads for a plain device copy of known size in the same
 run (the bench's bandwidth probe copies 4 GiB), and records a hash of the
 kernel sources so a later reader can tell whether the numbers still apply.
@@ -52,17 +54,23 @@ def _short(name, n=110):
     return name if len(name) <= n else name[: n - 3] + "..."
 
 
-def trace_summary(stats_csv, out_md, command):
-    rows = list(csv.DictReader(open(stats_csv)))
+def trace_summary(trace_csv, out_md, command, top=24):
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in groups.values()) or 1.0
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
     lines = [f"# Kernel trace: {os.path.basename(out_md)[:-3]}", "", "Command:", "",
-             f"    {command}", "", "| kernel | calls | avg us | min us | max us | % |",
-             "|---|---|---|---|---|---|"]
-    for r in rows[:20]:
-        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
-                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
-                     f"{float(r['Percentage']):.1f} |")
-    data = {r["Name"]: {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3}
-            for r in rows[:20]}
+             f"    {command}", "", "| kernel | grid | calls | avg us | min us | max us | % |",
+             "|---|---|---|---|---|---|---|"]
+    data = []
+    for (name, grid), d in rows:
+        avg = statistics.mean(d)
+        lines.append(f"| `{_short(name)}` | {grid} | {len(d)} | {avg:.1f} | {min(d):.1f} | "
+                     f"{max(d):.1f} | {100 * sum(d) / total:.1f} |")
+        data.append({"kernel": name, "grid": grid, "calls": len(d), "avg_us": avg,
+                     "median_us": statistics.median(d)})
     lines += ["", "```json", json.dumps(data, indent=1), "```", ""]
     open(out_md, "w").write("\n".join(lines))
 
@@ -73,7 +81,7 @@ def _counter_rows(d):
 
 
 def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_bytes=4 << 30,
-                    sources=DECODE_SOURCES):
+                    sources=DECODE_SOURCES, grid=None):
     fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
     copy_kib = copy_bytes / 1024
 
@@ -89,12 +97,15 @@ def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_byte
     cf = [f for f, w in zip(cf_all, cw_all) if abs(w - copy_kib) < 0.01 * copy_kib]
     f_scale = copy_kib / statistics.median(cf)
     w_scale = copy_kib / statistics.median(cw)
-    kf = [float(r["Counter_Value"]) for r in fetch if kernel_sub in r["Kernel_Name"]]
-    kw = [float(r["Counter_Value"]) for r in write if kernel_sub in r["Kernel_Name"]]
-    kname = next(r["Kernel_Name"] for r in fetch if kernel_sub in r["Kernel_Name"])
+    def mine(r):
+        return kernel_sub in r["Kernel_Name"] and (grid is None or int(r["Grid_Size"]) == grid)
+
+    kf = [float(r["Counter_Value"]) for r in fetch if mine(r)]
+    kw = [float(r["Counter_Value"]) for r in write if mine(r)]
+    kname = next(r["Kernel_Name"] for r in fetch if mine(r))
     rd = statistics.mean(kf) * f_scale * 1024
     wr = statistics.mean(kw) * w_scale * 1024
-    data = dict(kernel=kname, dispatches=len(kf), fetch_kib_raw=statistics.mean(kf),
+    data = dict(kernel=kname, grid=grid, dispatches=len(kf), fetch_kib_raw=statistics.mean(kf),
                 write_kib_raw=statistics.mean(kw), fetch_scale=f_scale, write_scale=w_scale,
                 read_bytes=rd, write_bytes=wr, traffic_bytes=rd + wr,
                 calibration=f"plain device copy of {copy_bytes} bytes: FETCH_SIZE "
@@ -104,7 +115,9 @@ def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_byte
     lines = [f"# HBM traffic: {os.path.basename(out_md)[:-3]}", "",
              "Two counter passes over the same command (FETCH_SIZE, then WRITE_SIZE):", "",
              f"    {command}", "",
-             f"Kernel: `{_short(kname, 200)}` ({len(kf)} dispatches averaged).", "",
+             f"Kernel: `{_short(kname, 200)}`"
+             + (f", grid {grid}" if grid is not None else "")
+             + f" ({len(kf)} dispatches averaged).", "",
              f"- FETCH_SIZE {data['fetch_kib_raw']:.0f} KiB/dispatch x {f_scale:.4f} = "
              f"{rd/1e6:.1f} MB read",
              f"- WRITE_SIZE {data['write_kib_raw']:.0f} KiB/dispatch x {w_scale:.4f} = "
@@ -115,14 +128,29 @@ def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_byte
     open(out_md, "w").write("\n".join(lines))
 
 
-if __name__ == "__main__":
-    mode = sys.argv[1]
-    if mode == "trace":
-        trace_summary(sys.argv[2], sys.argv[3], sys.argv[4])
-    elif mode == "traffic":
-        extra = {}
-        if len(sys.argv) > 7:
-            extra["copy_bytes"] = int(sys.argv[7])
-        traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], **extra)
+def main(argv):
+    import argparse
+
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("trace_csv")
+    t.add_argument("out_md")
+    t.add_argument("command")
+    f = sub.add_parser("traffic")
+    for name in ("fetch_dir", "write_dir", "out_md", "command", "kernel_sub"):
+        f.add_argument(name)
+    f.add_argument("--grid", type=int, default=None)
+    f.add_argument("--copy-bytes", type=int, default=4 << 30)
+    f.add_argument("--sources", choices=("decode", "prefill"), default="decode")
+    a = ap.parse_args(argv)
+    if a.mode == "trace":
+        trace_summary(a.trace_csv, a.out_md, a.command)
     else:
-        raise SystemExit(__doc__)
+        traffic_summary(a.fetch_dir, a.write_dir, a.out_md, a.command, a.kernel_sub,
+                        copy_bytes=a.copy_bytes, grid=a.grid,
+                        sources=DECODE_SOURCES if a.sources == "decode" else PREFILL_SOURCES)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
