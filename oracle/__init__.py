@@ -2,9 +2,10 @@
 
 TEST INFRASTRUCTURE: only tests/, the smoke check and the bench's CPU
 baseline leg import this package. It wraps `liboracle.so`, built by gcc
-from `gdn_oracle.c` in this folder, which computes every result in fp64
-straight from the definitions (see the header of gdn_oracle.c for the
-sources and readings). It shares no code with the HIP library.
+from `gdn_oracle.c` and `fork_attention_oracle.c` in this folder, which
+compute every result in fp64 straight from the definitions (see the
+headers of those files for the sources and readings). It shares no code
+with the HIP library.
 
 All array arguments are NumPy arrays of any float dtype; they are widened
 to float64 (bf16 and fp32 values widen exactly).
@@ -19,7 +20,7 @@ import subprocess
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "gdn_oracle.c")
+SRCS = [os.path.join(HERE, "gdn_oracle.c"), os.path.join(HERE, "fork_attention_oracle.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 _OVERRIDE = os.environ.get("ORACLE_LIB_OVERRIDE")
 
@@ -33,7 +34,7 @@ _lib = None
 def build(verbose=False):
     """Compile liboracle.so with gcc (OpenMP, -O2, strict IEEE: no fast-math)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
-           "-o", LIB + ".tmp", SRC, "-lm"]
+           "-o", LIB + ".tmp", *SRCS, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -46,7 +47,8 @@ def lib():
         if _OVERRIDE:
             _lib = ctypes.CDLL(_OVERRIDE)
         else:
-            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            if not os.path.exists(LIB) or any(os.path.getmtime(LIB) < os.path.getmtime(s)
+                                              for s in SRCS):
                 build()
             _lib = ctypes.CDLL(LIB)
         P = ctypes.c_void_p
@@ -57,6 +59,7 @@ def lib():
                                           P, I, D, P, P, P, P, P, I]
         _lib.oracle_materialize.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I]
         _lib.oracle_conv.argtypes = [I, I, I, I, P, P, P, P, P, I, D, P, P, P, P]
+        _lib.oracle_fork_attention.argtypes = [I, I, I, I, P, P, P, I, P, I, P, P, D, I, P, I]
         _lib.oracle_max_threads.restype = I
     return _lib
 
@@ -174,6 +177,34 @@ def materialize(base, log_u, log_k, log_lam, lengths, nthreads=0):
     out = np.zeros_like(base)
     lib().oracle_materialize(n, dk, dv, per_key, Mcap, _ptr(m), _ptr(base),
                              _ptr(lu), _ptr(lk), _ptr(ll), _ptr(out), nthreads)
+    return out
+
+
+def fork_attention(q, k, v, cu_seqlens, branch_cu=None, branch_parent=None, *, scale=None,
+                   trunk_queries=True, o=None, nthreads=0):
+    """Softmax attention over a flat token stream under the fork visibility
+    rule: a trunk token sees its request's trunk up to itself, a branch
+    token its parent request's whole trunk and its own branch up to itself.
+
+    q [N,H,d], k and v [N,H_kv,d]; cu_seqlens [R+1] and branch_cu [NB+1]
+    are absolute offsets into the stream; branch_parent [NB]. `scale`
+    defaults to 1/sqrt(d). Rows that no queried segment covers keep the
+    values of `o` (zeros when not given). Returns o [N,H,d] in fp64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, H, d = q.shape
+    Hkv = k.shape[1]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    if branch_cu is None:
+        bcu, bpar = np.zeros(1, dtype=np.int32), np.zeros(0, dtype=np.int32)
+    else:
+        bcu = np.ascontiguousarray(branch_cu, dtype=np.int32)
+        bpar = np.ascontiguousarray(branch_parent, dtype=np.int32)
+    out = np.zeros((N, H, d)) if o is None else np.array(o, dtype=np.float64, copy=True)
+    sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    lib().oracle_fork_attention(N, H, Hkv, d, _ptr(q), _ptr(k), _ptr(v), len(cu) - 1, _ptr(cu),
+                                len(bcu) - 1, _ptr(bcu), _ptr(bpar), sc, int(bool(trunk_queries)),
+                                _ptr(out), nthreads)
     return out
 
 

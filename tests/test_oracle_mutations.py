@@ -1,8 +1,9 @@
 """The oracle pins must catch plausible mistakes in the oracle.
 
-Each case plants one mistake in a copy of the oracle's C source (on the
-CPU, in a temporary folder), builds it, and runs the pin tests against the
-mutated library in a subprocess: at least one pin has to fail.
+Each case plants one mistake in a copy of one of the oracle's C sources (on
+the CPU, in a temporary folder), builds the library from it and the other
+source unchanged, and runs the pin tests against the mutated library in a
+subprocess: at least one pin has to fail.
 """
 
 import os
@@ -12,7 +13,10 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "oracle", "gdn_oracle.c")
+GDN_SRC = os.path.join(ROOT, "oracle", "gdn_oracle.c")
+ATT_SRC = os.path.join(ROOT, "oracle", "fork_attention_oracle.c")
+PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+        os.path.join(ROOT, "tests", "test_attention_oracle_pins.py")]
 
 MUTATIONS = {
     "output_before_update": (
@@ -30,20 +34,45 @@ MUTATIONS = {
     "readout_transposed": ("o[j] += row[j] * q[i];",
                            "o[j] += Sig[(size_t)j * dv + i] * q[i];"),
 }
+ATT_MUTATIONS = {
+    "attn_causal_off_by_one": ("for (int j = 0; j <= p; ++j) keys[n++] = t0 + j;",
+                               "for (int j = 0; j <= p + 1 && j < len; ++j) keys[n++] = t0 + j;"),
+    "attn_branch_without_trunk": ("for (int j = 0; j < plen; ++j) keys[n++] = p0 + j;",
+                                  "for (int j = 1; j < plen; ++j) keys[n++] = p0 + j;"),
+    "attn_scale_dropped": ("w[t] = scale * s;", "w[t] = s;"),
+    "attn_group_mapping": ("const int hk = h / (H / Hkv);", "const int hk = h % Hkv;"),
+    "attn_unnormalised": ("out[c] += (w[t] / den) * vj[c];", "out[c] += w[t] * vj[c];"),
+}
+CASES = {**{n: (GDN_SRC, m) for n, m in MUTATIONS.items()},
+         **{n: (ATT_SRC, m) for n, m in ATT_MUTATIONS.items()}}
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+@pytest.mark.parametrize("name", sorted(CASES))
 def test_pins_catch_planted_mistake(name, tmp_path):
-    before, after = MUTATIONS[name]
-    src = open(SRC).read()
+    path, (before, after) = CASES[name]
+    src = open(path).read()
     assert before in src, f"mutation site for {name} not found"
-    mutated = tmp_path / "mutated.c"
+    mutated = tmp_path / os.path.basename(path)
     mutated.write_text(src.replace(before, after, 1))
+    other = ATT_SRC if path == GDN_SRC else GDN_SRC
     so = tmp_path / "liboracle_mutated.so"
     subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
-                    str(mutated), "-lm"], check=True)
+                    str(mutated), other, "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(so))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        *PINS],
                        env=env, capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode != 0, f"no pin failed for mutation {name}:\n{r.stdout[-2000:]}"
+
+
+def test_unmutated_library_passes_the_pins(tmp_path):
+    """The same build and run without a planted mistake passes, so the
+    failures above come from the mutations, not from the harness."""
+    so = tmp_path / "liboracle_plain.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so), GDN_SRC,
+                    ATT_SRC, "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        *PINS],
+                       env=env, capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:]
