@@ -19,6 +19,12 @@ these synthetic draws):
                  per-slot log phases (pre-populated logs of 0..M-1 entries).
   perkey         B=128, H=32, d=128, per-key log a in R^128 ~ U(-0.1,-0.001),
                  256 steps (KDA and RWKV6-style).
+  fork attention the fork_prefill stream (8 x 8192-token trunks, 160
+                 branches of 64 tokens) for the softmax-attention half of
+                 the fork: q, k, v ~ N(0,1) per element rounded to bf16
+                 (not normalised, so scores q.k/sqrt(d) spread like N(0,1)
+                 and the softmax is neither flat nor one-hot), H = H_kv = 16,
+                 d = 128.
 
 Common distributions: q, k ~ N(0,1) per element, L2-normalised per
 (token, head) in fp32 and then rounded to bf16 (round to nearest even);
@@ -45,6 +51,7 @@ __all__ = [
     "decode_inputs",
     "seq_inputs",
     "log_entries",
+    "torch_attention_inputs",
     "WORKLOADS",
 ]
 
@@ -285,3 +292,43 @@ def torch_seq_inputs(prefix_lens, branch_lens, branch_parent, H, dk, dv, *, conv
                 cu_seqlens=cu.to(device), branch_cu=bcu.to(device),
                 branch_parent=torch.tensor(branch_parent, dtype=torch.int32, device=device),
                 Np=Np, Nb=Nb, N=N)
+
+
+def torch_attention_inputs(trunk_lens, branch_lens, branch_parent, *, H, Hkv, d,
+                           order="trunks_first", device="cuda", seed=0):
+    """A flat stream for fork attention, drawn on the device: q [N,H,d],
+    k, v [N,Hkv,d] ~ N(0,1) rounded to bf16, and int32 device offsets
+    (cu [R+1] of the trunks, bcu [NB+1] of the branches, both absolute).
+
+    Segment contents are drawn in a fixed order (trunks, then branches) and
+    then laid out: `order` "trunks_first" stores every trunk before every
+    branch, "branches_first" the reverse. The same seed gives the same
+    segments in either layout.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tl = [int(x) for x in trunk_lens]
+    bl = [int(x) for x in branch_lens]
+    Nt, Nb = sum(tl), sum(bl)
+    N = Nt + Nb
+
+    def draw(heads):
+        return torch.randn((N, heads, d), generator=g, device=device).to(torch.bfloat16)
+
+    q, k, v = draw(H), draw(Hkv), draw(Hkv)
+    if order == "trunks_first":
+        t0, b0 = 0, Nt
+    elif order == "branches_first":
+        t0, b0 = Nb, 0
+        perm = torch.cat([torch.arange(Nt, N), torch.arange(0, Nt)]).to(device)
+        q, k, v = q[perm].contiguous(), k[perm].contiguous(), v[perm].contiguous()
+    else:
+        raise ValueError(order)
+    cu = t0 + np.concatenate([[0], np.cumsum(tl)])
+    bcu = b0 + np.concatenate([[0], np.cumsum(bl)])
+    return dict(q=q, k=k, v=v,
+                cu=torch.from_numpy(cu.astype(np.int32)).to(device),
+                bcu=torch.from_numpy(bcu.astype(np.int32)).to(device),
+                bpar=torch.tensor(list(branch_parent), dtype=torch.int32, device=device))

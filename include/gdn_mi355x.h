@@ -271,6 +271,57 @@ int deltalog_merge(float *base, const float *log_u, const void *log_k,
                    int n_slots, int Mcap, int min_len, int variant,
                    int io_dtype, void *stream);
 
+/* ---------------------------------------------------------- fork attention
+ * Softmax attention over a flat token stream under the fork visibility rule
+ * ([FL] "연구방법을 단계별로", method step 1, and glossary "ForkAttention":
+ * requests and questions are GPU metadata over one flat stream; a token
+ * reads only its own request's trunk and the current and earlier tokens of
+ * its own branch -- other questions and other requests are invisible):
+ *   trunk token at position p of request r: keys = trunk r, positions 0..p
+ *   branch token at position p of branch b: keys = the whole trunk of
+ *       request branch_parent[b], then positions 0..p of branch b
+ *   o_i = sum_j softmax_j(scale <q_i, k_j>) v_j over those keys.
+ * Positions are not applied here (rotary or other position encodings are
+ * applied to q and k by the caller, with branch positions continuing after
+ * the trunk as in an independent prompt).
+ *
+ * Workspace bytes gdn_fork_attention needs: (n_req + n_branch + 1) int32.
+ */
+size_t gdn_fork_attention_workspace_bytes(int n_req, int n_branch);
+
+/*
+ * gdn_fork_attention -- one call over the whole stream.
+ *  q            [n_tokens, H, d] bf16
+ *  k, v         [n_tokens, H_kv, d] bf16 (head h reads k/v head
+ *               h / (H / H_kv); H_kv must divide H)
+ *  cu_seqlens   [n_req + 1] int32 device: trunk r is tokens
+ *               [cu_seqlens[r], cu_seqlens[r+1]) of the stream
+ *  branch_cu    [n_branch + 1] int32 device: branch b is tokens
+ *               [branch_cu[b], branch_cu[b+1]) (absolute, like cu_seqlens)
+ *  branch_parent [n_branch] int32 device, request index of each branch
+ *  scale        score scale (1/sqrt(d) is the usual choice), finite
+ *  trunk_queries 1: trunk rows of o are computed too; 0: trunks only serve
+ *               as keys/values (their o rows are left untouched) -- a round
+ *               of new branches against trunks computed earlier
+ *  o            [n_tokens, H, d] o_dtype (GDN_F32 or GDN_BF16); rows of
+ *               tokens in no queried segment are left untouched
+ *  d            64 or 128; io_dtype must be GDN_BF16
+ * Segments must be disjoint ranges of the stream (trunks and branches in
+ * any order) with non-decreasing offsets; offsets are clamped into
+ * [0, n_tokens]. A branch whose parent is outside [0, n_req) gets NaN
+ * outputs. Accumulation is fp32 with split-bf16 probabilities.
+ * Errors: INVALID_ARG (NULL pointer, negative count, H_kv not dividing H,
+ * non-finite scale, bad dtype code), UNSUPPORTED (d, or fp32 q/k/v),
+ * WORKSPACE, HIP.
+ */
+int gdn_fork_attention(const void *q, const void *k, const void *v,
+                       const int32_t *cu_seqlens, int n_req,
+                       const int32_t *branch_cu, const int32_t *branch_parent,
+                       int n_branch, int n_tokens, int H, int H_kv, int d,
+                       float scale, int trunk_queries, void *o, int io_dtype,
+                       int o_dtype, void *workspace, size_t ws_bytes,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

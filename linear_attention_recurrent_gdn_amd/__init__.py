@@ -3,8 +3,9 @@
 Thin Python binding over the C ABI of libgdn_mi355x.so (include/gdn_mi355x.h):
 shared-context prefill and forked branches (the two-call GDN fork of the
 Flide page), eager decode, and deferred base + log decode with its merge
-(the DeltaLog page). Tensors are torch device tensors; every step of the
-computation runs in the HIP kernels.
+(the DeltaLog page), and the softmax-attention half of the fork (attention
+under the trunk + own-branch visibility rule). Tensors are torch device
+tensors; every step of the computation runs in the HIP kernels.
 """
 
 from ._lib import (  # noqa: F401
@@ -13,7 +14,9 @@ from ._lib import (  # noqa: F401
     GDNError,
     deltalog_append_decode,
     deltalog_merge,
+    fork_attention_workspace_bytes,
     gdn_decode_eager,
+    gdn_fork_attention,
     gdn_fork_branches,
     gdn_prefill_checkpointed,
     gdn_prefill_shared,
@@ -25,9 +28,12 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "gdn_prefill_shared",
     "gdn_fork_branches",
+    "gdn_prefill_checkpointed",
     "gdn_decode_eager",
     "deltalog_append_decode",
     "deltalog_merge",
+    "gdn_fork_attention",
+    "fork_attention_workspace_bytes",
     "prefill_workspace_bytes",
     "status_string",
     "load",

@@ -40,6 +40,9 @@ SIGNATURES = {
     "deltalog_append_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
                                     _I, _I, _I, _I, _I, _I, _I, _P]),
     "deltalog_merge": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "gdn_fork_attention_workspace_bytes": (_S, [_I, _I]),
+    "gdn_fork_attention": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float,
+                                _I, _P, _I, _I, _P, _S, _P]),
 }
 
 
@@ -285,3 +288,34 @@ def gdn_fork_branches(q, k, v, log_alpha, beta, branch_cu, branch_parent, parent
         _dev(branch_window, "branch_window", q.dtype, (NB, 3, cc), optional=True),
         _variant(variant), io, _io_code(o), ws.data_ptr(), ws.numel(), _stream(stream))
     _check("gdn_fork_branches", st)
+
+
+# ------------------------------------------------------------------ fork attention
+def fork_attention_workspace_bytes(n_req, n_branch):
+    return int(load().gdn_fork_attention_workspace_bytes(n_req, n_branch))
+
+
+def gdn_fork_attention(q, k, v, cu_seqlens, o, branch_cu=None, branch_parent=None, scale=None,
+                       trunk_queries=True, workspace=None, stream=None):
+    """Softmax attention over a flat stream under the fork visibility rule
+    (a trunk token reads its request's trunk up to itself; a branch token
+    its parent request's whole trunk and its own branch up to itself).
+    q [N,H,d], k, v [N,H_kv,d] bf16; cu_seqlens [R+1], branch_cu [NB+1]
+    (absolute offsets), branch_parent [NB] int32; o [N,H,d] fp32 or bf16.
+    `scale` defaults to 1/sqrt(d)."""
+    N, H, d = q.shape
+    Hkv = k.shape[1]
+    R = cu_seqlens.shape[0] - 1
+    NB = 0 if branch_cu is None else branch_cu.shape[0] - 1
+    need = fork_attention_workspace_bytes(R, NB)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    sc = float(d) ** -0.5 if scale is None else float(scale)
+    st = load().gdn_fork_attention(
+        _dev(q, "q", torch.bfloat16, (N, H, d)), _dev(k, "k", torch.bfloat16, (N, Hkv, d)),
+        _dev(v, "v", torch.bfloat16, (N, Hkv, d)), _dev(cu_seqlens, "cu_seqlens", _I32, (R + 1,)),
+        R, _dev(branch_cu, "branch_cu", _I32, (NB + 1,), optional=NB == 0),
+        _dev(branch_parent, "branch_parent", _I32, (NB,), optional=NB == 0), NB, N, H, Hkv, d,
+        sc, int(bool(trunk_queries)), _dev(o, "o", _IO, (N, H, d)), _io_code(q), _io_code(o),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check("gdn_fork_attention", st)

@@ -5,6 +5,9 @@
 
 #include <limits.h>
 
+#include <cmath>
+
+#include "attention_launch.hpp"
 #include "gdn_device.hpp"
 #include "gdn_mi355x.h"
 
@@ -234,6 +237,45 @@ int gdn_fork_branches(const void *q, const void *k, const void *v, const float *
                           n_parent, n_tokens, H, d_k, d_v, chunk, conv_w, qk_l2norm,
                           parent_state, parent_window, o, branch_state, branch_window, variant,
                           io_dtype, o_dtype, workspace, ws_bytes, stream);
+}
+
+size_t gdn_fork_attention_workspace_bytes(int n_req, int n_branch) {
+    if (n_req < 0 || n_branch < 0) return 0;
+    return gdn::attention_workspace_bytes(n_req, n_branch);
+}
+
+int gdn_fork_attention(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                       int n_req, const int32_t *branch_cu, const int32_t *branch_parent,
+                       int n_branch, int n_tokens, int H, int H_kv, int d, float scale,
+                       int trunk_queries, void *o, int io_dtype, int o_dtype, void *workspace,
+                       size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !o) return GDN_ERR_INVALID_ARG;
+    if (n_req < 0 || n_branch < 0 || n_tokens < 0 || H < 1 || H_kv < 1 || H % H_kv != 0)
+        return GDN_ERR_INVALID_ARG;
+    if (!cu_seqlens || (n_branch > 0 && (!branch_cu || !branch_parent)))
+        return GDN_ERR_INVALID_ARG;
+    if (!dtype_ok(io_dtype) || !dtype_ok(o_dtype) || !std::isfinite(scale))
+        return GDN_ERR_INVALID_ARG;
+    if (io_dtype != GDN_BF16 || (d != 64 && d != 128)) return GDN_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < gdn::attention_workspace_bytes(n_req, n_branch))
+        return GDN_ERR_WORKSPACE;
+    gdn::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu = cu_seqlens;
+    a.bcu = branch_cu;
+    a.bparent = branch_parent;
+    a.o = o;
+    a.ws = workspace;
+    a.n_req = n_req;
+    a.n_branch = n_branch;
+    a.n_tokens = n_tokens;
+    a.H = H;
+    a.Hkv = H_kv;
+    a.scale = scale;
+    a.trunk_queries = trunk_queries ? 1 : 0;
+    return from_hip(gdn::launch_attention(d, o_dtype, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

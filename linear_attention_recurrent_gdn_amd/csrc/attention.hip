@@ -1,0 +1,345 @@
+// attention.hip -- ForkAttention: softmax attention over a flat token stream
+// in which every token reads only its own request's shared trunk and the
+// current and earlier tokens of its own branch.
+//
+// Source: "같은 맥락에서 여러 판단을 빠르게 처리하는 Flide" (yozm.zip summary
+// of the Flide paper), section "연구방법을 단계별로", method step 1 (tokens of
+// all requests and questions in one flat stream, membership as GPU metadata,
+// question positions continuing after the shared context; other questions
+// and other requests invisible), and the glossary entry "ForkAttention"
+// (in standard attention the fork is a visibility rule).
+//
+// Visibility as a causal rule. A branch of length L whose request's trunk
+// has P tokens sees exactly what its tokens would see in the independent
+// prompt trunk ++ branch: its query at branch position p is the query at
+// virtual position P + p of that prompt, and the keys it may read are the
+// virtual positions 0 .. P + p, where virtual position x < P is trunk token
+// x and x >= P is branch token x - P. A trunk token is the same rule with
+// P = 0 over its own request. So every work item is a causal attention over
+// a virtual key sequence, gathered from two ranges of the stream.
+//
+// Kernels:
+//   plan -- one workgroup: query tiles per segment (branches first, then
+//           trunks), exclusive prefix sums into the workspace, capped at
+//           the grid's capacity.
+//   attn -- one workgroup per (head, query tile of 64 rows): streams the
+//           tile's virtual keys in blocks of 64 through LDS (K row-major,
+//           V transposed, so both MFMA operands read contiguous keys) with
+//           an online softmax. Each of the 4 waves owns 16 queries.
+//
+// Layout of the products (v_mfma_f32_16x16x32_bf16; A rows and B columns
+// are indexed by lane % 16, the 8 reduction slots of a lane by lane / 16):
+//   S^T = K Q^T   keys x queries; a lane ends up with 4 keys of 4 key tiles
+//                 for one query (lane % 16), so the softmax statistics of a
+//                 query live in the 4 lanes lane % 16 + {0, 16, 32, 48};
+//   O^T = V^T P^T d x queries; the lane's own probabilities are its B
+//                 operand as they stand (its 8 reduction slots are the keys
+//                 of two adjacent key tiles), and V^T is read with the same
+//                 key order; the result keeps one query per lane column, so
+//                 the online-softmax rescale needs no data exchange.
+// q, k, v are bf16 (their products are exact in the fp32 accumulators);
+// the probabilities are split into bf16 hi + lo and both go through the
+// matrix cores (P = P_hi + P_lo to about 2^-17), since one bf16 rounding
+// of P (2^-9 relative) would not hold a 2e-3 end-to-end tolerance.
+
+#include "attention_launch.hpp"
+#include "gdn_device.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kAThreads = 256;
+constexpr int BM = 64;   // queries per workgroup (16 per wave)
+constexpr int BN = 64;   // keys per block
+constexpr int kGroup = 16;  // consecutive work items that share an XCD (and its L2)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Seg {
+    int t0, len;    // the segment's own tokens [t0, t0 + len)
+    int p0, plen;   // the trunk a branch reads first (plen = 0 for a trunk)
+    bool ok;        // false: a branch whose parent index is out of range
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// Segment `seg` in work order: branches 0 .. n_branch-1, then trunks.
+// Offsets are clamped into the stream, so bad metadata cannot address
+// outside it.
+__device__ __forceinline__ Seg segment(const AttnArgs &a, int seg) {
+    const int N = a.n_tokens;
+    Seg s{0, 0, 0, 0, true};
+    if (seg < a.n_branch) {
+        const int b0 = clampi(a.bcu[seg], 0, N), b1 = clampi(a.bcu[seg + 1], b0, N);
+        s.t0 = b0;
+        s.len = b1 - b0;
+        const int r = a.bparent[seg];
+        if (r < 0 || r >= a.n_req) {
+            s.ok = false;
+        } else {
+            const int c0 = clampi(a.cu[r], 0, N), c1 = clampi(a.cu[r + 1], c0, N);
+            s.p0 = c0;
+            s.plen = c1 - c0;
+        }
+    } else {
+        const int r = seg - a.n_branch;
+        const int c0 = clampi(a.cu[r], 0, N), c1 = clampi(a.cu[r + 1], c0, N);
+        s.t0 = c0;
+        s.len = a.trunk_queries ? c1 - c0 : 0;
+    }
+    return s;
+}
+
+// ws[seg] = first tile of segment seg, ws[n_seg] = number of tiles, all
+// capped at max_tiles (the grid's capacity; only overlapping segments,
+// which the interface excludes, can reach it).
+__global__ __launch_bounds__(kAThreads) void attn_plan_kernel(AttnArgs a, int max_tiles) {
+    __shared__ int s_scan[kAThreads];
+    int *ts = static_cast<int *>(a.ws);
+    const int n_seg = a.n_branch + a.n_req, tid = threadIdx.x;
+    int run = 0;
+    for (int base = 0; base < n_seg; base += kAThreads) {
+        const int seg = base + tid;
+        int c = 0;
+        if (seg < n_seg) c = (segment(a, seg).len + BM - 1) / BM;
+        s_scan[tid] = c;
+        __syncthreads();
+        for (int off = 1; off < kAThreads; off <<= 1) {
+            const int x = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        if (seg < n_seg) ts[seg] = min(run + s_scan[tid] - c, max_tiles);
+        run += s_scan[kAThreads - 1];
+        __syncthreads();
+    }
+    if (tid == 0) ts[n_seg] = min(run, max_tiles);
+}
+
+template <int D, typename TO>
+__global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
+    constexpr int KSD = D / 32;               // reduction steps of S^T over d
+    constexpr int NDT = D / 16;               // 16-row d tiles of O^T
+    constexpr int KP = D + 8;                 // padded K row in LDS (bf16)
+    constexpr int VP = BN + 8;                // padded V^T row in LDS (bf16)
+    constexpr int CPR = D / 8;                // 16-byte pieces per key row
+    constexpr int KPASS = BN * CPR / kAThreads;       // K pieces per thread
+    constexpr int KPP = 2 * kAThreads / CPR;          // keys per V pass (in pairs)
+    constexpr int VPASS = BN / KPP;                   // V passes (2 pieces each)
+    static_assert(KPASS >= 1 && VPASS >= 1, "block shape");
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[BN * KP];
+    __shared__ __attribute__((aligned(16))) __bf16 s_vt[D * VP];
+
+    const int *ts = static_cast<const int *>(a.ws);
+    const int n_seg = a.n_branch + a.n_req;
+    const int T = ts[n_seg];
+    // block -> work item: groups of kGroup consecutive items per XCD
+    // (blocks are dispatched to the 8 XCDs round-robin)
+    const int b = blockIdx.x, xcd = b % 8, local = b / 8;
+    const int wi = ((local / kGroup) * 8 + xcd) * kGroup + local % kGroup;
+    if (wi >= a.H * T) return;
+    const int h = wi / T, t = wi % T;
+    int lo = 0, hi = n_seg;  // ts[lo] <= t < ts[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ts[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    const Seg sg = segment(a, lo);
+    const int ntile = ts[lo + 1] - ts[lo];
+    const int tile = ntile - 1 - (t - ts[lo]);  // the longest tiles of a segment first
+    const int q_first = tile * BM;
+    const int L = min(BM, sg.len - q_first);
+    const int H = a.H;
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    TO *o = static_cast<TO *>(a.o);
+
+    if (!sg.ok) {  // a branch with an invalid parent: NaN outputs
+        for (int idx = tid; idx < L * D; idx += kAThreads)
+            o[((size_t)(sg.t0 + q_first + idx / D) * H + h) * D + idx % D] =
+                from_f32<TO>(quiet_nan());
+        return;
+    }
+
+    const int hk = h / (H / a.Hkv);
+    const int Hkv = a.Hkv;
+    const int qcol = w * 16 + lane % 16;      // this lane's query in the tile
+    const int qrow = min(qcol, L - 1);        // clamped for the rows past the tile end
+    const int qp = sg.plen + q_first + qrow;  // its virtual position
+    const int kv_len = sg.plen + q_first + L; // virtual keys the tile reads
+    const int nblk = (kv_len + BN - 1) / BN;
+    const int g4 = (lane / 16) * 4, g8 = (lane / 16) * 8;
+
+    // Q^T operand: 8 consecutive d of this lane's query per reduction step
+    const __bf16 *qg = static_cast<const __bf16 *>(a.q) +
+                       ((size_t)(sg.t0 + q_first + qrow) * H + h) * D + g8;
+    bf16x8 qf[KSD];
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qg + ks * 32);
+
+    const __bf16 *kg = static_cast<const __bf16 *>(a.k);
+    const __bf16 *vg = static_cast<const __bf16 *>(a.v);
+    // stream row of virtual key x (clamped into the tile's keys)
+    auto key_row = [&](int x) {
+        x = min(x, kv_len - 1);
+        return x < sg.plen ? sg.p0 + x : sg.t0 + (x - sg.plen);
+    };
+    bf16x8 kreg[KPASS];
+    u32x4 vreg[VPASS][2];
+    auto load_block = [&](int j) {
+#pragma unroll
+        for (int p = 0; p < KPASS; ++p) {
+            const int piece = p * kAThreads + tid, r = piece / CPR, c = piece % CPR;
+            kreg[p] = *reinterpret_cast<const bf16x8 *>(
+                kg + ((size_t)key_row(j * BN + r) * Hkv + hk) * D + c * 8);
+        }
+#pragma unroll
+        for (int p = 0; p < VPASS; ++p) {
+            const int c = tid % CPR, r = p * KPP + 2 * (tid / CPR);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                vreg[p][u] = *reinterpret_cast<const u32x4 *>(
+                    vg + ((size_t)key_row(j * BN + r + u) * Hkv + hk) * D + c * 8);
+        }
+    };
+    auto store_block = [&]() {
+#pragma unroll
+        for (int p = 0; p < KPASS; ++p) {
+            const int piece = p * kAThreads + tid, r = piece / CPR, c = piece % CPR;
+            *reinterpret_cast<bf16x8 *>(s_k + r * KP + c * 8) = kreg[p];
+        }
+#pragma unroll
+        for (int p = 0; p < VPASS; ++p) {
+            const int c = tid % CPR, r = p * KPP + 2 * (tid / CPR);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                // keys r and r + 1 of rows d = 8c + 2x (low halves) and
+                // 8c + 2x + 1 (high halves), each pair as one 4-byte word
+                const uint32_t a0 = vreg[p][0][x], a1 = vreg[p][1][x];
+                *reinterpret_cast<uint32_t *>(s_vt + (c * 8 + 2 * x) * VP + r) =
+                    (a0 & 0xffffu) | (a1 << 16);
+                *reinterpret_cast<uint32_t *>(s_vt + (c * 8 + 2 * x + 1) * VP + r) =
+                    (a0 >> 16) | (a1 & 0xffff0000u);
+            }
+        }
+    };
+
+    const float c2 = a.scale * 1.4426950408889634f;  // scores in log2 units
+    float m = -INFINITY, lsum = 0.f;
+    f32x4v acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+    load_block(0);
+    store_block();
+    __syncthreads();
+    for (int j = 0; j < nblk; ++j) {
+        if (j + 1 < nblk) load_block(j + 1);
+
+        // S^T: rows = keys kt*16 + g4 + i, column = this lane's query
+        f32x4v st[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            st[kt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                const bf16x8 kf =
+                    *reinterpret_cast<const bf16x8 *>(s_k + (kt * 16 + lane % 16) * KP + ks * 32 + g8);
+                st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[kt], 0, 0, 0);
+            }
+        }
+        // online softmax of this query over the block (keys after it masked)
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = j * BN + kt * 16 + g4 + i;
+                st[kt][i] = key <= qp ? st[kt][i] * c2 : -INFINITY;
+                mloc = fmaxf(mloc, st[kt][i]);
+            }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+        const float mnew = fmaxf(m, mloc);  // finite: key 0 is visible to every query
+        const float alpha = exp2f(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        bf16x8 ph[2], pl[2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = exp2f(st[kt][i] - mnew);
+                lsum += p;
+                const __bf16 hp = (__bf16)p;
+                ph[kt / 2][(kt % 2) * 4 + i] = hp;
+                pl[kt / 2][(kt % 2) * 4 + i] = (__bf16)(p - (float)hp);
+            }
+        // O^T += V^T P^T over the two 32-key halves of the block
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const __bf16 *vp = s_vt + (dt * 16 + lane % 16) * VP + c * 32 + g4;
+                const bf16x4 v0 = *reinterpret_cast<const bf16x4 *>(vp);
+                const bf16x4 v1 = *reinterpret_cast<const bf16x4 *>(vp + 16);
+                const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[c], acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[c], acc[dt], 0, 0, 0);
+            }
+        __syncthreads();  // every wave is done with this block's K and V^T
+        if (j + 1 < nblk) {
+            store_block();
+            __syncthreads();
+        }
+    }
+
+    // the row sum of a query is split over its 4 lanes
+    float ltot = lsum + __shfl_xor(lsum, 16, kWave);
+    ltot += __shfl_xor(ltot, 32, kWave);
+    if (qcol < L) {
+        TO *orow = o + ((size_t)(sg.t0 + q_first + qcol) * H + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) orow[dt * 16 + g4 + i] = from_f32<TO>(acc[dt][i] / ltot);
+    }
+}
+
+template <int D, typename TO>
+hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
+    const int n_seg = a.n_branch + a.n_req;
+    if (n_seg == 0) return hipSuccess;
+    const long long max_tiles = (long long)(a.n_tokens + BM - 1) / BM + n_seg;
+    const long long items = max_tiles * a.H;
+    const long long per = 8LL * kGroup;
+    const long long blocks = (items + per - 1) / per * per;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kAThreads), 0, stream, a, (int)max_tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_kernel<D, TO>), dim3((unsigned)blocks), dim3(kAThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attention_workspace_bytes(int n_req, int n_branch) {
+    return sizeof(int32_t) * ((size_t)n_req + (size_t)n_branch + 1);
+}
+
+hipError_t launch_attention(int d, int out, const AttnArgs &a, hipStream_t stream) {
+    if (d == 128) return out == kBF16 ? launch_typed<128, bf16>(a, stream)
+                                      : launch_typed<128, float>(a, stream);
+    if (d == 64) return out == kBF16 ? launch_typed<64, bf16>(a, stream)
+                                     : launch_typed<64, float>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

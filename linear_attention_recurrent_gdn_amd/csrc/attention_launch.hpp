@@ -1,0 +1,27 @@
+// attention_launch.hpp -- internal launch interface of the fork-attention
+// kernels (attention.hip) for the C ABI (api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct AttnArgs {
+    const void *q;             // [n_tokens, H, d] bf16
+    const void *k, *v;         // [n_tokens, H_kv, d] bf16
+    const int32_t *cu;         // [n_req + 1] trunk offsets (absolute)
+    const int32_t *bcu;        // [n_branch + 1] branch offsets (absolute)
+    const int32_t *bparent;    // [n_branch] request of each branch
+    void *o;                   // [n_tokens, H, d]
+    void *ws;                  // int32 tile table [n_req + n_branch + 1]
+    int n_req, n_branch, n_tokens, H, Hkv;
+    float scale;
+    int trunk_queries;         // 0: trunk rows give keys/values only
+};
+
+size_t attention_workspace_bytes(int n_req, int n_branch);
+hipError_t launch_attention(int d, int out, const AttnArgs &a, hipStream_t stream);
+
+}  // namespace gdn

@@ -130,3 +130,28 @@ def test_prefill_validation_and_workspace(lib):
     assert lib.gdn_fork_branches(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 100, 4, 128, 128,
                                  64, NULL, 0, NULL, NULL, FAKE, NULL, NULL, 0, 1, 0, FAKE, need,
                                  NULL) == INVALID
+
+
+def test_fork_attention_validation_and_workspace(lib):
+    need = lib.gdn_fork_attention_workspace_bytes(2, 5)
+    assert need == 4 * (2 + 5 + 1)
+
+    def call(q=FAKE, cu=FAKE, bcu=FAKE, bpar=FAKE, nb=5, H=8, Hkv=2, d=128, scale=0.1,
+             io=1, out=0, ws=FAKE, ws_bytes=need):
+        return lib.gdn_fork_attention(q, FAKE, FAKE, cu, 2, bcu, bpar, nb, 100, H, Hkv, d, scale,
+                                      1, FAKE, io, out, ws, ws_bytes, NULL)
+    assert call(q=NULL) == INVALID
+    assert call(cu=NULL) == INVALID
+    assert call(bcu=NULL) == INVALID
+    assert call(bpar=NULL) == INVALID
+    assert call(Hkv=3) == INVALID                  # does not divide H
+    assert call(Hkv=0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(out=2) == INVALID
+    assert call(nb=-1) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(d=32) == UNSUPPORTED
+    assert call(io=0) == UNSUPPORTED               # fp32 q/k/v not built
+    assert call(ws=NULL) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE
