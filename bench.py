@@ -14,11 +14,12 @@ through them. `value` is head-steps per second.
 Alongside: the eager step on the same workload (state-write ratio and
 speedup), the two-call fork (8 requests x 8192-token contexts, 20 branches
 of 64 tokens each, H=16, d=128, conv width 4) as branches per second, the
-per-key decode workload (KDA and the RWKV6-style update, B=128, H=32,
-M=8), the small decode workload launched plainly and as one replayed HIP
-graph, the roofline of the deferred kernel from HIP events on its stream,
-and the fp64 CPU oracle timed on a bounded sample of the same decode
-workload.
+softmax-attention half of the fork on the same stream (one fork-attention
+call over trunks and branches), the per-key decode workload (KDA and the
+RWKV6-style update, B=128, H=32, M=8), the small decode workload launched
+plainly and as one replayed HIP graph, the roofline of the deferred kernel
+from HIP events on its stream, and the fp64 CPU oracle timed on a bounded
+sample of the same decode workload.
 """
 
 from __future__ import annotations
@@ -204,6 +205,49 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
                 branches_per_s=NB / ((tp_ms + tf_ms) / 1e3),
                 branch_phase_branches_per_s=NB / (tf_ms / 1e3),
                 prefix_token_heads_per_s=Np * H / (tp_ms / 1e3))
+
+
+# ---------------------------------------------------------------- fork attention
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD public figure
+
+
+def bench_fork_attention(torch, gdn, gi, reps):
+    """The softmax-attention half of the fork on the fork_prefill stream (8
+    requests x 8192-token trunks, 20 branches of 64 tokens each, H=16, d=128,
+    bf16): one gdn_fork_attention call over the whole stream (trunks and
+    branches), and the branch round alone (trunks as keys only)."""
+    w = gi.WORKLOADS["fork_prefill"]
+    R, H, d, P, Lb = w["R"], w["H"], w["d"], w["prefix"], w["branch_len"]
+    pl, bl, par = gi.fork_layout(R, P, w["branches_per_req"], Lb)
+    t = gi.torch_attention_inputs(pl, bl, par, H=H, Hkv=H, d=d, seed=0)
+    N, NB = t["q"].shape[0], len(bl)
+    o = torch.empty((N, H, d), device="cuda")
+    ws = torch.empty(gdn.fork_attention_workspace_bytes(R, NB), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    # useful flops: per (query, visible key, head), q.k and p.v, 2 * 2 * d
+    trunk_pairs = R * P * (P + 1) // 2
+    branch_pairs = NB * (Lb * P + Lb * (Lb + 1) // 2)
+    out = {}
+    for name, tq, pairs in (("round", True, trunk_pairs + branch_pairs),
+                            ("branches_only", False, branch_pairs)):
+        def call():
+            gdn.gdn_fork_attention(t["q"], t["k"], t["v"], t["cu"], o, t["bcu"], t["bpar"],
+                                   trunk_queries=tq, workspace=ws)
+        call()
+        ts = []
+        for _ in range(reps):
+            with Timer(torch, stream) as a:
+                call()
+            ts.append(a.ms)
+        ms = float(np.median(ts))
+        useful = pairs * H * 4 * d / (ms / 1e3) / 1e12
+        out[name] = dict(ms=ms, branches_per_s=NB / (ms / 1e3), useful_tflops=useful,
+                         mfma_issued_tflops=1.5 * useful,
+                         frac_of_bf16_peak=1.5 * useful / BF16_MFMA_PEAK_TFLOPS)
+    out["workload"] = ("fork attention: 8 x 8192-token trunks + 160 branches x 64 tokens, "
+                       "H=16, d=128, bf16 q/k/v, fp32 o; split-bf16 probabilities (the "
+                       "p.v products issue 2 MFMAs, so issued = 1.5 x useful)")
+    return out
 
 
 # ---------------------------------------------------------------- per-key decode
@@ -394,6 +438,12 @@ def main():
         log("two-call fork, per-key decay (KDA) ...")
         fork_kda = bench_fork(torch, gdn, gi, args.fork_reps, variant="kda")
 
+    fork_attn = None
+    if not args.no_fork:
+        log("fork attention ...")
+        fork_attn = bench_fork_attention(torch, gdn, gi, args.fork_reps)
+        torch.cuda.empty_cache()
+
     log("per-key decode (KDA, RWKV6-style) ...")
     perkey = {v: bench_decode_perkey(torch, gdn, gi, v) for v in ("kda", "rwkv6")}
     torch.cuda.empty_cache()
@@ -449,6 +499,7 @@ def main():
             "ratio": eager_writes / state_writes},
         "fork": fork,
         "fork_kda": fork_kda,
+        "fork_attention": fork_attn,
         "decode_perkey": perkey,
         "decode_small": small,
         "hbm_probe": probe,

@@ -299,7 +299,7 @@ size_t gdn_fork_attention_workspace_bytes(int n_req, int n_branch);
  *  branch_cu    [n_branch + 1] int32 device: branch b is tokens
  *               [branch_cu[b], branch_cu[b+1]) (absolute, like cu_seqlens)
  *  branch_parent [n_branch] int32 device, request index of each branch
- *  scale        score scale (1/sqrt(d) is the usual choice), finite
+ *  scale        score scale, finite and > 0 (1/sqrt(d) is the usual choice)
  *  trunk_queries 1: trunk rows of o are computed too; 0: trunks only serve
  *               as keys/values (their o rows are left untouched) -- a round
  *               of new branches against trunks computed earlier
@@ -311,8 +311,8 @@ size_t gdn_fork_attention_workspace_bytes(int n_req, int n_branch);
  * [0, n_tokens]. A branch whose parent is outside [0, n_req) gets NaN
  * outputs. Accumulation is fp32 with split-bf16 probabilities.
  * Errors: INVALID_ARG (NULL pointer, negative count, H_kv not dividing H,
- * non-finite scale, bad dtype code), UNSUPPORTED (d, or fp32 q/k/v),
- * WORKSPACE, HIP.
+ * scale not finite and positive, bad dtype code), UNSUPPORTED (d, fp32
+ * q/k/v, or n_tokens * H * d >= 2^31), WORKSPACE, HIP.
  */
 int gdn_fork_attention(const void *q, const void *k, const void *v,
                        const int32_t *cu_seqlens, int n_req,

@@ -254,9 +254,11 @@ int gdn_fork_attention(const void *q, const void *k, const void *v, const int32_
         return GDN_ERR_INVALID_ARG;
     if (!cu_seqlens || (n_branch > 0 && (!branch_cu || !branch_parent)))
         return GDN_ERR_INVALID_ARG;
-    if (!dtype_ok(io_dtype) || !dtype_ok(o_dtype) || !std::isfinite(scale))
+    if (!dtype_ok(io_dtype) || !dtype_ok(o_dtype) || !std::isfinite(scale) || !(scale > 0.f))
         return GDN_ERR_INVALID_ARG;
     if (io_dtype != GDN_BF16 || (d != 64 && d != 128)) return GDN_ERR_UNSUPPORTED;
+    // in-kernel row offsets are 32-bit
+    if ((long long)n_tokens * H * d >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < gdn::attention_workspace_bytes(n_req, n_branch))
         return GDN_ERR_WORKSPACE;
     gdn::AttnArgs a{};

@@ -125,14 +125,19 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
     constexpr int KSD = D / 32;               // reduction steps of S^T over d
     constexpr int NDT = D / 16;               // 16-row d tiles of O^T
     constexpr int KP = D + 8;                 // padded K row in LDS (bf16)
-    constexpr int VP = BN + 8;                // padded V^T row in LDS (bf16)
+    // V^T rows of BN keys padded to 34 words: the transposing stores (16
+    // key pairs of one row per quarter-wave, rows 8 apart across quarter-
+    // waves) and the operand reads (16 consecutive rows, same keys) both
+    // spread over all 32 banks
+    constexpr int VP = BN + 4;
     constexpr int CPR = D / 8;                // 16-byte pieces per key row
     constexpr int KPASS = BN * CPR / kAThreads;       // K pieces per thread
-    constexpr int KPP = 2 * kAThreads / CPR;          // keys per V pass (in pairs)
-    constexpr int VPASS = BN / KPP;                   // V passes (2 pieces each)
-    static_assert(KPASS >= 1 && VPASS >= 1, "block shape");
-    __shared__ __attribute__((aligned(16))) __bf16 s_k[BN * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 s_vt[D * VP];
+    constexpr int PPP = kAThreads / CPR;              // key pairs per V pass
+    constexpr int VPASS = (BN / 2) / PPP;             // V passes (2 pieces each)
+    static_assert(KPASS >= 1 && VPASS >= 1 && PPP >= 16, "block shape");
+    // two buffers: block j + 1 is written while block j is read
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[2 * BN * KP];
+    __shared__ __attribute__((aligned(16))) __bf16 s_vt[2 * D * VP];
 
     const int *ts = static_cast<const int *>(a.ws);
     const int n_seg = a.n_branch + a.n_req;
@@ -181,12 +186,17 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qg + ks * 32);
 
-    const __bf16 *kg = static_cast<const __bf16 *>(a.k);
-    const __bf16 *vg = static_cast<const __bf16 *>(a.v);
-    // stream row of virtual key x (clamped into the tile's keys)
-    auto key_row = [&](int x) {
+    // k / v rows of the two ranges a tile reads (the parent's trunk and the
+    // segment itself); offsets inside a range fit 32 bits (checked on the host)
+    const uint32_t rs = (uint32_t)(Hkv * D);  // elements per stream row
+    const __bf16 *kg = static_cast<const __bf16 *>(a.k) + hk * D;
+    const __bf16 *vg = static_cast<const __bf16 *>(a.v) + hk * D;
+    const __bf16 *k_tr = kg + (size_t)sg.p0 * rs, *k_own = kg + (size_t)sg.t0 * rs;
+    const __bf16 *v_tr = vg + (size_t)sg.p0 * rs, *v_own = vg + (size_t)sg.t0 * rs;
+    // row of virtual key x (clamped into the tile's keys) in range tr / own
+    auto row = [&](const __bf16 *tr, const __bf16 *own, int x) {
         x = min(x, kv_len - 1);
-        return x < sg.plen ? sg.p0 + x : sg.t0 + (x - sg.plen);
+        return x < sg.plen ? tr + (uint32_t)x * rs : own + (uint32_t)(x - sg.plen) * rs;
     };
     bf16x8 kreg[KPASS];
     u32x4 vreg[VPASS][2];
@@ -194,51 +204,61 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int p = 0; p < KPASS; ++p) {
             const int piece = p * kAThreads + tid, r = piece / CPR, c = piece % CPR;
-            kreg[p] = *reinterpret_cast<const bf16x8 *>(
-                kg + ((size_t)key_row(j * BN + r) * Hkv + hk) * D + c * 8);
+            kreg[p] = *reinterpret_cast<const bf16x8 *>(row(k_tr, k_own, j * BN + r) + c * 8);
         }
 #pragma unroll
         for (int p = 0; p < VPASS; ++p) {
-            const int c = tid % CPR, r = p * KPP + 2 * (tid / CPR);
+            const int c = tid / PPP, r = 2 * (p * PPP + tid % PPP);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                vreg[p][u] = *reinterpret_cast<const u32x4 *>(
-                    vg + ((size_t)key_row(j * BN + r + u) * Hkv + hk) * D + c * 8);
+                vreg[p][u] =
+                    *reinterpret_cast<const u32x4 *>(row(v_tr, v_own, j * BN + r + u) + c * 8);
         }
     };
-    auto store_block = [&]() {
+    auto store_block = [&](int buf) {
+        __bf16 *sk = s_k + buf * (BN * KP);
+        __bf16 *sv = s_vt + buf * (D * VP);
 #pragma unroll
         for (int p = 0; p < KPASS; ++p) {
             const int piece = p * kAThreads + tid, r = piece / CPR, c = piece % CPR;
-            *reinterpret_cast<bf16x8 *>(s_k + r * KP + c * 8) = kreg[p];
+            *reinterpret_cast<bf16x8 *>(sk + r * KP + c * 8) = kreg[p];
         }
 #pragma unroll
         for (int p = 0; p < VPASS; ++p) {
-            const int c = tid % CPR, r = p * KPP + 2 * (tid / CPR);
+            const int c = tid / PPP, r = 2 * (p * PPP + tid % PPP);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 // keys r and r + 1 of rows d = 8c + 2x (low halves) and
                 // 8c + 2x + 1 (high halves), each pair as one 4-byte word
                 const uint32_t a0 = vreg[p][0][x], a1 = vreg[p][1][x];
-                *reinterpret_cast<uint32_t *>(s_vt + (c * 8 + 2 * x) * VP + r) =
+                *reinterpret_cast<uint32_t *>(sv + (c * 8 + 2 * x) * VP + r) =
                     (a0 & 0xffffu) | (a1 << 16);
-                *reinterpret_cast<uint32_t *>(s_vt + (c * 8 + 2 * x + 1) * VP + r) =
+                *reinterpret_cast<uint32_t *>(sv + (c * 8 + 2 * x + 1) * VP + r) =
                     (a0 >> 16) | (a1 & 0xffff0000u);
             }
         }
     };
 
-    const float c2 = a.scale * 1.4426950408889634f;  // scores in log2 units
+    // Online softmax in log2 units with a lazily moved reference: the
+    // exponent base m changes only when a block's maximum exceeds it by more
+    // than kLazy, so most blocks skip the rescale of o and of the row sum;
+    // the weights exp2(s - m) then stay below 2^kLazy (exact in fp32 either
+    // way: the same m scales o and the row sum).
+    constexpr float kLazy = 8.f;
+    const float c2 = a.scale * 1.4426950408889634f;  // scale > 0 (checked on the host)
+    const int qp_lo = sg.plen + q_first;              // first query of the tile
     float m = -INFINITY, lsum = 0.f;
     f32x4v acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
     load_block(0);
-    store_block();
+    store_block(0);
+    if (nblk > 1) load_block(1);
     __syncthreads();
     for (int j = 0; j < nblk; ++j) {
-        if (j + 1 < nblk) load_block(j + 1);
+        const __bf16 *sk = s_k + (j & 1) * (BN * KP);
+        const __bf16 *sv = s_vt + (j & 1) * (D * VP);
 
         // S^T: rows = keys kt*16 + g4 + i, column = this lane's query
         f32x4v st[4];
@@ -248,56 +268,73 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
                 const bf16x8 kf =
-                    *reinterpret_cast<const bf16x8 *>(s_k + (kt * 16 + lane % 16) * KP + ks * 32 + g8);
+                    *reinterpret_cast<const bf16x8 *>(sk + (kt * 16 + lane % 16) * KP + ks * 32 + g8);
                 st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[kt], 0, 0, 0);
             }
         }
-        // online softmax of this query over the block (keys after it masked)
+        // keys after a query (and past the tile's keys) only in the last blocks
+        if (j * BN + BN - 1 > qp_lo) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (j * BN + kt * 16 + g4 + i > qp) st[kt][i] = -INFINITY;
+        }
         float mloc = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = j * BN + kt * 16 + g4 + i;
-                st[kt][i] = key <= qp ? st[kt][i] * c2 : -INFINITY;
-                mloc = fmaxf(mloc, st[kt][i]);
-            }
+            for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, st[kt][i]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-        const float mnew = fmaxf(m, mloc);  // finite: key 0 is visible to every query
-        const float alpha = exp2f(m - mnew);
-        m = mnew;
-        lsum *= alpha;
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * c2;
+        if (__builtin_amdgcn_ballot_w64(mloc > m + kLazy) != 0) {
+            const float mn = fmaxf(m, mloc);  // finite: key 0 is visible to every query
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            m = mn;
+            lsum *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-        bf16x8 ph[2], pl[2];
+            for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        }
+        // P^T operands: p = hi + lo with hi the upper half of p's bits
+        // (exact split: lo = p - hi has at most 16 significant bits, of which
+        // bf16 keeps 8 -- p to about 2^-16 relative)
+        u32x4 ph[2];
+        bf16x8 pl[2];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = exp2f(st[kt][i] - mnew);
-                lsum += p;
-                const __bf16 hp = (__bf16)p;
-                ph[kt / 2][(kt % 2) * 4 + i] = hp;
-                pl[kt / 2][(kt % 2) * 4 + i] = (__bf16)(p - (float)hp);
+            for (int i = 0; i < 4; i += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][i], c2, -m));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][i + 1], c2, -m));
+                lsum += p0 + p1;
+                const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
+                const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
+                const int e = (kt % 2) * 4 + i;  // reduction slot of key kt*16 + g4 + i
+                ph[kt / 2][e / 2] = (h0 >> 16) | h1;
+                pl[kt / 2][e] = (__bf16)(p0 - __uint_as_float(h0));
+                pl[kt / 2][e + 1] = (__bf16)(p1 - __uint_as_float(h1));
             }
         // O^T += V^T P^T over the two 32-key halves of the block
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c) {
+            const bf16x8 phc = __builtin_bit_cast(bf16x8, ph[c]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const __bf16 *vp = s_vt + (dt * 16 + lane % 16) * VP + c * 32 + g4;
+                const __bf16 *vp = sv + (dt * 16 + lane % 16) * VP + c * 32 + g4;
                 const bf16x4 v0 = *reinterpret_cast<const bf16x4 *>(vp);
                 const bf16x4 v1 = *reinterpret_cast<const bf16x4 *>(vp + 16);
                 const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[c], acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phc, acc[dt], 0, 0, 0);
                 acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[c], acc[dt], 0, 0, 0);
             }
-        __syncthreads();  // every wave is done with this block's K and V^T
-        if (j + 1 < nblk) {
-            store_block();
-            __syncthreads();
         }
+        // block j + 1 into the other buffer (its readers finished before the
+        // previous barrier), then fetch block j + 2
+        if (j + 1 < nblk) {
+            store_block((j + 1) & 1);
+            if (j + 2 < nblk) load_block(j + 2);
+        }
+        __syncthreads();
     }
 
     // the row sum of a query is split over its 4 lanes

@@ -148,10 +148,15 @@ def test_fork_attention_validation_and_workspace(lib):
     assert call(Hkv=0) == INVALID
     assert call(scale=float("nan")) == INVALID
     assert call(scale=float("inf")) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(scale=-0.1) == INVALID
     assert call(out=2) == INVALID
     assert call(nb=-1) == INVALID
     assert call(d=96) == UNSUPPORTED
     assert call(d=32) == UNSUPPORTED
     assert call(io=0) == UNSUPPORTED               # fp32 q/k/v not built
+    # 32-bit in-kernel row offsets: n_tokens * H * d < 2^31
+    assert lib.gdn_fork_attention(FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 5, 1 << 21, 8, 2, 128,
+                                  0.1, 1, FAKE, 1, 0, FAKE, need, NULL) == UNSUPPORTED
     assert call(ws=NULL) == WORKSPACE
     assert call(ws_bytes=need - 1) == WORKSPACE
