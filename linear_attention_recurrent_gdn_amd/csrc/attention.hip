@@ -280,14 +280,18 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
                 for (int i = 0; i < 4; ++i)
                     if (j * BN + kt * 16 + g4 + i > qp) st[kt][i] = -INFINITY;
         }
+        // the reference is shared by a query's 4 lanes (their products are
+        // summed by the matrix cores); lanes compare their own maxima and
+        // only a move of the reference combines them
         float mloc = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, st[kt][i]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * c2;
+        mloc *= c2;
         if (__builtin_amdgcn_ballot_w64(mloc > m + kLazy) != 0) {
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
             const float mn = fmaxf(m, mloc);  // finite: key 0 is visible to every query
             const float alpha = __builtin_amdgcn_exp2f(m - mn);
             m = mn;
