@@ -49,8 +49,11 @@ namespace gdn {
 namespace {
 
 constexpr int kAThreads = 256;
-constexpr int BM = 64;   // queries per workgroup (16 per wave)
 constexpr int BN = 64;   // keys per block
+// queries per workgroup: 16 * QR per wave. Branches (typically short) use
+// QR = 1; trunks QR = 2, where each K / V operand read from LDS feeds two
+// query groups (half the LDS traffic per product).
+constexpr int kQrBranch = 1, kQrTrunk = 2;
 constexpr int kGroup = 16;  // consecutive work items that share an XCD (and its L2)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -104,7 +107,10 @@ __global__ __launch_bounds__(kAThreads) void attn_plan_kernel(AttnArgs a, int ma
     for (int base = 0; base < n_seg; base += kAThreads) {
         const int seg = base + tid;
         int c = 0;
-        if (seg < n_seg) c = (segment(a, seg).len + BM - 1) / BM;
+        if (seg < n_seg) {
+            const int bm = 64 * (seg < a.n_branch ? kQrBranch : kQrTrunk);
+            c = (segment(a, seg).len + bm - 1) / bm;
+        }
         s_scan[tid] = c;
         __syncthreads();
         for (int off = 1; off < kAThreads; off <<= 1) {
@@ -120,43 +126,21 @@ __global__ __launch_bounds__(kAThreads) void attn_plan_kernel(AttnArgs a, int ma
     if (tid == 0) ts[n_seg] = min(run, max_tiles);
 }
 
-template <int D, typename TO>
-__global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
+// One query tile of one segment and head: 16 * QR queries per wave.
+template <int D, typename TO, int QR>
+__device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int h, int tile,
+                                          __bf16 *s_k, __bf16 *s_vt) {
+    constexpr int BM = 64 * QR;               // queries per workgroup
     constexpr int KSD = D / 32;               // reduction steps of S^T over d
     constexpr int NDT = D / 16;               // 16-row d tiles of O^T
     constexpr int KP = D + 8;                 // padded K row in LDS (bf16)
-    // V^T rows of BN keys padded to 34 words: the transposing stores (16
-    // key pairs of one row per quarter-wave, rows 8 apart across quarter-
-    // waves) and the operand reads (16 consecutive rows, same keys) both
-    // spread over all 32 banks
-    constexpr int VP = BN + 4;
+    constexpr int VP = BN + 4;                // padded V^T row (see attn_kernel)
     constexpr int CPR = D / 8;                // 16-byte pieces per key row
     constexpr int KPASS = BN * CPR / kAThreads;       // K pieces per thread
     constexpr int PPP = kAThreads / CPR;              // key pairs per V pass
     constexpr int VPASS = (BN / 2) / PPP;             // V passes (2 pieces each)
     static_assert(KPASS >= 1 && VPASS >= 1 && PPP >= 16, "block shape");
-    // two buffers: block j + 1 is written while block j is read
-    __shared__ __attribute__((aligned(16))) __bf16 s_k[2 * BN * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 s_vt[2 * D * VP];
 
-    const int *ts = static_cast<const int *>(a.ws);
-    const int n_seg = a.n_branch + a.n_req;
-    const int T = ts[n_seg];
-    // block -> work item: groups of kGroup consecutive items per XCD
-    // (blocks are dispatched to the 8 XCDs round-robin)
-    const int b = blockIdx.x, xcd = b % 8, local = b / 8;
-    const int wi = ((local / kGroup) * 8 + xcd) * kGroup + local % kGroup;
-    if (wi >= a.H * T) return;
-    const int h = wi / T, t = wi % T;
-    int lo = 0, hi = n_seg;  // ts[lo] <= t < ts[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (ts[mid] <= t) lo = mid;
-        else hi = mid;
-    }
-    const Seg sg = segment(a, lo);
-    const int ntile = ts[lo + 1] - ts[lo];
-    const int tile = ntile - 1 - (t - ts[lo]);  // the longest tiles of a segment first
     const int q_first = tile * BM;
     const int L = min(BM, sg.len - q_first);
     const int H = a.H;
@@ -172,19 +156,23 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
 
     const int hk = h / (H / a.Hkv);
     const int Hkv = a.Hkv;
-    const int qcol = w * 16 + lane % 16;      // this lane's query in the tile
-    const int qrow = min(qcol, L - 1);        // clamped for the rows past the tile end
-    const int qp = sg.plen + q_first + qrow;  // its virtual position
-    const int kv_len = sg.plen + q_first + L; // virtual keys the tile reads
+    const int kv_len = sg.plen + q_first + L;  // virtual keys the tile reads
     const int nblk = (kv_len + BN - 1) / BN;
     const int g4 = (lane / 16) * 4, g8 = (lane / 16) * 8;
-
-    // Q^T operand: 8 consecutive d of this lane's query per reduction step
-    const __bf16 *qg = static_cast<const __bf16 *>(a.q) +
-                       ((size_t)(sg.t0 + q_first + qrow) * H + h) * D + g8;
-    bf16x8 qf[KSD];
+    // query group qg of this wave: tile rows w*16*QR + qg*16 + lane % 16
+    int qcol[QR], qp[QR];
+    bf16x8 qf[QR][KSD];  // Q^T operand: 8 consecutive d per reduction step
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qg + ks * 32);
+    for (int qg = 0; qg < QR; ++qg) {
+        qcol[qg] = w * 16 * QR + qg * 16 + lane % 16;
+        const int qrow = min(qcol[qg], L - 1);  // clamped for rows past the tile end
+        qp[qg] = sg.plen + q_first + qrow;      // virtual position
+        const __bf16 *qsrc = static_cast<const __bf16 *>(a.q) +
+                             ((size_t)(sg.t0 + q_first + qrow) * H + h) * D + g8;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+            qf[qg][ks] = *reinterpret_cast<const bf16x8 *>(qsrc + ks * 32);
+    }
 
     // k / v rows of the two ranges a tile reads (the parent's trunk and the
     // segment itself); offsets inside a range fit 32 bits (checked on the host)
@@ -247,10 +235,15 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
     constexpr float kLazy = 8.f;
     const float c2 = a.scale * 1.4426950408889634f;  // scale > 0 (checked on the host)
     const int qp_lo = sg.plen + q_first;              // first query of the tile
-    float m = -INFINITY, lsum = 0.f;
-    f32x4v acc[NDT];
+    float m[QR], lsum[QR];
+    f32x4v acc[QR][NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int qg = 0; qg < QR; ++qg) {
+        m[qg] = -INFINITY;
+        lsum[qg] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[qg][dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
 
     load_block(0);
     store_block(0);
@@ -260,76 +253,89 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
         const __bf16 *sk = s_k + (j & 1) * (BN * KP);
         const __bf16 *sv = s_vt + (j & 1) * (D * VP);
 
-        // S^T: rows = keys kt*16 + g4 + i, column = this lane's query
-        f32x4v st[4];
+        // S^T: rows = keys kt*16 + g4 + i, column = the lane's query of group qg
+        f32x4v st[QR][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            st[kt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qg = 0; qg < QR; ++qg) st[qg][kt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
                 const bf16x8 kf =
                     *reinterpret_cast<const bf16x8 *>(sk + (kt * 16 + lane % 16) * KP + ks * 32 + g8);
-                st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[kt], 0, 0, 0);
+#pragma unroll
+                for (int qg = 0; qg < QR; ++qg)
+                    st[qg][kt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][ks], st[qg][kt], 0, 0, 0);
             }
         }
         // keys after a query (and past the tile's keys) only in the last blocks
         if (j * BN + BN - 1 > qp_lo) {
 #pragma unroll
+            for (int qg = 0; qg < QR; ++qg)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (j * BN + kt * 16 + g4 + i > qp[qg]) st[qg][kt][i] = -INFINITY;
+        }
+        u32x4 ph[QR][2];
+        bf16x8 pl[QR][2];
+#pragma unroll
+        for (int qg = 0; qg < QR; ++qg) {
+            // the reference is shared by a query's 4 lanes (their products
+            // are summed by the matrix cores); lanes compare their own maxima
+            // and only a move of the reference combines them
+            float mloc = -INFINITY;
+#pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (j * BN + kt * 16 + g4 + i > qp) st[kt][i] = -INFINITY;
-        }
-        // the reference is shared by a query's 4 lanes (their products are
-        // summed by the matrix cores); lanes compare their own maxima and
-        // only a move of the reference combines them
-        float mloc = -INFINITY;
+                for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, st[qg][kt][i]);
+            mloc *= c2;
+            if (__builtin_amdgcn_ballot_w64(mloc > m[qg] + kLazy) != 0) {
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+                const float mn = fmaxf(m[qg], mloc);  // finite: key 0 is visible to every query
+                const float alpha = __builtin_amdgcn_exp2f(m[qg] - mn);
+                m[qg] = mn;
+                lsum[qg] *= alpha;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, st[kt][i]);
-        mloc *= c2;
-        if (__builtin_amdgcn_ballot_w64(mloc > m + kLazy) != 0) {
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-            const float mn = fmaxf(m, mloc);  // finite: key 0 is visible to every query
-            const float alpha = __builtin_amdgcn_exp2f(m - mn);
-            m = mn;
-            lsum *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-        }
-        // P^T operands: p = hi + lo with hi the upper half of p's bits
-        // (exact split: lo = p - hi has at most 16 significant bits, of which
-        // bf16 keeps 8 -- p to about 2^-16 relative)
-        u32x4 ph[2];
-        bf16x8 pl[2];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][i], c2, -m));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][i + 1], c2, -m));
-                lsum += p0 + p1;
-                const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
-                const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
-                const int e = (kt % 2) * 4 + i;  // reduction slot of key kt*16 + g4 + i
-                ph[kt / 2][e / 2] = (h0 >> 16) | h1;
-                pl[kt / 2][e] = (__bf16)(p0 - __uint_as_float(h0));
-                pl[kt / 2][e + 1] = (__bf16)(p1 - __uint_as_float(h1));
+                for (int dt = 0; dt < NDT; ++dt) acc[qg][dt] *= alpha;
             }
+            // P^T operands: p = hi + lo with hi the upper half of p's bits
+            // (exact split: lo = p - hi has at most 16 significant bits, of
+            // which bf16 keeps 8 -- p to about 2^-16 relative)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(st[qg][kt][i], c2, -m[qg]));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(st[qg][kt][i + 1], c2, -m[qg]));
+                    lsum[qg] += p0 + p1;
+                    const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
+                    const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
+                    const int e = (kt % 2) * 4 + i;  // reduction slot of key kt*16 + g4 + i
+                    ph[qg][kt / 2][e / 2] = (h0 >> 16) | h1;
+                    pl[qg][kt / 2][e] = (__bf16)(p0 - __uint_as_float(h0));
+                    pl[qg][kt / 2][e + 1] = (__bf16)(p1 - __uint_as_float(h1));
+                }
+        }
         // O^T += V^T P^T over the two 32-key halves of the block
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const bf16x8 phc = __builtin_bit_cast(bf16x8, ph[c]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const __bf16 *vp = sv + (dt * 16 + lane % 16) * VP + c * 32 + g4;
                 const bf16x4 v0 = *reinterpret_cast<const bf16x4 *>(vp);
                 const bf16x4 v1 = *reinterpret_cast<const bf16x4 *>(vp + 16);
                 const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phc, acc[dt], 0, 0, 0);
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[c], acc[dt], 0, 0, 0);
+#pragma unroll
+                for (int qg = 0; qg < QR; ++qg) {
+                    acc[qg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        vf, __builtin_bit_cast(bf16x8, ph[qg][c]), acc[qg][dt], 0, 0, 0);
+                    acc[qg][dt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qg][c], acc[qg][dt], 0, 0, 0);
+                }
             }
         }
         // block j + 1 into the other buffer (its readers finished before the
@@ -341,23 +347,63 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
         __syncthreads();
     }
 
-    // the row sum of a query is split over its 4 lanes
-    float ltot = lsum + __shfl_xor(lsum, 16, kWave);
-    ltot += __shfl_xor(ltot, 32, kWave);
-    if (qcol < L) {
-        TO *orow = o + ((size_t)(sg.t0 + q_first + qcol) * H + h) * D;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+    for (int qg = 0; qg < QR; ++qg) {
+        // the row sum of a query is split over its 4 lanes
+        float ltot = lsum[qg] + __shfl_xor(lsum[qg], 16, kWave);
+        ltot += __shfl_xor(ltot, 32, kWave);
+        if (qcol[qg] < L) {
+            TO *orow = o + ((size_t)(sg.t0 + q_first + qcol[qg]) * H + h) * D;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) orow[dt * 16 + g4 + i] = from_f32<TO>(acc[dt][i] / ltot);
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    orow[dt * 16 + g4 + i] = from_f32<TO>(acc[qg][dt][i] / ltot);
+        }
     }
+}
+
+template <int D, typename TO>
+__global__ __launch_bounds__(kAThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnArgs a) {
+    constexpr int KP = D + 8;
+    // V^T rows of BN keys padded to 34 words: the transposing stores (16
+    // key pairs of one row per quarter-wave, rows 8 apart across quarter-
+    // waves) and the operand reads (16 consecutive rows, same keys) both
+    // spread over all 32 banks
+    constexpr int VP = BN + 4;
+    // two buffers: block j + 1 is written while block j is read
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[2 * BN * KP];
+    __shared__ __attribute__((aligned(16))) __bf16 s_vt[2 * D * VP];
+
+    const int *ts = static_cast<const int *>(a.ws);
+    const int n_seg = a.n_branch + a.n_req;
+    const int T = ts[n_seg];
+    // block -> work item: groups of kGroup consecutive items per XCD
+    // (blocks are dispatched to the 8 XCDs round-robin)
+    const int b = blockIdx.x, xcd = b % 8, local = b / 8;
+    const int wi = ((local / kGroup) * 8 + xcd) * kGroup + local % kGroup;
+    if (wi >= a.H * T) return;
+    const int h = wi / T, t = wi % T;
+    int lo = 0, hi = n_seg;  // ts[lo] <= t < ts[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ts[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    const Seg sg = segment(a, lo);
+    const int ntile = ts[lo + 1] - ts[lo];
+    const int tile = ntile - 1 - (t - ts[lo]);  // the longest tiles of a segment first
+    if (lo < a.n_branch)
+        attn_tile<D, TO, kQrBranch>(a, sg, h, tile, s_k, s_vt);
+    else
+        attn_tile<D, TO, kQrTrunk>(a, sg, h, tile, s_k, s_vt);
 }
 
 template <int D, typename TO>
 hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
     const int n_seg = a.n_branch + a.n_req;
     if (n_seg == 0) return hipSuccess;
-    const long long max_tiles = (long long)(a.n_tokens + BM - 1) / BM + n_seg;
+    const long long max_tiles = (long long)(a.n_tokens + 63) / 64 + n_seg;  // tiles of >= 64
     const long long items = max_tiles * a.H;
     const long long per = 8LL * kGroup;
     const long long blocks = (items + per - 1) / per * per;
