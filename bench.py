@@ -201,7 +201,15 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
         tp.append(a.ms)
         tf.append(b.ms)
     tp_ms, tf_ms = float(np.median(tp)), float(np.median(tf))
+    # dense-tile work of the chunked form per token-head (d_k = d_v = d,
+    # chunk C): 5Cd + 3d^2 + C^2/6 multiply-adds; split-bf16 issues 3x
+    C = w["chunk"]
+    mac = 5 * C * d + 3 * d * d + C * C / 6
+    pre_tflops = Np * H * 2 * mac / (tp_ms / 1e3) / 1e12
     return dict(branches=NB, prefill_ms=tp_ms, fork_ms=tf_ms,
+                prefill_dense_tile_tflops=pre_tflops,
+                prefill_mfma_issued_tflops=3 * pre_tflops,
+                prefill_mfma_frac_of_bf16_peak=3 * pre_tflops / BF16_MFMA_PEAK_TFLOPS,
                 branches_per_s=NB / ((tp_ms + tf_ms) / 1e3),
                 branch_phase_branches_per_s=NB / (tf_ms / 1e3),
                 prefix_token_heads_per_s=Np * H / (tp_ms / 1e3))
@@ -264,60 +272,97 @@ def bench_decode_perkey(torch, gdn, gi, variant, K=64, W=16):
     run_deferred(torch, gdn, t, logs, base, o, M, range(W), variant)
     with Timer(torch, stream) as tm:
         run_deferred(torch, gdn, t, logs, base, o, M, range(W, W + K), variant)
-    alg, _ = schedule_bytes(phase, H, M, W, K, per_key=True, has_beta=variant != "rwkv6")
+    alg, writes = schedule_bytes(phase, H, M, W, K, per_key=True, has_beta=variant != "rwkv6")
+    # eager on the same inputs
+    state = t["state0"].clone()
+    beta = None if variant == "rwkv6" else t["beta"]
+
+    def eager(rng):
+        for i in rng:
+            s = i % T
+            gdn.gdn_decode_eager(t["q"][s], t["k"][s], t["v"][s], t["log_alpha"][s],
+                                 None if beta is None else beta[s], state, o, variant=variant)
+    eager(range(W))
+    with Timer(torch, stream) as te:
+        eager(range(W, W + K))
+    hs = B * H * K
+    eager_b = 2 * STATE_B + QKV_B + 4 * D + (4 if beta is not None else 0) + O_B
     return dict(workload=f"perkey {variant}: deferred M=8, B={B}, H={H}, d=128, per-key "
                          "log a, per-slot log phases",
-                value=B * H * K / (tm.ms / 1e3), unit="head-steps/s",
-                us_per_step=tm.ms * 1e3 / K, hbm_gbps_effective=alg / (tm.ms / 1e3) / 1e9)
+                value=hs / (tm.ms / 1e3), unit="head-steps/s",
+                us_per_step=tm.ms * 1e3 / K, hbm_gbps_effective=alg / (tm.ms / 1e3) / 1e9,
+                eager_head_steps_per_s=hs / (te.ms / 1e3), eager_us_per_step=te.ms * 1e3 / K,
+                eager_gbps_effective=eager_b * hs / (te.ms / 1e3) / 1e9,
+                speedup_deferred_vs_eager=te.ms / tm.ms,
+                state_write_ratio_eager_vs_deferred=STATE_B * hs / writes)
 
 
 # ---------------------------------------------------------------- decode_small
 def bench_decode_small(torch, gdn, gi, reps=5):
     """The small decode workload (B=64, H=16, d=128: a 64 MiB state that the
-    256 MB last-level cache holds), deferred M=8 over 256 steps, launched one
-    call at a time and as one captured HIP graph replayed; the steps are
-    short enough that launch gaps matter."""
+    256 MB last-level cache holds), 256 steps from empty logs: eager and the
+    deferred schedule with M in {1, 4, 8, 16}, each launched one call at a
+    time and as one captured HIP graph replayed (the steps are short enough
+    that launch gaps matter); head-steps/s, algorithmic GB/s and state-write
+    bytes per head-step."""
     w = gi.WORKLOADS["decode_small"]
-    B, H, d, T, M = w["B"], w["H"], w["d"], w["steps"], 8
+    B, H, d, T = w["B"], w["H"], w["d"], w["steps"]
     t = gi.torch_decode_inputs(B, H, d, d, T, seed=0)
-    base = t["state0"].clone()
-    logs = dict(log_u=torch.zeros((B, H, M, d), device="cuda"),
-                log_k=torch.zeros((B, H, M, d), device="cuda", dtype=torch.bfloat16),
-                log_lam=torch.zeros((B, H, M), device="cuda"),
-                log_len=torch.zeros((B, H), device="cuda", dtype=torch.int32))
     o = torch.empty((B, H, d), device="cuda")
-
-    def steps():
-        run_deferred(torch, gdn, t, logs, base, o, M, range(T))
-
     stream = torch.cuda.current_stream()
-    steps()
-    plain = []
-    for _ in range(reps):
-        with Timer(torch, stream) as a:
-            steps()
-        plain.append(a.ms)
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        steps()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        steps()
-    graph.replay()
-    graphed = []
-    for _ in range(reps):
-        with Timer(torch, stream) as a:
-            graph.replay()
-        graphed.append(a.ms)
     hs = B * H * T
-    p_ms, g_ms = float(np.median(plain)), float(np.median(graphed))
-    return dict(workload="decode_small: deferred M=8, B=64, H=16, d=128, 256 steps "
-                         "(64 MiB state, cache-resident)",
-                plain_head_steps_per_s=hs / (p_ms / 1e3), plain_us_per_step=p_ms * 1e3 / T,
-                graph_head_steps_per_s=hs / (g_ms / 1e3), graph_us_per_step=g_ms * 1e3 / T)
+    zero = np.zeros(B, dtype=np.int64)
+
+    def timed(steps):
+        steps()
+        plain = []
+        for _ in range(reps):
+            with Timer(torch, stream) as a:
+                steps()
+            plain.append(a.ms)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            steps()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            steps()
+        graph.replay()
+        graphed = []
+        for _ in range(reps):
+            with Timer(torch, stream) as a:
+                graph.replay()
+            graphed.append(a.ms)
+        return float(np.median(plain)), float(np.median(graphed))
+
+    out = {"workload": "decode_small: B=64, H=16, d=128, 256 steps from empty logs "
+                       "(64 MiB state, cache-resident)"}
+    cases = [("eager", None)] + [(f"M={M}", M) for M in w["Ms"]]
+    for name, M in cases:
+        if M is None:
+            state = t["state0"].clone()
+
+            def steps():
+                run_eager(torch, gdn, t, state, o, range(T))
+            nbytes, writes = eager_bytes() * hs, STATE_B * hs
+        else:
+            base = t["state0"].clone()
+            logs = dict(log_u=torch.zeros((B, H, M, d), device="cuda"),
+                        log_k=torch.zeros((B, H, M, d), device="cuda", dtype=torch.bfloat16),
+                        log_lam=torch.zeros((B, H, M), device="cuda"),
+                        log_len=torch.zeros((B, H), device="cuda", dtype=torch.int32))
+
+            def steps(base=base, logs=logs, M=M):
+                run_deferred(torch, gdn, t, logs, base, o, M, range(T))
+            nbytes, writes = schedule_bytes(zero, H, M, 0, T)
+        p_ms, g_ms = timed(steps)
+        out[name] = dict(plain_head_steps_per_s=hs / (p_ms / 1e3), plain_us_per_step=p_ms * 1e3 / T,
+                         graph_head_steps_per_s=hs / (g_ms / 1e3), graph_us_per_step=g_ms * 1e3 / T,
+                         graph_gbps_effective=nbytes / (g_ms / 1e3) / 1e9,
+                         state_write_bytes_per_head_step=writes / hs)
+    return out
 
 
 # ---------------------------------------------------------------- HBM probe
@@ -366,9 +411,42 @@ def cpu_baseline(torch, t, target_s):
     oracle.decode(q, k, v, la, be, s0, nthreads=threads)
     dt = time.perf_counter() - t0
     hs = b * H * steps
+    # one thread, on a small sample
+    q, k, v, la, be, s0 = sample(1, 64)
+    t0 = time.perf_counter()
+    oracle.decode(q, k, v, la, be, s0, nthreads=1)
+    one = H * 64 / (time.perf_counter() - t0)
     return dict(value=hs / dt, unit="head-steps/s", cores=threads, kind="oracle",
                 sample=f"{b} of {B} sequences x {H} heads x {steps} steps ({hs} head-steps, "
-                       f"plain fp64 recurrence, {dt:.1f} s)")
+                       f"plain fp64 recurrence, {dt:.1f} s)",
+                value_one_thread=one, sample_one_thread=f"1 sequence x {H} heads x 64 steps")
+
+
+def cpu_fork_baseline(torch, gi):
+    """The fp64 oracle on a bounded sample of the fork workload: one request
+    of the fork_prefill stream cut to a 1024-token context, its 20 branches
+    of 64 tokens, all 16 heads (prefill + branches, conv, q/k norm)."""
+    import oracle
+
+    w = gi.WORKLOADS["fork_prefill"]
+    prefix = 1024
+    pl, bl, par = gi.fork_layout(1, prefix, w["branches_per_req"], w["branch_len"])
+    inp = gi.seq_inputs(pl, bl, par, w["H"], w["d"], w["d"], io="bf16", conv=True,
+                        la_range=w["la_range"], seed=0)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    _, st, win = oracle.prefill(inp.q[:prefix], inp.k[:prefix], inp.v[:prefix],
+                                inp.log_alpha[:prefix], inp.beta[:prefix], inp.cu_seqlens,
+                                conv_w=inp.conv_w, qk_norm=True, nthreads=threads)
+    oracle.fork(inp.q[prefix:], inp.k[prefix:], inp.v[prefix:], inp.log_alpha[prefix:],
+                inp.beta[prefix:], inp.branch_cu, inp.branch_parent, st, parent_window=win,
+                conv_w=inp.conv_w, qk_norm=True, nthreads=threads)
+    dt = time.perf_counter() - t0
+    nb = len(bl)
+    toks = (prefix + nb * w["branch_len"]) * w["H"]
+    return dict(branches_per_s=nb / dt, token_heads_per_s=toks / dt, cores=threads,
+                sample=f"1 request, {prefix}-token context + {nb} branches x "
+                       f"{w['branch_len']} tokens, H={w['H']}, d={w['d']} ({dt:.1f} s)")
 
 
 def measured_traffic(ms_per_launch):
@@ -457,6 +535,7 @@ def main():
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         cpu = cpu_baseline(torch, t, args.cpu_seconds)
+        cpu["fork"] = cpu_fork_baseline(torch, gi)
 
     out = {
         "metric": METRIC,
