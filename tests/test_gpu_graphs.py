@@ -182,3 +182,54 @@ def test_fixed_capacity_graph_serves_changing_rounds():
         assert torch.equal(st, st_r), lay
         assert torch.equal(win, win_r), lay
         assert torch.equal(o[:used], o_r[:used]), lay
+
+
+def test_fork_attention_graph_serves_changing_rounds():
+    """Fork attention captured once for a stream capacity (2 trunks, 3
+    branches, 600 tokens) replays rounds whose trunk and branch offsets and
+    parents are rewritten in place (shorter streams, empty segments, moved
+    parents); each replay equals an eager call with the same metadata."""
+    H, Hkv, d, N = 4, 2, 128, 600
+    t = gi.torch_attention_inputs([N], [], [], H=H, Hkv=Hkv, d=d, seed=21)
+    cu = torch.zeros(3, dtype=torch.int32, device=DEV)
+    bcu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    par = torch.zeros(3, dtype=torch.int32, device=DEV)
+    ws = torch.empty(gdn.fork_attention_workspace_bytes(2, 3), dtype=torch.uint8, device=DEV)
+    o = torch.empty((N, H, d), device=DEV)
+
+    def run(cu_t, bcu_t, par_t, o_t):
+        gdn.gdn_fork_attention(t["q"], t["k"], t["v"], cu_t, o_t, bcu_t, par_t, workspace=ws)
+
+    rounds = [([0, 300, 450], [450, 500, 564, 600], [0, 1, 0]),
+              ([0, 0, 200], [200, 200, 264, 265], [1, 0, 1]),
+              ([0, 129, 130], [130, 194, 258, 400], [1, 1, 0])]
+
+    def load(lay):
+        cu.copy_(torch.tensor(lay[0], dtype=torch.int32))
+        bcu.copy_(torch.tensor(lay[1], dtype=torch.int32))
+        par.copy_(torch.tensor(lay[2], dtype=torch.int32))
+
+    load(rounds[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(cu, bcu, par, o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(cu, bcu, par, o)
+    for lay in rounds * 2:
+        load(lay)
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_r = torch.full_like(o, float("nan"))
+        run(torch.tensor(lay[0], dtype=torch.int32, device=DEV),
+            torch.tensor(lay[1], dtype=torch.int32, device=DEV),
+            torch.tensor(lay[2], dtype=torch.int32, device=DEV), o_r)
+        torch.cuda.synchronize()
+        used = lay[1][-1]
+        assert torch.equal(o[:used], o_r[:used]), lay
+        assert not torch.isnan(o[:used]).any(), lay
