@@ -96,6 +96,26 @@ __device__ __forceinline__ Seg segment(const AttnArgs &a, int seg) {
     return s;
 }
 
+// Branches 2i and 2i + 1 share one tile of 128 queries (64 each, two query
+// groups per wave like a trunk tile) when they hang off the same valid
+// request and are at most 64 tokens long: both read the same trunk, each
+// then its own tokens (a branch's keys are invisible to the other's
+// queries).
+__device__ __forceinline__ bool pair_first(const AttnArgs &a, int b) {
+    if ((b & 1) || b + 1 >= a.n_branch) return false;
+    const Seg x = segment(a, b), y = segment(a, b + 1);
+    return x.ok && y.ok && a.bparent[b] == a.bparent[b + 1] && x.len <= 64 && y.len <= 64;
+}
+
+// query tiles of segment seg: trunks of 128 queries, branches of 64 or in
+// pairs
+__device__ __forceinline__ int seg_tiles(const AttnArgs &a, int seg) {
+    if (seg >= a.n_branch) return (segment(a, seg).len + 64 * kQrTrunk - 1) / (64 * kQrTrunk);
+    if (pair_first(a, seg)) return segment(a, seg).len + segment(a, seg + 1).len > 0 ? 1 : 0;
+    if ((seg & 1) && pair_first(a, seg - 1)) return 0;
+    return (segment(a, seg).len + 64 * kQrBranch - 1) / (64 * kQrBranch);
+}
+
 // ws[seg] = first tile of segment seg, ws[n_seg] = number of tiles, all
 // capped at max_tiles (the grid's capacity; only overlapping segments,
 // which the interface excludes, can reach it).
@@ -107,10 +127,7 @@ __global__ __launch_bounds__(kAThreads) void attn_plan_kernel(AttnArgs a, int ma
     for (int base = 0; base < n_seg; base += kAThreads) {
         const int seg = base + tid;
         int c = 0;
-        if (seg < n_seg) {
-            const int bm = 64 * (seg < a.n_branch ? kQrBranch : kQrTrunk);
-            c = (segment(a, seg).len + bm - 1) / bm;
-        }
+        if (seg < n_seg) c = seg_tiles(a, seg);
         s_scan[tid] = c;
         __syncthreads();
         for (int off = 1; off < kAThreads; off <<= 1) {
@@ -126,10 +143,14 @@ __global__ __launch_bounds__(kAThreads) void attn_plan_kernel(AttnArgs a, int ma
     if (tid == 0) ts[n_seg] = min(run, max_tiles);
 }
 
-// One query tile of one segment and head: 16 * QR queries per wave.
-template <int D, typename TO, int QR>
-__device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int h, int tile,
-                                          __bf16 *s_k, __bf16 *s_vt) {
+// One query tile of one segment and head: 16 * QR queries per wave. PAIR:
+// a tile of two branches sg (rows 0..63) and sb (rows 64..127) of the same
+// request; their virtual keys are the trunk, then sg's tokens, then sb's,
+// and sb's queries skip sg's tokens.
+template <int D, typename TO, int QR, bool PAIR>
+__device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, const Seg &sb, int h,
+                                          int tile, __bf16 *s_k, __bf16 *s_vt) {
+    static_assert(!PAIR || QR == 2, "a branch pair fills two query groups per wave");
     constexpr int BM = 64 * QR;               // queries per workgroup
     constexpr int KSD = D / 32;               // reduction steps of S^T over d
     constexpr int NDT = D / 16;               // 16-row d tiles of O^T
@@ -141,13 +162,14 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int 
     constexpr int VPASS = (BN / 2) / PPP;             // V passes (2 pieces each)
     static_assert(KPASS >= 1 && VPASS >= 1 && PPP >= 16, "block shape");
 
-    const int q_first = tile * BM;
-    const int L = min(BM, sg.len - q_first);
+    const int q_first = PAIR ? 0 : tile * BM;
+    const int L = PAIR ? BM : min(BM, sg.len - q_first);
     const int H = a.H;
-    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     TO *o = static_cast<TO *>(a.o);
 
-    if (!sg.ok) {  // a branch with an invalid parent: NaN outputs
+    if (!PAIR && !sg.ok) {  // a branch with an invalid parent: NaN outputs
         for (int idx = tid; idx < L * D; idx += kAThreads)
             o[((size_t)(sg.t0 + q_first + idx / D) * H + h) * D + idx % D] =
                 from_f32<TO>(quiet_nan());
@@ -156,35 +178,60 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int 
 
     const int hk = h / (H / a.Hkv);
     const int Hkv = a.Hkv;
-    const int kv_len = sg.plen + q_first + L;  // virtual keys the tile reads
+    const int la = PAIR ? sg.len : 0;  // keys of the first branch of a pair
+    // virtual keys the tile reads
+    const int kv_len = PAIR ? sg.plen + sg.len + sb.len : sg.plen + q_first + L;
     const int nblk = (kv_len + BN - 1) / BN;
     const int g4 = (lane / 16) * 4, g8 = (lane / 16) * 8;
-    // query group qg of this wave: tile rows w*16*QR + qg*16 + lane % 16
-    int qcol[QR], qp[QR];
+    // query group qg of this wave: tile row w*16*QR + qg*16 + lane % 16;
+    // its stream token, virtual position, validity, and the virtual keys
+    // [hlo, hhi) it skips (the other branch of a pair)
+    int qtok[QR], qp[QR], hlo[QR], hhi[QR];
+    bool qok[QR];
     bf16x8 qf[QR][KSD];  // Q^T operand: 8 consecutive d per reduction step
 #pragma unroll
     for (int qg = 0; qg < QR; ++qg) {
-        qcol[qg] = w * 16 * QR + qg * 16 + lane % 16;
-        const int qrow = min(qcol[qg], L - 1);  // clamped for rows past the tile end
-        qp[qg] = sg.plen + q_first + qrow;      // virtual position
-        const __bf16 *qsrc = static_cast<const __bf16 *>(a.q) +
-                             ((size_t)(sg.t0 + q_first + qrow) * H + h) * D + g8;
+        const int r = w * 16 * QR + qg * 16 + lane % 16;
+        if constexpr (PAIR) {
+            const bool second = w >= 2;  // rows 64..127: waves 2 and 3
+            const int pos = r & 63, len = second ? sb.len : sg.len;
+            const int posc = len > 0 ? min(pos, len - 1) : 0;  // clamped for rows past the end
+            qok[qg] = pos < len;
+            // an empty branch's rows read the other (non-empty) branch's token
+            qtok[qg] = len > 0 ? (second ? sb.t0 : sg.t0) + posc : (second ? sg.t0 : sb.t0);
+            qp[qg] = sg.plen + (second ? sg.len : 0) + posc;
+            hlo[qg] = second ? sg.plen : 0;
+            hhi[qg] = second ? sg.plen + sg.len : 0;
+        } else {
+            const int qrow = min(r, L - 1);  // clamped for rows past the tile end
+            qok[qg] = r < L;
+            qtok[qg] = sg.t0 + q_first + qrow;
+            qp[qg] = sg.plen + q_first + qrow;
+            hlo[qg] = hhi[qg] = 0;
+        }
+        const __bf16 *qsrc =
+            static_cast<const __bf16 *>(a.q) + ((size_t)qtok[qg] * H + h) * D + g8;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks)
             qf[qg][ks] = *reinterpret_cast<const bf16x8 *>(qsrc + ks * 32);
     }
 
-    // k / v rows of the two ranges a tile reads (the parent's trunk and the
-    // segment itself); offsets inside a range fit 32 bits (checked on the host)
+    // k / v rows of the ranges a tile reads (the parent's trunk, the
+    // segment itself, and for a pair the second branch); offsets inside a
+    // range fit 32 bits (checked on the host)
     const uint32_t rs = (uint32_t)(Hkv * D);  // elements per stream row
     const __bf16 *kg = static_cast<const __bf16 *>(a.k) + hk * D;
     const __bf16 *vg = static_cast<const __bf16 *>(a.v) + hk * D;
+    const int t_last = PAIR ? sb.t0 : sg.t0;  // the range after the first la own keys
     const __bf16 *k_tr = kg + (size_t)sg.p0 * rs, *k_own = kg + (size_t)sg.t0 * rs;
     const __bf16 *v_tr = vg + (size_t)sg.p0 * rs, *v_own = vg + (size_t)sg.t0 * rs;
-    // row of virtual key x (clamped into the tile's keys) in range tr / own
-    auto row = [&](const __bf16 *tr, const __bf16 *own, int x) {
+    const __bf16 *k_last = kg + (size_t)t_last * rs, *v_last = vg + (size_t)t_last * rs;
+    // row of virtual key x (clamped into the tile's keys)
+    auto row = [&](const __bf16 *tr, const __bf16 *own, const __bf16 *last, int x) {
         x = min(x, kv_len - 1);
-        return x < sg.plen ? tr + (uint32_t)x * rs : own + (uint32_t)(x - sg.plen) * rs;
+        if (x < sg.plen) return tr + (uint32_t)x * rs;
+        if (PAIR && x < sg.plen + la) return own + (uint32_t)(x - sg.plen) * rs;
+        return last + (uint32_t)(x - sg.plen - la) * rs;
     };
     bf16x8 kreg[KPASS];
     u32x4 vreg[VPASS][2];
@@ -192,15 +239,16 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int 
 #pragma unroll
         for (int p = 0; p < KPASS; ++p) {
             const int piece = p * kAThreads + tid, r = piece / CPR, c = piece % CPR;
-            kreg[p] = *reinterpret_cast<const bf16x8 *>(row(k_tr, k_own, j * BN + r) + c * 8);
+            kreg[p] =
+                *reinterpret_cast<const bf16x8 *>(row(k_tr, k_own, k_last, j * BN + r) + c * 8);
         }
 #pragma unroll
         for (int p = 0; p < VPASS; ++p) {
             const int c = tid / PPP, r = 2 * (p * PPP + tid % PPP);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                vreg[p][u] =
-                    *reinterpret_cast<const u32x4 *>(row(v_tr, v_own, j * BN + r + u) + c * 8);
+                vreg[p][u] = *reinterpret_cast<const u32x4 *>(
+                    row(v_tr, v_own, v_last, j * BN + r + u) + c * 8);
         }
     };
     auto store_block = [&](int buf) {
@@ -239,7 +287,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int 
     f32x4v acc[QR][NDT];
 #pragma unroll
     for (int qg = 0; qg < QR; ++qg) {
-        m[qg] = -INFINITY;
+        // finite: a pair's second branch over an empty trunk sees no key in
+        // its first blocks, and exp2(-inf - m) must then give 0, not NaN
+        m[qg] = -1e30f;
         lsum[qg] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[qg][dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
@@ -276,8 +326,11 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int 
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (j * BN + kt * 16 + g4 + i > qp[qg]) st[qg][kt][i] = -INFINITY;
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = j * BN + kt * 16 + g4 + i;
+                        if (key > qp[qg] || (key >= hlo[qg] && key < hhi[qg]))
+                            st[qg][kt][i] = -INFINITY;
+                    }
         }
         u32x4 ph[QR][2];
         bf16x8 pl[QR][2];
@@ -295,7 +348,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int 
             if (__builtin_amdgcn_ballot_w64(mloc > m[qg] + kLazy) != 0) {
                 mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
                 mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-                const float mn = fmaxf(m[qg], mloc);  // finite: key 0 is visible to every query
+                const float mn = fmaxf(m[qg], mloc);
                 const float alpha = __builtin_amdgcn_exp2f(m[qg] - mn);
                 m[qg] = mn;
                 lsum[qg] *= alpha;
@@ -352,8 +405,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, const Seg &sg, int 
         // the row sum of a query is split over its 4 lanes
         float ltot = lsum[qg] + __shfl_xor(lsum[qg], 16, kWave);
         ltot += __shfl_xor(ltot, 32, kWave);
-        if (qcol[qg] < L) {
-            TO *orow = o + ((size_t)(sg.t0 + q_first + qcol[qg]) * H + h) * D;
+        if (qok[qg]) {
+            TO *orow = o + ((size_t)qtok[qg] * H + h) * D;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -393,10 +446,12 @@ __global__ __launch_bounds__(kAThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     const Seg sg = segment(a, lo);
     const int ntile = ts[lo + 1] - ts[lo];
     const int tile = ntile - 1 - (t - ts[lo]);  // the longest tiles of a segment first
-    if (lo < a.n_branch)
-        attn_tile<D, TO, kQrBranch>(a, sg, h, tile, s_k, s_vt);
+    if (lo >= a.n_branch)
+        attn_tile<D, TO, kQrTrunk, false>(a, sg, sg, h, tile, s_k, s_vt);
+    else if (pair_first(a, lo))
+        attn_tile<D, TO, 2, true>(a, sg, segment(a, lo + 1), h, 0, s_k, s_vt);
     else
-        attn_tile<D, TO, kQrTrunk>(a, sg, h, tile, s_k, s_vt);
+        attn_tile<D, TO, kQrBranch, false>(a, sg, sg, h, tile, s_k, s_vt);
 }
 
 template <int D, typename TO>

@@ -77,6 +77,26 @@ def test_ragged_stream(d, Hkv):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("d,Hkv", [(128, 2), (64, 4)])
+def test_branch_pairs(d, Hkv):
+    """Consecutive branches 2i, 2i+1 of one request, each at most 64 tokens,
+    share a tile: pairs with a full / one-token / empty member, pairs over
+    an empty trunk (with a 64-token first member, the second member's whole
+    first key block is invisible to it),
+    a pair split because a member is longer than 64, an unpaired last
+    branch, and branches of different requests side by side."""
+    trunks = [0, 70, 130]
+    blen = [64, 1, 5, 64, 0, 33, 40, 0, 64, 65, 3, 9, 64, 10, 17]
+    par = [1, 1, 0, 0, 2, 2, 2, 2, 1, 1, 0, 2, 0, 0, 0]
+    t = gi.torch_attention_inputs(trunks, blen, par, H=4, Hkv=Hkv, d=d, seed=5 + d)
+    g = host64(run(t))
+    r = ref(t)
+    segs = segments(t["cu"].cpu(), t["bcu"].cpu())
+    e = worst_err(g, r, segs)
+    print(f"pairs d={d} Hkv={Hkv}: {e:.2e}", flush=True)
+    assert e <= TOL
+
+
 def test_bf16_output_is_a_rounding_of_the_exact_result():
     t = gi.torch_attention_inputs([130, 7], [64, 3], [0, 1], H=4, Hkv=2, d=128, seed=11)
     g = host64(run(t, o_dtype=torch.bfloat16))
