@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--no-fork", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="profiling aid: run only the fork-attention round (warmup + steps "
+                         "calls), report its time on stderr, print no JSON line")
     return ap.parse_args()
 
 
@@ -219,7 +222,7 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD public figure
 
 
-def bench_fork_attention(torch, gdn, gi, reps):
+def bench_fork_attention(torch, gdn, gi, reps, warmup=1, branches_only=True):
     """The softmax-attention half of the fork on the fork_prefill stream (8
     requests x 8192-token trunks, 20 branches of 64 tokens each, H=16, d=128,
     bf16): one gdn_fork_attention call over the whole stream (trunks and
@@ -236,12 +239,15 @@ def bench_fork_attention(torch, gdn, gi, reps):
     trunk_pairs = R * P * (P + 1) // 2
     branch_pairs = NB * (Lb * P + Lb * (Lb + 1) // 2)
     out = {}
-    for name, tq, pairs in (("round", True, trunk_pairs + branch_pairs),
-                            ("branches_only", False, branch_pairs)):
+    legs = [("round", True, trunk_pairs + branch_pairs)]
+    if branches_only:
+        legs.append(("branches_only", False, branch_pairs))
+    for name, tq, pairs in legs:
         def call():
             gdn.gdn_fork_attention(t["q"], t["k"], t["v"], t["cu"], o, t["bcu"], t["bpar"],
                                    trunk_queries=tq, workspace=ws)
-        call()
+        for _ in range(warmup):
+            call()
         ts = []
         for _ in range(reps):
             with Timer(torch, stream) as a:
@@ -480,6 +486,11 @@ def main():
         sys.exit(1)
     gdn.load()
     torch.manual_seed(0)
+    if args.only_attention:
+        res = bench_fork_attention(torch, gdn, gi, max(args.steps, 1), warmup=args.warmup,
+                                   branches_only=False)
+        log(json.dumps(res))
+        return
     B, H, M, NSTEP = 256, 32, 8, 512
     K, W = args.steps, args.warmup
     stream = torch.cuda.current_stream()

@@ -1,9 +1,13 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
     python -m linear_attention_recurrent_gdn_amd.profiling trace <kernel_trace.csv> <out.md> "<command>"
+    python -m linear_attention_recurrent_gdn_amd.profiling counters <out.md> "<command>" \
+        <kernel-substring> <pass_dir> [<pass_dir> ...] [--sources attention|decode|prefill]
     python -m linear_attention_recurrent_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
         <out.md> "<command>" <kernel-substring> [--grid N] [--copy-bytes B] [--sources decode|prefill]
 
+`counters` averages every counter of one or more --pmc passes per dispatch
+of the named kernel (e.g. SQ_* utilisation and LDS counters).
 `trace` keeps, per kernel and launch grid, the call count and the average /
 min / max duration (one kernel serves workloads of different sizes, told
 apart by their grids). `traffic` turns two --pmc passes (FETCH_SIZE, then
@@ -28,6 +32,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/gdn_device.hpp")
 PREFILL_SOURCES = ("csrc/prefill.hip", "csrc/gdn_device.hpp")
+ATTENTION_SOURCES = ("csrc/attention.hip", "csrc/attention_launch.hpp", "csrc/gdn_device.hpp")
+SOURCES = {"decode": DECODE_SOURCES, "prefill": PREFILL_SOURCES, "attention": ATTENTION_SOURCES}
 
 
 def source_hash(rel_paths) -> str:
@@ -128,6 +134,27 @@ def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_byte
     open(out_md, "w").write("\n".join(lines))
 
 
+def counters_summary(out_md, command, kernel_sub, pass_dirs, sources=ATTENTION_SOURCES):
+    vals, kname = {}, None
+    for d in pass_dirs:
+        for r in _counter_rows(d):
+            if kernel_sub not in r["Kernel_Name"]:
+                continue
+            kname = kname or r["Kernel_Name"]
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel_sub} in {pass_dirs}")
+    data = {c: statistics.mean(v) for c, v in sorted(vals.items())}
+    lines = [f"# Counters: {os.path.basename(out_md)[:-3]}", "",
+             "Command (one --pmc pass per counter group):", "", f"    {command}", "",
+             f"Kernel: `{_short(kname, 200)}` (mean per dispatch).", "",
+             "| counter | per dispatch |", "|---|---|"]
+    lines += [f"| {c} | {v:.4g} |" for c, v in data.items()]
+    block = dict(kernel=kname, counters=data, source_hash=source_hash(sources))
+    lines += ["", "```json", json.dumps(block, indent=1), "```", ""]
+    open(out_md, "w").write("\n".join(lines))
+
+
 def main(argv):
     import argparse
 
@@ -143,9 +170,17 @@ def main(argv):
     f.add_argument("--grid", type=int, default=None)
     f.add_argument("--copy-bytes", type=int, default=4 << 30)
     f.add_argument("--sources", choices=("decode", "prefill"), default="decode")
+    c = sub.add_parser("counters")
+    c.add_argument("out_md")
+    c.add_argument("command")
+    c.add_argument("kernel_sub")
+    c.add_argument("pass_dirs", nargs="+")
+    c.add_argument("--sources", choices=tuple(SOURCES), default="attention")
     a = ap.parse_args(argv)
     if a.mode == "trace":
         trace_summary(a.trace_csv, a.out_md, a.command)
+    elif a.mode == "counters":
+        counters_summary(a.out_md, a.command, a.kernel_sub, a.pass_dirs, SOURCES[a.sources])
     else:
         traffic_summary(a.fetch_dir, a.write_dir, a.out_md, a.command, a.kernel_sub,
                         copy_bytes=a.copy_bytes, grid=a.grid,
