@@ -15,7 +15,9 @@ import os
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgdn_mi355x.so")
+# GDN_LIB_OVERRIDE: load another build of the same library instead (the
+# sanitizer test loads one built with host-side ASan / UBSan)
+LIB_PATH = os.environ.get("GDN_LIB_OVERRIDE") or os.path.join(PKG, "libgdn_mi355x.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, -1, -2, -3, -4
 GDN_F32, GDN_BF16 = 0, 1
