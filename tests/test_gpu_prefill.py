@@ -342,3 +342,41 @@ def test_full_size_fork_prefill_sampled():
         assert max(e_o, e_s, e_ob, e_sb) <= TOL
         wb = win[r].cpu().view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(wb, gi.bf16_round(win_r[0].astype(np.float32))[0])
+
+
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+def test_batch_composition_invariance(variant):
+    """A request's outputs do not depend on what else shares the call: the
+    middle request of three, run alone (at another stream offset), gives the
+    same bits for its o, final state and window, and so do its branches
+    when the other requests' branches are dropped."""
+    prefix, branches, parent = [300, 130, 77], [9, 64, 40, 3], [1, 0, 1, 2]
+    full = gi.seq_inputs(prefix, branches, parent, 4, 128, 128, io="bf16", conv=True,
+                         per_key=variant != "gdn", seed=13)
+    g_full = run_fork(full, variant=variant)
+    # request 1 alone, with its own branches (0 and 2 of the full call)
+    Np = full.Np
+    rows_p = np.r_[300:430]
+    keep_b = [0, 2]
+    rows_b = np.concatenate([np.arange(full.branch_cu[b], full.branch_cu[b + 1]) + Np
+                             for b in keep_b])
+    rows = np.concatenate([rows_p, rows_b])
+    sub = gi.SeqInputs(**{**full.__dict__})
+    for n in ("q", "k", "v", "log_alpha", "beta"):
+        setattr(sub, n, getattr(full, n)[rows])
+    for n in ("q_bits", "k_bits", "v_bits"):
+        setattr(sub, n, getattr(full, n)[rows])
+    sub.Np, sub.Nb, sub.N = 130, len(rows_b), len(rows)
+    sub.cu_seqlens = np.array([0, 130], dtype=np.int32)
+    sub.branch_cu = np.array([0, branches[0], branches[0] + branches[2]], dtype=np.int32)
+    sub.branch_parent = np.array([0, 0], dtype=np.int32)
+    g_sub = run_fork(sub, variant=variant)
+    assert np.array_equal(g_sub["o_p"], g_full["o_p"][300:430])
+    assert np.array_equal(g_sub["st"][0], g_full["st"][1])
+    assert torch.equal(g_sub["win"][0], g_full["win"][1])
+    b0 = slice(int(full.branch_cu[0]), int(full.branch_cu[1]))
+    b2 = slice(int(full.branch_cu[2]), int(full.branch_cu[3]))
+    assert np.array_equal(g_sub["o_b"][:branches[0]], g_full["o_b"][b0])
+    assert np.array_equal(g_sub["o_b"][branches[0]:], g_full["o_b"][b2])
+    assert np.array_equal(g_sub["st_b"][0], g_full["st_b"][0])
+    assert np.array_equal(g_sub["st_b"][1], g_full["st_b"][2])
