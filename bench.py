@@ -472,9 +472,10 @@ def measured_traffic(ms_per_launch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); decode slot-heads "
-              "and fork requests shard across GPUs with no exchange, so a multi-GPU run is "
-              "not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this library "
+              "has no multi-GPU path. Decode slot-heads and fork requests would shard across "
+              "GPUs with no exchange, each GPU running the one-GPU kernels on its share.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 
