@@ -424,6 +424,37 @@ __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
+// Sum over each group of 4 lanes (DPP quad permutations: lane ^ 1, lane ^ 2).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+    return x;
+}
+
+// Rows R0 + 1 .. C - 1 of the column solve of T = (I + A)^-1 (see prep_body):
+// t[q] holds T[4q + part][col]; arow points at this lane's j = part (mod 4)
+// group of row 0 of A (rows of AP floats). Row r needs the terms j < r,
+// i.e. q < ceil(r / 4); A is zero on and above the diagonal, so the last
+// group needs no mask.
+template <int R0, int AP>
+__device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], int col, int part) {
+#pragma unroll
+    for (int r = R0 + 1; r < C; ++r) {
+        const int nq = (r + 3) / 4;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < (nq + 3) / 4; ++i) {
+            const float4 av = *reinterpret_cast<const float4 *>(arow + r * AP + 4 * i);
+            if (4 * i < nq) acc0 = fmaf(av.x, t[4 * i], acc0);
+            if (4 * i + 1 < nq) acc1 = fmaf(av.y, t[4 * i + 1], acc1);
+            if (4 * i + 2 < nq) acc0 = fmaf(av.z, t[4 * i + 2], acc0);
+            if (4 * i + 3 < nq) acc1 = fmaf(av.w, t[4 * i + 3], acc1);
+        }
+        const float acc = quad_sum(acc0 + acc1);
+        if (r > col && r % 4 == part) t[r / 4] = -acc;
+    }
+}
+
 // VAR: the decay / update rule. kScalar: log a [N, H], the gated delta rule.
 // kKda: per-key log a [N, H, d_k], delta rule. kRwkv6: per-key log a, raw
 // value update (u = v: no A, T' = I, no K Sig term, beta unused).
@@ -433,6 +464,22 @@ __device__ __forceinline__ float row_shr(float x) {
 //   U = T' (V - K^ Sig0),  O = Q^ Sig0 + P U,
 //   Sig_L = diag(e^{g_L}) Sig0 + sum_r (k_r . e^{g_L - g_r}) u_r^T,
 // which the scan runs with gamma = 1 and a per-key state decay.
+// Rows x C matrix staged in LDS (rows padded to C + 1 floats) -> hi / lo
+// bf16 planes [rows][C] of the record, 8 elements (16 bytes) per store.
+template <int ROWS>
+__device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 *lo) {
+    constexpr int G = C / 8;  // 8-element groups per row
+    for (int idx = threadIdx.x; idx < ROWS * G; idx += kThreads) {
+        const int r = idx / G, c0 = (idx % G) * 8;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = src[r * (C + 1) + c0 + e];
+        const Split8 sp = split8(x);
+        *reinterpret_cast<bf16x8 *>(hi + r * C + c0) = sp.hi;
+        *reinterpret_cast<bf16x8 *>(lo + r * C + c0) = sp.lo;
+    }
+}
+
 template <int DK, int DV, typename TI, int VAR>
 __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr bool kPerKey = VAR != kScalar;
@@ -443,7 +490,12 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
     constexpr int SK = SK0 > C * (C + 1) ? SK0 : C * (C + 1);
     __shared__ __attribute__((aligned(16))) float s_k[SK];
-    __shared__ __attribute__((aligned(16))) float s_A[C * (C + 1)];  // strictly lower A
+    // A, strictly lower, rows of AP floats with each row's entries grouped by
+    // j mod 4 (see a_idx), so the substitution reads them as float4
+    constexpr int AP = C + 4;
+    const auto a_idx = [](int r, int j) { return r * AP + (j % 4) * (C / 4) + j / 4; };
+    __shared__ __attribute__((aligned(16))) float s_A[C * AP];
+    __shared__ __attribute__((aligned(16))) float s_P[C * (C + 1)];  // P, staged for the record
     __shared__ __attribute__((aligned(16))) float s_wq[DK * 4], s_wk[DK * 4];
     __shared__ float s_gt[kPerKey ? kWaves * DK : 1];  // per-key: each wave's row-block sums
     __shared__ __attribute__((aligned(16))) float s_gl[kPerKey ? DK : 4];  // per-key: g_L
@@ -604,8 +656,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             // the decay between rows: a factor here (scalar), inside the
             // products already (per key)
             const float dec = (live && col <= r) ? (kPerKey ? 1.f : expf(g_r - g_c)) : 0.f;
-            s_A[r * (C + 1) + col] = (kDelta && col < r) ? b_r * dec * kk[i] : 0.f;
-            split1(dec * qk[i], rec[RL.phi + r * C + col], rec[RL.plo + r * C + col]);
+            s_A[a_idx(r, col)] = (kDelta && col < r) ? b_r * dec * kk[i] : 0.f;
+            s_P[r * (C + 1) + col] = dec * qk[i];
         }
     }
     __syncthreads();  // s_A complete; the K rows in s_k are no longer needed
@@ -620,28 +672,24 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
                 s_k[(ks * 32 + cq + e) * (C + 1) + row] = kPerKey ? kf[ks][e] : kf[ks][e] * f;
     }
     __syncthreads();
-    for (int idx = tid; idx < DK * C; idx += kThreads)
-        split1(s_k[(idx / C) * (C + 1) + idx % C], rec[RL.kthi + idx], rec[RL.ktlo + idx]);
+    put_planes<DK>(s_k, rec + RL.kthi, rec + RL.ktlo);
+    put_planes<C>(s_P, rec + RL.phi, rec + RL.plo);
 
     // T = (I + A)^-1, one column per group of 4 lanes (columns are
-    // independent): lane (col, part) keeps T[j][col] for j = part (mod 4).
+    // independent): lane (col, part) keeps T[j][col] for j = part (mod 4),
+    // starting from the identity column; rows r <= col leave the column
+    // unchanged, so a wave starts after its first column.
     {
         const int col = w * 16 + lane / 4, part = lane % 4;
         float t[C / 4];
 #pragma unroll
-        for (int q = 0; q < C / 4; ++q) t[q] = 0.f;
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int q = 0; q < C / 4; ++q) {
-                const int j = q * 4 + part;
-                if (j < r) acc = fmaf(s_A[r * (C + 1) + j], t[q], acc);
-            }
-            acc += __shfl_xor(acc, 1, kWave);
-            acc += __shfl_xor(acc, 2, kWave);
-            const float val = (r == col) ? 1.f : (r > col ? -acc : 0.f);
-            if (r % 4 == part) t[r / 4] = val;
+        for (int q = 0; q < C / 4; ++q) t[q] = (q * 4 + part == col) ? 1.f : 0.f;
+        const float *arow = s_A + part * (C / 4);
+        switch (__builtin_amdgcn_readfirstlane(w)) {  // straight-line rows per wave
+            case 0: tri_solve<0, AP>(arow, t, col, part); break;
+            case 1: tri_solve<16, AP>(arow, t, col, part); break;
+            case 2: tri_solve<32, AP>(arow, t, col, part); break;
+            default: tri_solve<48, AP>(arow, t, col, part); break;
         }
         __syncthreads();  // every lane is done with s_A and with the K~^T copy-out
         // T'[j][col] = T[j][col] beta_col, staged through LDS for coalesced stores
@@ -650,8 +698,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         for (int q = 0; q < C / 4; ++q) s_k[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
     }
     __syncthreads();
-    for (int idx = tid; idx < C * C; idx += kThreads)
-        split1(s_k[(idx / C) * (C + 1) + idx % C], rec[RL.thi + idx], rec[RL.tlo + idx]);
+    put_planes<C>(s_k, rec + RL.thi, rec + RL.tlo);
 }
 
 template <int DK, int DV, typename TI>
