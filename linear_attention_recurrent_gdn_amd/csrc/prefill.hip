@@ -495,8 +495,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr int AP = C + 4;
     const auto a_idx = [](int r, int j) { return r * AP + (j % 4) * (C / 4) + j / 4; };
     __shared__ __attribute__((aligned(16))) float s_A[C * AP];
-    __shared__ __attribute__((aligned(16))) float s_P[C * (C + 1)];  // P, staged for the record
-    __shared__ __attribute__((aligned(16))) float s_wq[DK * 4], s_wk[DK * 4];
+    // the q / k conv taps live in s_A's space until A is formed
+    static_assert(2 * DK * 4 <= C * AP, "taps fit the A buffer");
+    float *const s_wq = s_A, *const s_wk = s_A + DK * 4;
     __shared__ float s_gt[kPerKey ? kWaves * DK : 1];  // per-key: each wave's row-block sums
     __shared__ __attribute__((aligned(16))) float s_gl[kPerKey ? DK : 4];  // per-key: g_L
 
@@ -631,7 +632,10 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     }
     __syncthreads();
 
-    // KK^T and QK^T tiles (w, ct), ct <= w, on MFMA; A and P from them
+    // KK^T and QK^T tiles (w, ct), ct <= w, on MFMA; A to LDS, P kept in
+    // registers until s_k is free
+    float pv[C / RB][4];
+#pragma unroll
     for (int ct = 0; ct < C / RB; ++ct) {
         f32x4v kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
         if (ct <= w) {
@@ -657,7 +661,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             // products already (per key)
             const float dec = (live && col <= r) ? (kPerKey ? 1.f : expf(g_r - g_c)) : 0.f;
             s_A[a_idx(r, col)] = (kDelta && col < r) ? b_r * dec * kk[i] : 0.f;
-            s_P[r * (C + 1) + col] = dec * qk[i];
+            pv[ct][i] = dec * qk[i];
         }
     }
     __syncthreads();  // s_A complete; the K rows in s_k are no longer needed
@@ -673,7 +677,14 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     }
     __syncthreads();
     put_planes<DK>(s_k, rec + RL.kthi, rec + RL.ktlo);
-    put_planes<C>(s_P, rec + RL.phi, rec + RL.plo);
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < C / RB; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s_k[(w * RB + (lane / 16) * 4 + i) * (C + 1) + ct * RB + lane % 16] = pv[ct][i];
+    __syncthreads();
+    put_planes<C>(s_k, rec + RL.phi, rec + RL.plo);
 
     // T = (I + A)^-1, one column per group of 4 lanes (columns are
     // independent): lane (col, part) keeps T[j][col] for j = part (mod 4),
@@ -691,7 +702,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             case 2: tri_solve<32, AP>(arow, t, col, part); break;
             default: tri_solve<48, AP>(arow, t, col, part); break;
         }
-        __syncthreads();  // every lane is done with s_A and with the K~^T copy-out
+        __syncthreads();  // every lane is done with s_A and with the P copy-out
         // T'[j][col] = T[j][col] beta_col, staged through LDS for coalesced stores
         const float bcol = __shfl(b_l, col, kWave);
 #pragma unroll
@@ -702,7 +713,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 }
 
 template <int DK, int DV, typename TI>
-__global__ __launch_bounds__(kThreads) void prep_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void prep_kernel(PrefillArgs a) {
     prep_body<DK, DV, TI, kScalar>(a);
 }
 
