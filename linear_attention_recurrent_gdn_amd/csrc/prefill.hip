@@ -127,6 +127,8 @@ __device__ __forceinline__ void load8(const bf16 *p, float (&x)[8]) {
 //   T'  [C][C], P [C][C]              row-major (A operands)
 //   K, Q [C][d_k]                     the conv'd, normalised chunk rows (A operands)
 //   K~^T [d_k][C]                     exp(g_L - g_r) k_r, transposed (B operand)
+//   fp32 slot of max(d_k, C) floats   scalar decay: gamma_r = exp(g_r) per row;
+//                                     per key: exp(g_L) per key column
 struct RecLayout {
     size_t thi, tlo, phi, plo, khi, klo, qhi, qlo, kthi, ktlo, egl, elems;
 };
@@ -143,7 +145,7 @@ __host__ __device__ constexpr RecLayout rec_layout(int dk) {
                      4 * (size_t)C * C + 4 * (size_t)C * dk,
                      4 * (size_t)C * C + 5 * (size_t)C * dk,
                      4 * (size_t)C * C + 6 * (size_t)C * dk,
-                     4 * (size_t)C * C + 6 * (size_t)C * dk + 2 * (size_t)dk};
+                     4 * (size_t)C * C + 6 * (size_t)C * dk + 2 * (size_t)(dk > C ? dk : C)};
 }
 
 struct WsLayout {
@@ -536,6 +538,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     if constexpr (!kPerKey) {
         g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
         gL = __shfl(g, C - 1, kWave);
+        if (w == 0) reinterpret_cast<float *>(rec + RL.egl)[lane] = expf(g);  // gamma_r for the scan
     } else {
         // log a of this lane's row (rows >= L add nothing), then an inclusive
         // scan over the wave's 16 rows (DPP within 16-lane rows) plus the
@@ -757,7 +760,8 @@ template <int KS, int NVT, typename TI>
 struct ChunkRegs {
     Split8 ka[KS], qa[KS], ta[2], pa[2];
     TI vraw[NVT][7];  // raw V rows r0-3 .. r0+3 of this lane's columns
-    float la;         // scalar decay: log a of row `lane` (clamped)
+    float4 gam;       // scalar decay: gamma of this lane's 4 rows (C/D layout)
+    float gaml;       // scalar decay: gamma_L
 };
 
 // PK: per-key decay (K and Q arrive pre-scaled, gamma = 1; the state decays
@@ -916,9 +920,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         if constexpr (PK) {
-            r.la = 0.f;
+            r.gam = make_float4(1.f, 1.f, 1.f, 1.f);
+            r.gaml = 1.f;
         } else {
-            r.la = a.log_alpha[(size_t)(sp.start + p0 + min(lane, L - 1)) * H + h];
+            const float *gr = reinterpret_cast<const float *>(rec + RL.egl);
+            r.gam = *reinterpret_cast<const float4 *>(gr + r0v);
+            r.gaml = gr[C - 1];
         }
     };
     // K~^T hi / lo planes of chunk c into LDS (direct-to-LDS, 16 B per lane;
@@ -949,17 +956,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const ChunkRegs<KS, NVT, TI> cur = nxt;
         load_kt(c);
 
-        // g (running log a over the chunk rows; rows >= L add nothing)
-        float g = lane < cs.L ? cur.la : 0.f;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float o = __shfl_up(g, off, kWave);
-            if (lane >= off) g += o;
-        }
-        const float gL = __shfl(g, C - 1, kWave);
-        float gam[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gam[i] = PK ? 1.f : expf(__shfl(g, r0v + i, kWave));
+        // gamma_r = exp(g_r) of this lane's rows, from the chunk record (the
+        // prep kernel's running sums; rows >= L add nothing)
+        const float gam[4] = {cur.gam.x, cur.gam.y, cur.gam.z, cur.gam.w};
 
         // conv'd V entries of this lane (C/D layout), from the raw rows
         float vf[NVT][4];
@@ -1060,7 +1059,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
 
         // Sig^T <- gamma_L Sig^T + U^T K~   (tiles: value sub-tile x 16 keys)
-        const float gamL = expf(gL);
+        const float gamL = cur.gaml;
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
             const int ft = w + m * kWaves;
