@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--only-attention", action="store_true",
                     help="profiling aid: run only the fork-attention round (warmup + steps "
                          "calls), report its time on stderr, print no JSON line")
+    ap.add_argument("--only-fork", action="store_true",
+                    help="profiling aid: run only the two-call fork (fork-reps timed rounds) "
+                         "and the device-copy probe, report on stderr, print no JSON line")
     return ap.parse_args()
 
 
@@ -487,6 +490,11 @@ def main():
         sys.exit(1)
     gdn.load()
     torch.manual_seed(0)
+    if args.only_fork:
+        res = bench_fork(torch, gdn, gi, args.fork_reps)
+        res["hbm_probe"] = hbm_probe(torch, torch.cuda.current_stream())
+        log(json.dumps(res))
+        return
     if args.only_attention:
         res = bench_fork_attention(torch, gdn, gi, max(args.steps, 1), warmup=args.warmup,
                                    branches_only=False)
