@@ -124,11 +124,21 @@ __device__ __forceinline__ void load8(const bf16 *p, float (&x)[8]) {
 // ------------------------------------------------------------ workspace
 // Per (chunk, head) record of bf16 hi / lo planes, split once by the prep
 // kernel for the scan:
-//   T'  [C][C], P [C][C]              row-major (A operands)
-//   K, Q [C][d_k]                     the conv'd, normalised chunk rows (A operands)
+//   T'  [C][C], P [C][C]              A operands, in fragment order (frag_off)
+//   K, Q [C][d_k]                     the conv'd, normalised chunk rows (A
+//                                     operands, fragment order)
 //   K~^T [d_k][C]                     exp(g_L - g_r) k_r, transposed (B operand)
 //   fp32 slot of max(d_k, C) floats   scalar decay: gamma_r = exp(g_r) per row;
 //                                     per key: exp(g_L) per key column
+// A-operand planes are stored in the order the 16x16x32 MFMA reads them:
+// the 16-row x 32-column block (w, ks) of a plane is 1 KiB contiguous, lane
+// l's 8 values (row w*16 + l%16, columns ks*32 + (l/16)*8 ..) at element
+// frag_off(nks, w, ks, l), nks = columns / 32. A wave's operand load then
+// covers 8 whole 128-byte lines instead of 16 half lines.
+__host__ __device__ constexpr int frag_off(int nks, int w, int ks, int lane) {
+    return ((w * nks + ks) * kWave + lane) * 8;
+}
+
 struct RecLayout {
     size_t thi, tlo, phi, plo, khi, klo, qhi, qlo, kthi, ktlo, egl, elems;
 };
@@ -467,8 +477,9 @@ __device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], 
 //   Sig_L = diag(e^{g_L}) Sig0 + sum_r (k_r . e^{g_L - g_r}) u_r^T,
 // which the scan runs with gamma = 1 and a per-key state decay.
 // Rows x C matrix staged in LDS (rows padded to C + 1 floats) -> hi / lo
-// bf16 planes [rows][C] of the record, 8 elements (16 bytes) per store.
-template <int ROWS>
+// bf16 planes of the record, 8 elements (16 bytes) per store: row-major
+// [rows][C], or in A-fragment order (FRAG, rows = C).
+template <int ROWS, bool FRAG = false>
 __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 *lo) {
     constexpr int G = C / 8;  // 8-element groups per row
     for (int idx = threadIdx.x; idx < ROWS * G; idx += kThreads) {
@@ -477,8 +488,10 @@ __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = src[r * (C + 1) + c0 + e];
         const Split8 sp = split8(x);
-        *reinterpret_cast<bf16x8 *>(hi + r * C + c0) = sp.hi;
-        *reinterpret_cast<bf16x8 *>(lo + r * C + c0) = sp.lo;
+        const int off = FRAG ? frag_off(C / 32, r / 16, c0 / 32, r % 16 + 16 * ((c0 % 32) / 8))
+                             : r * C + c0;
+        *reinterpret_cast<bf16x8 *>(hi + off) = sp.hi;
+        *reinterpret_cast<bf16x8 *>(lo + off) = sp.lo;
     }
 }
 
@@ -601,7 +614,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qf[ks][e] *= expf(gr[ks][e]);  // Q^
             qa[ks] = split8(qf[ks]);
-            const size_t off = (size_t)row * DK + ks * 32 + cq;
+            const int off = frag_off(KS, w, ks, lane);
             *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
             *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = qa[ks].lo;
         }
@@ -627,7 +640,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             }
         }
         ka[ks] = split8(ak);
-        const size_t off = (size_t)row * DK + ks * 32 + cq;
+        const int off = frag_off(KS, w, ks, lane);
         *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
         *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
 #pragma unroll
@@ -687,7 +700,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         for (int i = 0; i < 4; ++i)
             s_k[(w * RB + (lane / 16) * 4 + i) * (C + 1) + ct * RB + lane % 16] = pv[ct][i];
     __syncthreads();
-    put_planes<C>(s_k, rec + RL.phi, rec + RL.plo);
+    put_planes<C, true>(s_k, rec + RL.phi, rec + RL.plo);
 
     // T = (I + A)^-1, one column per group of 4 lanes (columns are
     // independent): lane (col, part) keeps T[j][col] for j = part (mod 4),
@@ -712,7 +725,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         for (int q = 0; q < C / 4; ++q) s_k[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
     }
     __syncthreads();
-    put_planes<C>(s_k, rec + RL.thi, rec + RL.tlo);
+    put_planes<C, true>(s_k, rec + RL.thi, rec + RL.tlo);
 }
 
 template <int DK, int DV, typename TI>
@@ -896,14 +909,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int p0 = c * C, L = min(C, sp.len - p0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const size_t off = (size_t)arow * DK + ks * 32 + acol;
+            const int off = frag_off(KS, w, ks, lane);
             r.ka[ks] = read_split8(rec + RL.khi + off, rec + RL.klo + off);
             if (want_o) r.qa[ks] = read_split8(rec + RL.qhi + off, rec + RL.qlo + off);
         }
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq)
             if (kq <= kmax) {
-                const int off = arow * C + kq * 32 + acol;
+                const int off = frag_off(C / 32, w, kq, lane);
                 r.ta[kq] = read_split8(rec + RL.thi + off, rec + RL.tlo + off);
                 if (want_o) r.pa[kq] = read_split8(rec + RL.phi + off, rec + RL.plo + off);
             }
