@@ -92,6 +92,15 @@ __device__ __forceinline__ Split8 read_split8(const __bf16 *hi, const __bf16 *lo
     return s;
 }
 
+// 4 consecutive values -> hi / lo bf16 (one 8-byte store each; 8-byte aligned)
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void split4_store(f32x4v x, __bf16 *hi, __bf16 *lo) {
+    const bf16x4 h = __builtin_convertvector(x, bf16x4);
+    const bf16x4 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4v), bf16x4);
+    *reinterpret_cast<bf16x4 *>(hi) = h;
+    *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+
 __device__ __forceinline__ void split1(float x, __bf16 &hi, __bf16 &lo) {
     hi = (__bf16)x;
     lo = (__bf16)(x - (float)hi);
@@ -1012,11 +1021,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 acc = mma3(cur.ka[ks], bs, acc);
                 if (want_o) acc_o[t] = mma3(cur.qa[ks], bs, acc_o[t]);
             }
+            // the lane's 4 rows are consecutive in the R^T planes
+            f32x4v rv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = t * 16 + lane % 16, r = r0v + i;
-                split1(vf[t][i] - gam[i] * acc[i], s_Rh[col * CB + r], s_Rl[col * CB + r]);
-            }
+            for (int i = 0; i < 4; ++i) rv[i] = vf[t][i] - gam[i] * acc[i];
+            const int ro = (t * 16 + lane % 16) * CB + r0v;
+            split4_store(rv, s_Rh + ro, s_Rl + ro);
         }
         __syncthreads();
 
@@ -1030,11 +1040,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
                     acc = mma3(cur.ta[kq], read_split8(s_Rh + off, s_Rl + off), acc);
                 }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = t * 16 + lane % 16, r = r0v + i;
-                split1(acc[i], s_Uh[col * CB + r], s_Ul[col * CB + r]);
-            }
+            const int uo = (t * 16 + lane % 16) * CB + r0v;
+            split4_store(acc, s_Uh + uo, s_Ul + uo);
         }
         __syncthreads();
 
