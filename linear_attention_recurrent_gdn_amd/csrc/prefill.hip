@@ -309,28 +309,30 @@ __device__ __forceinline__ uint32_t ror16(uint32_t x) {
 // window). The three earlier taps of a row then come from the lanes 1-3 rows
 // up through DPP row rotations, which match the 16-row layout exactly.
 template <int D, typename TI>
-__device__ void rows_afrag(const TI *x, int H, int h, const ChunkSrc<TI> &cs, int rb, int CC,
-                           int cwin, const float *s_w, bool norm, float (&out)[D / 32][8]) {
+struct RawRows {
+    Raw8<TI> own[D / 32], halo[D / 32];
+};
+
+// rows_load issues the loads (two parts' loads can then be in flight
+// together): every load is unconditional from a clamped, in-bounds address
+// (validity is applied in rows_compute) and nothing is consumed here.
+template <int D, typename TI>
+__device__ __forceinline__ void rows_load(const TI *x, int H, int h, const ChunkSrc<TI> &cs,
+                                          int rb, int CC, int cwin, bool conv,
+                                          RawRows<D, TI> &rr) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x % kWave;
     const int i = lane % 16;
     const int cq = (lane / 16) * 8;
     const int row = rb * RB + i;
-    const bool live = row < cs.L;
-    // Every load is unconditional from a clamped, in-bounds address (validity
-    // is applied afterwards) and all of them are issued before any use, so
-    // they travel as one batch.
     const TI *own_p = x + (size_t)(cs.seq0 + cs.p0 + min(row, cs.L - 1)) * H * D + (size_t)h * D;
-    Raw8<TI> own[KS], halo[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw_load(own_p + ks * 32 + cq, own[ks]);
-    const bool conv = s_w != nullptr;
+    for (int ks = 0; ks < KS; ++ks) raw_load(own_p + ks * 32 + cq, rr.own[ks]);
     if (conv) {
         // halo rows (lanes 13..15): stream position ph, or window row 3 + ph.
         // A block with no live row may put ph past the sequence: clamp it (a
         // block with a live row has its halo inside the sequence).
         const int ph = cs.p0 + rb * RB + i - RB;
-        const bool hvalid = i >= RB - 3 && (ph >= 0 || cs.win != nullptr);
         const TI *hp = own_p;
         if (i >= RB - 3) {
             if (ph >= 0)
@@ -339,7 +341,26 @@ __device__ void rows_afrag(const TI *x, int H, int h, const ChunkSrc<TI> &cs, in
                 hp = cs.win + (size_t)(3 + max(ph, -3)) * CC + cwin;
         }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) raw_load(hp + ks * 32 + cq, halo[ks]);
+        for (int ks = 0; ks < KS; ++ks) raw_load(hp + ks * 32 + cq, rr.halo[ks]);
+    }
+}
+
+template <int D, typename TI>
+__device__ __forceinline__ void rows_compute(RawRows<D, TI> &rr, const ChunkSrc<TI> &cs, int rb,
+                                             const float *s_w, bool norm,
+                                             float (&out)[D / 32][8]) {
+    constexpr int KS = D / 32;
+    const int lane = threadIdx.x % kWave;
+    const int i = lane % 16;
+    const int cq = (lane / 16) * 8;
+    const int row = rb * RB + i;
+    const bool live = row < cs.L;
+    const bool conv = s_w != nullptr;
+    Raw8<TI>(&own)[KS] = rr.own;
+    Raw8<TI>(&halo)[KS] = rr.halo;
+    if (conv) {
+        const int ph = cs.p0 + rb * RB + i - RB;
+        const bool hvalid = i >= RB - 3 && (ph >= 0 || cs.win != nullptr);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -611,12 +632,21 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     if constexpr (kDelta) b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
     b_l = lane < cs.L ? b_l : 0.f;
 
-    // conv'd, normalised Q and K rows; their split A operands go to the record
+    // conv'd, normalised Q and K rows; their split A operands go to the
+    // record. With a scalar decay the raw Q and K rows are requested
+    // together (the per-key form has no registers to spare for that).
     Split8 qa[DK / 32], ka[DK / 32];
+    RawRows<DK, TI> rk;
+    const auto load_k = [&] {
+        rows_load<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK + h * DK, conv,
+                          rk);
+    };
     {
+        RawRows<DK, TI> rq;
+        rows_load<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, h * DK, conv, rq);
+        if constexpr (!kPerKey) load_k();
         float qf[DK / 32][8];
-        rows_afrag<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, h * DK,
-                           conv ? s_wq : nullptr, a.qk_norm != 0, qf);
+        rows_compute<DK, TI>(rq, cs, w, conv ? s_wq : nullptr, a.qk_norm != 0, qf);
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks) {
             if constexpr (kPerKey)
@@ -628,9 +658,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = qa[ks].lo;
         }
     }
+    if constexpr (kPerKey) load_k();
     float kf[DK / 32][8];
-    rows_afrag<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK + h * DK,
-                       conv ? s_wk : nullptr, a.qk_norm != 0, kf);
+    rows_compute<DK, TI>(rk, cs, w, conv ? s_wk : nullptr, a.qk_norm != 0, kf);
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
         // A operand of KK^T and the scan's K Sig term: K (scalar decay), K^
@@ -840,12 +870,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     const bool conv = a.conv_w != nullptr;
     if (conv) stage_taps(a.conv_w, 2 * H * DK + h * DV + j0, TV, s_wv);
-    for (int idx = tid; idx < DK * TV; idx += kThreads) {
-        const int d = idx / TV, j = idx % TV;
-        s_St[j * SP + d] =
-            a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + j] : 0.f;
-    }
-    __syncthreads();
 
     const bool want_o = a.o != nullptr;
     const int kmax = (w * RB + RB - 1) / 32;  // T', P lower triangular: k-steps to use
@@ -969,8 +993,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if (w == 0 && lane < DK / 4) lds_dma16(rec + RL.egl + lane * 8, s_eg);
     };
 
+    // the first chunk's operands are requested before the incoming state
+    // tile, so the two round trips overlap (a one-chunk branch pays one)
     ChunkRegs<KS, NVT, TI> nxt;
     if (nchunks > 0) load_regs(0, nxt);
+    for (int idx = tid; idx < DK * TV; idx += kThreads) {
+        const int d = idx / TV, j = idx % TV;
+        s_St[j * SP + d] =
+            a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + j] : 0.f;
+    }
+    __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
         if constexpr (CK)
             if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
