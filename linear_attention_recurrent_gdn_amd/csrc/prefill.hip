@@ -801,6 +801,15 @@ __device__ __forceinline__ int kt_swz(int r, int ch) { return r * C + ((ch ^ (r 
 // go in here (no arithmetic on the results), so the loads can stay in
 // flight until the step consumes them.
 
+// Two adjacent outputs (pair-aligned) in one store.
+__device__ __forceinline__ void store_pair(float *p, float x, float y) {
+    *reinterpret_cast<float2 *>(p) = make_float2(x, y);
+}
+__device__ __forceinline__ void store_pair(bf16 *p, float x, float y) {
+    *reinterpret_cast<uint32_t *>(p) =
+        (uint32_t)from_f32<bf16>(x).bits | ((uint32_t)from_f32<bf16>(y).bits << 16);
+}
+
 // 16-byte direct-to-LDS load (lane l lands at lds + 8 l elements). Kept out
 // of the kernel templates: with the builtin inside a template the host pass
 // drops the kernel's launch stub without a diagnostic.
@@ -808,10 +817,30 @@ __device__ __forceinline__ void lds_dma16(const __bf16 *g, __bf16 *lds) {
     __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
+// Two adjacent io-dtype values in one load: the value columns 2n, 2n + 1 of
+// a lane (see vcol).
+template <typename TI> struct VPair;
+template <> struct VPair<bf16> {
+    typedef uint32_t type;
+    static __device__ __forceinline__ float get(type x, int t) {
+        return __uint_as_float(t == 0 ? x << 16 : x & 0xffff0000u);
+    }
+};
+template <> struct VPair<float> {
+    typedef float2 type;
+    static __device__ __forceinline__ float get(type x, int t) { return t == 0 ? x.x : x.y; }
+};
+
+// Value columns of a scan tile: internal column c (sub-tile t = c / 16,
+// MFMA column n = c % 16) is the tile's column 2n + t, so the two columns a
+// lane holds are adjacent in memory (one load / store per row for both).
+__device__ __forceinline__ int vcol(int c) { return 2 * (c % 16) + c / 16; }
+
 template <int KS, int NVT, typename TI>
 struct ChunkRegs {
+    static_assert(NVT == 2, "a lane holds one adjacent pair of value columns");
     Split8 ka[KS], qa[KS], ta[2], pa[2];
-    TI vraw[NVT][7];  // raw V rows r0-3 .. r0+3 of this lane's columns
+    typename VPair<TI>::type vraw[7];  // raw V rows r0-3 .. r0+3 of this lane's column pair
     float4 gam;       // scalar decay: gamma of this lane's 4 rows (C/D layout)
     float gaml;       // scalar decay: gamma_L
 };
@@ -888,8 +917,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // that closes the previous state update)
     auto put_state = [&](float *dst) {
         for (int idx = tid; idx < DK * TV; idx += kThreads) {
-            const int d = idx / TV, j = idx % TV;
-            dst[(size_t)d * DV + j0 + j] = s_St[j * SP + d];
+            const int d = idx / TV, c = idx % TV;
+            dst[(size_t)d * DV + j0 + vcol(c)] = s_St[c * SP + d];
         }
     };
     // conv window after position `end` of the sequence: its last 3 raw
@@ -953,16 +982,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 r.ta[kq] = read_split8(rec + RL.thi + off, rec + RL.tlo + off);
                 if (want_o) r.pa[kq] = read_split8(rec + RL.phi + off, rec + RL.plo + off);
             }
-#pragma unroll
-        for (int t = 0; t < NVT; ++t) {
-            const int j = j0 + t * 16 + lane % 16;
+        {
+            const int j = j0 + 2 * (lane % 16);  // columns j, j + 1 (even: pair-aligned)
 #pragma unroll
             for (int q = 0; q < 7; ++q) {
                 const int p = p0 + r0v - 3 + q;  // >= -3
                 const TI *ptr = (p < 0 && win) ? win + (size_t)(3 + p) * CC + cwin_v + j
                                                : vs + (size_t)(sp.start + min(max(p, 0), p0 + L - 1)) *
                                                           H * DV + (size_t)h * DV + j;
-                r.vraw[t][q] = *ptr;
+                r.vraw[q] = *reinterpret_cast<const typename VPair<TI>::type *>(ptr);
             }
         }
         if constexpr (PK) {
@@ -998,9 +1026,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     ChunkRegs<KS, NVT, TI> nxt;
     if (nchunks > 0) load_regs(0, nxt);
     for (int idx = tid; idx < DK * TV; idx += kThreads) {
-        const int d = idx / TV, j = idx % TV;
-        s_St[j * SP + d] =
-            a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + j] : 0.f;
+        const int d = idx / TV, c = idx % TV;
+        s_St[c * SP + d] =
+            a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + vcol(c)] : 0.f;
     }
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
@@ -1018,13 +1046,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         float vf[NVT][4];
 #pragma unroll
         for (int t = 0; t < NVT; ++t) {
-            const int jt = t * 16 + lane % 16;
+            const int jt = vcol(t * 16 + lane % 16);  // the tile column, for its taps
             float xr[7];
 #pragma unroll
             for (int q = 0; q < 7; ++q) {
                 const int row = r0v - 3 + q, p = cs.p0 + row;
                 const bool ok = (conv || q >= 3) && ((row < cs.L && p >= 0) || (p < 0 && win));
-                xr[q] = ok ? to_f32(cur.vraw[t][q]) : 0.f;
+                xr[q] = ok ? VPair<TI>::get(cur.vraw[q], t) : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1100,14 +1128,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (c + 1 < nchunks) load_regs(c + 1, nxt);  // prefetch the next step
         if (want_o) {
 #pragma unroll
-            for (int t = 0; t < NVT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = r0v + i;
-                    if (r < cs.L)
-                        static_cast<TO *>(a.o)[((size_t)(cs.seq0 + cs.p0 + r) * H + h) * DV + j0 +
-                                               t * 16 + lane % 16] = from_f32<TO>(acc_o[t][i]);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0v + i;
+                if (r < cs.L)
+                    store_pair(static_cast<TO *>(a.o) + ((size_t)(cs.seq0 + cs.p0 + r) * H + h) * DV +
+                                   j0 + 2 * (lane % 16),
+                               acc_o[0][i], acc_o[1][i]);
+            }
         }
 
         // Sig^T <- gamma_L Sig^T + U^T K~   (tiles: value sub-tile x 16 keys)
