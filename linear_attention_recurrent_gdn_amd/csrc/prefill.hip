@@ -683,7 +683,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
         *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_k[row * KP + ks * 32 + cq + e] = bk[e];
+        for (int e = 0; e < 8; e += 4)  // 16-byte LDS stores (KP, cq keep them aligned)
+            *reinterpret_cast<float4 *>(s_k + row * KP + ks * 32 + cq + e) =
+                make_float4(bk[e], bk[e + 1], bk[e + 2], bk[e + 3]);
     }
     __syncthreads();
 
