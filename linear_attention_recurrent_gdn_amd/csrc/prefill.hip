@@ -1090,6 +1090,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const int ro = (t * 16 + lane % 16) * CB + r0v;
             split4_store(rv, s_Rh + ro, s_Rl + ro);
         }
+        // This wave's direct-to-LDS copies of K~^T are its only vector memory
+        // operations in flight here: finish them before this barrier (a
+        // workgroup fence would wait for them here anyway), so the whole
+        // plane is visible to every wave after it and the state update needs
+        // no barrier of its own. Sig^T is last read above (K Sig0, Q Sig0),
+        // so it may be rewritten by the state update after the next barrier.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
 
         // U = T' R
@@ -1121,11 +1128,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     }
             }
         }
-        // This wave's direct-to-LDS copies of K~^T are the only memory
-        // operations in flight here; finish them before the barrier so the
-        // whole plane is visible to every wave after it.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();  // K~^T complete; Sig^T fully read before it is rewritten
 
         if (c + 1 < nchunks) load_regs(c + 1, nxt);  // prefetch the next step
         if (want_o) {
