@@ -508,12 +508,15 @@ __device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], 
 // which the scan runs with gamma = 1 and a per-key state decay.
 // Rows x C matrix staged in LDS (rows padded to C + 1 floats) -> hi / lo
 // bf16 planes of the record, 8 elements (16 bytes) per store: row-major
-// [rows][C], or in A-fragment order (FRAG, rows = C).
+// [rows][C], or in A-fragment order (FRAG: a lower-triangular C x C matrix,
+// T' or P, whose 16 x 32 blocks above the diagonal are all zero; the scan
+// never reads them, so they are not written).
 template <int ROWS, bool FRAG = false>
 __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 *lo) {
     constexpr int G = C / 8;  // 8-element groups per row
     for (int idx = threadIdx.x; idx < ROWS * G; idx += kThreads) {
         const int r = idx / G, c0 = (idx % G) * 8;
+        if (FRAG && c0 / 32 > (r / 16 * 16 + 15) / 32) continue;
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = src[r * (C + 1) + c0 + e];
