@@ -536,7 +536,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr int KP = DK + 4;  // padded row of the staged K rows
     // staged K rows [C][KP]; then K~^T [DK][C + 1]; then T' [C][C + 1]
     constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
-    constexpr int SK = SK0 > C * (C + 1) ? SK0 : C * (C + 1);
+    constexpr int SK = SK0 > 2 * C * (C + 1) ? SK0 : 2 * C * (C + 1);
     __shared__ __attribute__((aligned(16))) float s_k[SK];
     // A, strictly lower, rows of AP floats with each row's entries grouped by
     // j mod 4 (see a_idx), so the substitution reads them as float4
@@ -737,24 +737,17 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     }
     __syncthreads();
     put_planes<DK>(s_k, rec + RL.kthi, rec + RL.ktlo);
-    __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < C / RB; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s_k[(w * RB + (lane / 16) * 4 + i) * (C + 1) + ct * RB + lane % 16] = pv[ct][i];
-    __syncthreads();
-    put_planes<C, true>(s_k, rec + RL.phi, rec + RL.plo);
 
     // T = (I + A)^-1, one column per group of 4 lanes (columns are
     // independent): lane (col, part) keeps T[j][col] for j = part (mod 4),
     // starting from the identity column; rows r <= col leave the column
-    // unchanged, so a wave starts after its first column.
-    {
-        const int col = w * 16 + lane / 4, part = lane % 4;
-        float t[C / 4];
+    // unchanged, so a wave starts after its first column. It runs while the
+    // K~^T stores drain (it reads only s_A).
+    const int col = w * 16 + lane / 4, part = lane % 4;
+    float t[C / 4];
 #pragma unroll
-        for (int q = 0; q < C / 4; ++q) t[q] = (q * 4 + part == col) ? 1.f : 0.f;
+    for (int q = 0; q < C / 4; ++q) t[q] = (q * 4 + part == col) ? 1.f : 0.f;
+    {
         const float *arow = s_A + part * (C / 4);
         switch (__builtin_amdgcn_readfirstlane(w)) {  // straight-line rows per wave
             case 0: tri_solve<0, AP>(arow, t, col, part); break;
@@ -762,14 +755,23 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             case 2: tri_solve<32, AP>(arow, t, col, part); break;
             default: tri_solve<48, AP>(arow, t, col, part); break;
         }
-        __syncthreads();  // every lane is done with s_A and with the P copy-out
-        // T'[j][col] = T[j][col] beta_col, staged through LDS for coalesced stores
-        const float bcol = __shfl(b_l, col, kWave);
-#pragma unroll
-        for (int q = 0; q < C / 4; ++q) s_k[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
     }
+    __syncthreads();  // every lane is done with the K~^T copy-out from s_k
+    // P (from registers) and T'[j][col] = T[j][col] beta_col, staged side by
+    // side in s_k for coalesced stores
+    float *const s_P = s_k, *const s_T = s_k + C * (C + 1);
+    static_assert(2 * C * (C + 1) <= SK, "P and T' staging fit s_k");
+#pragma unroll
+    for (int ct = 0; ct < C / RB; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s_P[(w * RB + (lane / 16) * 4 + i) * (C + 1) + ct * RB + lane % 16] = pv[ct][i];
+    const float bcol = __shfl(b_l, col, kWave);
+#pragma unroll
+    for (int q = 0; q < C / 4; ++q) s_T[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
     __syncthreads();
-    put_planes<C, true>(s_k, rec + RL.thi, rec + RL.tlo);
+    put_planes<C, true>(s_P, rec + RL.phi, rec + RL.plo);
+    put_planes<C, true>(s_T, rec + RL.thi, rec + RL.tlo);
 }
 
 template <int DK, int DV, typename TI>
@@ -907,7 +909,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     const bool want_o = a.o != nullptr;
     const int kmax = (w * RB + RB - 1) / 32;  // T', P lower triangular: k-steps to use
-    const int arow = w * RB + lane % 16;       // this lane's row in the A layout
     const int acol = (lane / 16) * 8;
     const int r0v = w * RB + (lane / 16) * 4;  // first of this lane's rows in the C/D layout
     // read once: inside the loop the compiler could not prove these unchanged
