@@ -534,7 +534,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr bool kDelta = VAR != kRwkv6;
     constexpr int KS = DK / 32;
     constexpr int KP = DK + 4;  // padded row of the staged K rows
-    // staged K rows [C][KP]; then K~^T [DK][C + 1]; then T' [C][C + 1]
+    // staged K rows [C][KP]; then K~^T [DK][C + 1]; then P and T' [C][C + 1]
+    // side by side
     constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
     constexpr int SK = SK0 > 2 * C * (C + 1) ? SK0 : 2 * C * (C + 1);
     __shared__ __attribute__((aligned(16))) float s_k[SK];
@@ -1118,7 +1119,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         __syncthreads();
 
-        // O = diag(gamma) Q Sig0 + P U (stored after the next barrier)
+        // O = diag(gamma) Q Sig0 + P U (stored below, after the next chunk's
+        // operands are requested)
         if (want_o) {
 #pragma unroll
             for (int t = 0; t < NVT; ++t) {

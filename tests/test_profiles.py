@@ -60,3 +60,26 @@ def test_deferred_writes_at_least_3x_less_than_eager():
 def test_workload_shapes_match_the_profiled_command():
     w = gi.WORKLOADS["decode_large"]
     assert (w["B"], w["H"], w["d"], w["M"]) == (256, 32, bench.D, 8)
+
+
+def test_prep_traffic_matches_algorithmic_bytes():
+    """The scalar prep kernel on the fork_prefill prefix: q and k rows (bf16),
+    log a and beta read once; the chunk record written once (its all-zero
+    T' / P blocks above the diagonal are not written). Reads run above the
+    algorithmic count by the conv halo rows (3 extra rows per 16-row block),
+    so the band is on the total."""
+    prof = profiling.read_profile_block(os.path.join(ROOT, "profiles",
+                                                     "fork_prefill_prep_traffic.md"))
+    assert prof is not None, "profiles/fork_prefill_prep_traffic.md missing"
+    if prof["source_hash"] != profiling.source_hash(profiling.PREFILL_SOURCES):
+        pytest.skip("profiles/fork_prefill_prep_traffic.md was taken from other prefill sources")
+    w = gi.WORKLOADS["fork_prefill"]
+    d, C, H = w["d"], w["chunk"], w["H"]
+    chunk_heads = w["R"] * (w["prefix"] // C) * H
+    reads = C * d * 2 * 2 + C * 4 * 2                       # q, k rows; log a, beta
+    record = (4 * C * C + 6 * C * d) * 2 + 4 * max(d, C)     # bf16 planes + fp32 slot
+    zero_blocks = 2 * 2 * 2 * 16 * 32 * 2                    # T', P: hi / lo, 2 blocks each
+    alg = chunk_heads * (reads + record - zero_blocks)
+    ratio = prof["traffic_bytes"] / alg
+    assert 0.98 <= ratio <= 1.10, ratio
+    assert abs(prof["write_bytes"] / (chunk_heads * (record - zero_blocks)) - 1) < 0.02
