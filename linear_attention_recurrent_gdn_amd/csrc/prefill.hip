@@ -466,6 +466,12 @@ __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
+// e^x for the per-key decay factors of a chunk (|x| is at most the chunk's
+// summed log decay): the hardware base-2 exponential of x log2(e), about
+// 1e-6 relative here, in place of the library expf's longer range reduction
+// (128 of these per lane per chunk).
+__device__ __forceinline__ float exp_pk(float x) { return __expf(x); }
+
 // Sum over each group of 4 lanes (DPP quad permutations: lane ^ 1, lane ^ 2).
 __device__ __forceinline__ float quad_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
@@ -655,7 +661,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         for (int ks = 0; ks < DK / 32; ++ks) {
             if constexpr (kPerKey)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qf[ks][e] *= expf(gr[ks][e]);  // Q^
+                for (int e = 0; e < 8; ++e) qf[ks][e] *= exp_pk(gr[ks][e]);  // Q^
             qa[ks] = split8(qf[ks]);
             const int off = frag_off(KS, w, ks, lane);
             *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
@@ -675,9 +681,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             if constexpr (kPerKey) {
-                ak[e] = kDelta ? kf[ks][e] * expf(gr[ks][e]) : 0.f;
-                bk[e] = kf[ks][e] * expf(-gr[ks][e]);  // B operand rows: K-
-                kf[ks][e] *= expf(glv[e] - gr[ks][e]);
+                ak[e] = kDelta ? kf[ks][e] * exp_pk(gr[ks][e]) : 0.f;
+                bk[e] = kf[ks][e] * exp_pk(-gr[ks][e]);  // B operand rows: K-
+                kf[ks][e] *= exp_pk(glv[e] - gr[ks][e]);
             } else {
                 ak[e] = bk[e] = kf[ks][e];
             }
