@@ -159,11 +159,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // 32-bit element offsets from the uniform tile base keep the addresses
     // of the 16 loads and stores in single VGPRs (scalar base + vector offset)
     const auto tile_off = [&](int p) { return (uint32_t)((r0 + p * Map::RPP) * DV + col); };
-    // The waves of a workgroup issue all of its loads at raised priority
-    // (back to normal before the first use), so a newly started workgroup
-    // gets its requests out ahead of the arithmetic of the others on the CU
-    // (measured 105 -> 102 us per deferred step on 256 x 32 slot-heads).
-    __builtin_amdgcn_s_setprio(1);
+    // The waves of a deferred-step workgroup issue all of its loads at
+    // raised priority (back to normal before the first use), so a newly
+    // started workgroup gets its requests out ahead of the arithmetic of the
+    // others on the CU (measured 105 -> 102 us per deferred step on 256 x 32
+    // slot-heads). The eager step, a copy-like stream with a store for every
+    // load, measured slower with it (192 -> 203 us) and runs without.
+    if constexpr (MODE != kEager) __builtin_amdgcn_s_setprio(1);
     float4 reg[Map::P];
 #pragma unroll
     for (int p = 0; p < Map::P; ++p)
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             ul[r] = logu[e * DV + j];
         }
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (MODE != kEager) __builtin_amdgcn_s_setprio(0);
     if (m == 0) lam_prev = 0.f;
     const float kx = to_f32(k_raw), qx = to_f32(q_raw), vx = to_f32(v_raw);
 
