@@ -409,49 +409,6 @@ __device__ __forceinline__ void rows_compute(RawRows<D, TI> &rr, const ChunkSrc<
     }
 }
 
-// Conv'd value entries of one 16-row block in the C/D layout of a 16x16 MFMA:
-// lane l holds rows rb*16 + (l/16)*4 + i (i < 4) of columns j0 + t*16 + l%16
-// for the value tiles t < TV/16. s_w: taps [TV][4] of the tile's v channels
-// in LDS (null: no convolution); cwin: first v channel of head h.
-template <int DV, typename TI>
-__device__ void rows_dfrag_v(const TI *v, int H, int h, const ChunkSrc<TI> &cs, int rb, int j0,
-                             int CC, int cwin, const float *s_w, float (&out)[TV / 16][4]) {
-    const int lane = threadIdx.x % kWave;
-    const int r0 = rb * RB + (lane / 16) * 4;
-#pragma unroll
-    for (int t = 0; t < TV / 16; ++t) {
-        const int jt = t * 16 + lane % 16;  // column inside the tile
-        const int j = j0 + jt;
-        float xr[7];                         // raw rows r0 - 3 .. r0 + 3
-#pragma unroll
-        for (int q = 0; q < 7; ++q) {
-            const int row = r0 - 3 + q;
-            const int p = cs.p0 + row;          // >= -3
-            const bool inseq = row < cs.L && p >= 0;
-            const bool inwin = p < 0 && cs.win != nullptr;
-            const bool need = s_w != nullptr || q >= 3;
-            // unconditional load from a clamped in-bounds address
-            const TI *ptr = inwin ? cs.win + (size_t)(3 + p) * CC + cwin + j
-                                  : v + (size_t)(cs.seq0 + min(max(p, 0), cs.p0 + cs.L - 1)) * H * DV +
-                                        (size_t)h * DV + j;
-            const float xv = to_f32(*ptr);
-            xr[q] = (need && (inseq || inwin)) ? xv : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float y;
-            if (s_w) {
-                y = 0.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) y = fmaf(s_w[jt * 4 + r], xr[i + r], y);
-            } else {
-                y = xr[i + 3];
-            }
-            out[t][i] = r0 + i < cs.L ? y : 0.f;
-        }
-    }
-}
-
 // Stage the conv taps of `n` channels starting at channel c0 into LDS [n][4].
 __device__ __forceinline__ void stage_taps(const float *conv_w, int c0, int n, float *s_w) {
     for (int idx = threadIdx.x; idx < n; idx += kThreads)
