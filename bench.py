@@ -376,8 +376,11 @@ def bench_decode_small(torch, gdn, gi, reps=5):
 
 # ---------------------------------------------------------------- HBM probe
 def hbm_probe(torch, stream, nbytes=4 << 30, reps=5):
-    """Attainable HBM bandwidth on this GPU: a plain device copy (read +
-    write nbytes each) and a read-only sum over nbytes, best of reps."""
+    """Reference rates of two library kernels on this GPU: torch's device
+    copy (read + write nbytes each) and torch's sum over nbytes, best of
+    reps. They are what those library kernels reach, not the attainable HBM
+    bandwidth (the deferred decode kernel streams faster than both); the
+    copy also calibrates the FETCH_SIZE / WRITE_SIZE counters."""
     n = nbytes // 4
     a = torch.rand(n, device="cuda")
     b = torch.empty_like(a)
@@ -392,7 +395,8 @@ def hbm_probe(torch, stream, nbytes=4 << 30, reps=5):
             a.sum()
         read.append(nbytes / (t.ms / 1e3) / 1e9)
     del a, b
-    return dict(copy_gbps=max(copy), read_gbps=max(read), bytes=nbytes)
+    return dict(torch_copy_gbps=max(copy), torch_sum_read_gbps=max(read), bytes=nbytes,
+                note="library kernels (torch copy_ / sum), not an attainable-bandwidth bound")
 
 
 # ---------------------------------------------------------------- CPU oracle
