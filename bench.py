@@ -375,6 +375,27 @@ def bench_decode_small(torch, gdn, gi, reps=5):
 
 
 # ---------------------------------------------------------------- HBM probe
+def stream_probe(torch, gdn, stream, nbytes=4 << 30, reps=5):
+    """Attainable HBM rate measured with the library's streaming probe
+    (gdn_stream_probe: the decode step's access form, non-temporal 16-byte
+    loads / stores over a 4 GiB buffer, far beyond the caches): read-only and
+    copy (read + write bytes both counted), best of reps."""
+    a = torch.rand(nbytes // 4, device="cuda")
+    b = torch.empty_like(a)
+    gdn.gdn_stream_probe(a, b, copy=False)
+    gdn.gdn_stream_probe(a, b, copy=True)
+    read, copy = [], []
+    for _ in range(reps):
+        with Timer(torch, stream) as t:
+            gdn.gdn_stream_probe(a, b, copy=False)
+        read.append(nbytes / (t.ms / 1e3) / 1e9)
+        with Timer(torch, stream) as t:
+            gdn.gdn_stream_probe(a, b, copy=True)
+        copy.append(2 * nbytes / (t.ms / 1e3) / 1e9)
+    del a, b
+    return dict(read_gbps=max(read), copy_gbps=max(copy), bytes=nbytes)
+
+
 def hbm_probe(torch, stream, nbytes=4 << 30, reps=5):
     """Reference rates of two library kernels on this GPU: torch's device
     copy (read + write nbytes each) and torch's sum over nbytes, best of
@@ -554,6 +575,7 @@ def main():
     small = bench_decode_small(torch, gdn, gi)
 
     probe = hbm_probe(torch, stream)
+    probe["stream"] = stream_probe(torch, gdn, stream)
 
     cpu = None
     if not args.no_cpu:
@@ -593,6 +615,11 @@ def main():
             "traffic_gbps": traffic_gbps,
             "bytes_per_launch": alg_bytes / K,
             "launch_ms": ms_step,
+            # attainable rates measured in this run with the library's
+            # streaming probe (same access form, 4 GiB buffer)
+            "measured_read_gbps": probe["stream"]["read_gbps"],
+            "measured_copy_gbps": probe["stream"]["copy_gbps"],
+            "frac_of_measured_read": achieved / probe["stream"]["read_gbps"],
         },
         "eager": {"value": eager_value, "unit": "head-steps/s", "ms_per_step": te.ms / K,
                   "hbm_gbps_effective": eager_gbps,

@@ -322,6 +322,23 @@ int gdn_fork_attention(const void *q, const void *k, const void *v,
                        int o_dtype, void *workspace, size_t ws_bytes,
                        void *stream);
 
+/*
+ * gdn_stream_probe -- a measurement aid, not part of the recurrence: streams
+ * a device buffer with the access form the decode step uses for its state
+ * (non-temporal 16-byte loads, and stores in copy mode), so the attainable
+ * HBM rate is measured beside the kernels' own rates.
+ *  src      n_bytes of device memory, read once
+ *  dst      mode 0 (read): at least 4 bytes, normally left untouched (the
+ *           loaded data is folded into a value that is stored only when it
+ *           equals one NaN bit pattern); mode 1 (copy): n_bytes, receives a
+ *           copy of src (the two buffers must not overlap)
+ *  n_bytes  a multiple of 16 (0: nothing is enqueued, and src / dst may be
+ *           NULL)
+ * Errors: INVALID_ARG (NULL pointer with n_bytes > 0, n_bytes not a multiple
+ * of 16, mode not 0 or 1), HIP.
+ */
+int gdn_stream_probe(const void *src, void *dst, size_t n_bytes, int mode, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     gdn_fork_branches,
     gdn_prefill_checkpointed,
     gdn_prefill_shared,
+    gdn_stream_probe,
     load,
     prefill_workspace_bytes,
     status_string,
@@ -35,6 +36,7 @@ __all__ = [
     "gdn_fork_attention",
     "fork_attention_workspace_bytes",
     "prefill_workspace_bytes",
+    "gdn_stream_probe",
     "status_string",
     "load",
     "GDNError",

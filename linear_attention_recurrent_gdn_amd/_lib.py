@@ -45,6 +45,7 @@ SIGNATURES = {
     "gdn_fork_attention_workspace_bytes": (_S, [_I, _I]),
     "gdn_fork_attention": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float,
                                 _I, _P, _I, _I, _P, _S, _P]),
+    "gdn_stream_probe": (_I, [_P, _P, _S, _I, _P]),
 }
 
 
@@ -321,3 +322,16 @@ def gdn_fork_attention(q, k, v, cu_seqlens, o, branch_cu=None, branch_parent=Non
         sc, int(bool(trunk_queries)), _dev(o, "o", _IO, (N, H, d)), _io_code(q), _io_code(o),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check("gdn_fork_attention", st)
+
+
+def gdn_stream_probe(src, dst, copy=False, stream=None):
+    """Measurement aid: stream src (a contiguous device tensor, size a
+    multiple of 16 bytes) with non-temporal 16-byte loads; copy=True also
+    writes it to dst (same size), else dst (>= 4 bytes) is normally left
+    untouched."""
+    nbytes = src.numel() * src.element_size()
+    if copy and dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    st = load().gdn_stream_probe(_dev(src, "src"), _dev(dst, "dst"), nbytes, 1 if copy else 0,
+                                 _stream(stream))
+    _check("gdn_stream_probe", st)

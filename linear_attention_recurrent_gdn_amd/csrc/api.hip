@@ -280,4 +280,12 @@ int gdn_fork_attention(const void *q, const void *k, const void *v, const int32_
     return from_hip(gdn::launch_attention(d, o_dtype, a, static_cast<hipStream_t>(stream)));
 }
 
+int gdn_stream_probe(const void *src, void *dst, size_t n_bytes, int mode, void *stream) {
+    if ((mode != 0 && mode != 1) || n_bytes % 16 != 0) return GDN_ERR_INVALID_ARG;
+    if (n_bytes == 0) return GDN_OK;
+    if (!src || !dst) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_stream_probe(src, dst, n_bytes, mode,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

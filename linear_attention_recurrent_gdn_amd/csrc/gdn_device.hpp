@@ -115,4 +115,8 @@ size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,
 hipError_t launch_prefill(int dk, int dv, int io, int out, const PrefillArgs &a,
                           hipStream_t stream);
 
+// Streaming read (copy = 0) or copy (copy = 1) of n_bytes (a multiple of 16).
+hipError_t launch_stream_probe(const void *src, void *dst, size_t n_bytes, int copy,
+                               hipStream_t stream);
+
 }  // namespace gdn

@@ -160,3 +160,11 @@ def test_fork_attention_validation_and_workspace(lib):
                                   0.1, 1, FAKE, 1, 0, FAKE, need, NULL) == UNSUPPORTED
     assert call(ws=NULL) == WORKSPACE
     assert call(ws_bytes=need - 1) == WORKSPACE
+
+
+def test_stream_probe_validation(lib):
+    assert lib.gdn_stream_probe(NULL, FAKE, 1024, 0, NULL) == INVALID
+    assert lib.gdn_stream_probe(FAKE, NULL, 1024, 1, NULL) == INVALID
+    assert lib.gdn_stream_probe(FAKE, FAKE, 1000, 0, NULL) == INVALID   # not a multiple of 16
+    assert lib.gdn_stream_probe(FAKE, FAKE, 1024, 2, NULL) == INVALID   # mode 0 or 1
+    assert lib.gdn_stream_probe(NULL, NULL, 0, 1, NULL) == OK              # nothing to stream
