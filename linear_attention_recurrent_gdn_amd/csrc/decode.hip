@@ -239,10 +239,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const int idx = tid + r * kThreads, e = idx / DK, i = idx % DK;
             float pc = 0.f, pd = 0.f;
             if (e < m) {
-                // per-key: fold the decay ratio into k~ here; scalar: it
+                // per-key: fold the decay ratio into k~ here (the hardware
+                // base-2 exponential: the argument is <= 0 and at most the
+                // log's summed decay, about 1e-6 relative); scalar: it
                 // factors out of the sums and is applied per entry
                 const float kl = to_f32(kl_raw[r]);
-                const float kt = kPerKey ? kl * expf(s_lam[i] - ll[r]) : kl;
+                const float kt = kPerKey ? kl * __expf(s_lam[i] - ll[r]) : kl;
                 pc = kt * s_k[i];
                 pd = kt * s_q[i];
                 if (merge) s_ktg[e * DK + rg(i)] = kt;
