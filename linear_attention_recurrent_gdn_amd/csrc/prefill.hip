@@ -423,10 +423,10 @@ __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
-// e^x for the per-key decay factors of a chunk (|x| is at most the chunk's
+// e^x for the decay factors inside a chunk (|x| is at most the chunk's
 // summed log decay): the hardware base-2 exponential of x log2(e), about
 // 1e-6 relative here, in place of the library expf's longer range reduction
-// (128 of these per lane per chunk).
+// (per key 128 of these per lane per chunk, 16 with a scalar decay).
 __device__ __forceinline__ float exp_pk(float x) { return __expf(x); }
 
 // Sum over each group of 4 lanes (DPP quad permutations: lane ^ 1, lane ^ 2).
@@ -683,7 +683,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             const bool live = r < cs.L && col < cs.L;
             // the decay between rows: a factor here (scalar), inside the
             // products already (per key)
-            const float dec = (live && col <= r) ? (kPerKey ? 1.f : expf(g_r - g_c)) : 0.f;
+            const float dec = (live && col <= r) ? (kPerKey ? 1.f : exp_pk(g_r - g_c)) : 0.f;
             s_A[a_idx(r, col)] = (kDelta && col < r) ? b_r * dec * kk[i] : 0.f;
             pv[ct][i] = dec * qk[i];
         }
