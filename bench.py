@@ -190,29 +190,42 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
                                t["beta"][:Np], t["cu_seqlens"], st, o=o_p, conv_w=t["conv_w"],
                                qk_l2norm=True, final_window=win, workspace=ws, variant=variant)
 
-    def fork():
+    # call 2 as timed: o of every branch token. A caller that goes on
+    # decoding from the branches also wants each branch's final state and
+    # conv window; that variant is timed alongside.
+    b_st = torch.empty((NB, H, d, d), device=dev)
+    b_win = torch.empty((NB, 3, cc), device=dev, dtype=torch.bfloat16)
+
+    def fork(states=False):
         gdn.gdn_fork_branches(t["q"][Np:], t["k"][Np:], t["v"][Np:], t["log_alpha"][Np:],
                               t["beta"][Np:], t["branch_cu"], t["branch_parent"], st, o_b,
-                              parent_window=win, conv_w=t["conv_w"], qk_l2norm=True,
-                              workspace=ws, variant=variant)
+                              parent_window=win, branch_state=b_st if states else None,
+                              branch_window=b_win if states else None, conv_w=t["conv_w"],
+                              qk_l2norm=True, workspace=ws, variant=variant)
 
     prefill()
     fork()
-    tp, tf = [], []
+    fork(states=True)
+    tp, tf, tfs = [], [], []
     for _ in range(reps):
         with Timer(torch, stream) as a:
             prefill()
         with Timer(torch, stream) as b:
             fork()
+        with Timer(torch, stream) as c:
+            fork(states=True)
         tp.append(a.ms)
         tf.append(b.ms)
-    tp_ms, tf_ms = float(np.median(tp)), float(np.median(tf))
+        tfs.append(c.ms)
+    tp_ms, tf_ms, tfs_ms = float(np.median(tp)), float(np.median(tf)), float(np.median(tfs))
     # dense-tile work of the chunked form per token-head (d_k = d_v = d,
     # chunk C): 5Cd + 3d^2 + C^2/6 multiply-adds; split-bf16 issues 3x
     C = w["chunk"]
     mac = 5 * C * d + 3 * d * d + C * C / 6
     pre_tflops = Np * H * 2 * mac / (tp_ms / 1e3) / 1e12
     return dict(branches=NB, prefill_ms=tp_ms, fork_ms=tf_ms,
+                fork_with_states_ms=tfs_ms,
+                branches_per_s_with_states=NB / ((tp_ms + tfs_ms) / 1e3),
                 prefill_dense_tile_tflops=pre_tflops,
                 prefill_mfma_issued_tflops=3 * pre_tflops,
                 prefill_mfma_frac_of_bf16_peak=3 * pre_tflops / BF16_MFMA_PEAK_TFLOPS,

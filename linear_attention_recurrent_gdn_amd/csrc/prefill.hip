@@ -885,10 +885,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // the state tile [DK][TV] of this workgroup (Sig^T in s_St) into a
     // [DK][DV] state at dst; valid at a chunk boundary (after the barrier
     // that closes the previous state update)
+    // (4 consecutive tile columns per 16-byte store; tile column j is
+    // internal column (j % 2) * 16 + j / 2, the inverse of vcol)
     auto put_state = [&](float *dst) {
-        for (int idx = tid; idx < DK * TV; idx += kThreads) {
-            const int d = idx / TV, c = idx % TV;
-            dst[(size_t)d * DV + j0 + vcol(c)] = s_St[c * SP + d];
+        for (int idx = tid; idx < DK * TV / 4; idx += kThreads) {
+            const int d = idx / (TV / 4), j = 4 * (idx % (TV / 4));
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = s_St[((j + e) % 2 * 16 + (j + e) / 2) * SP + d];
+            *reinterpret_cast<float4 *>(dst + (size_t)d * DV + j0 + j) =
+                make_float4(x[0], x[1], x[2], x[3]);
         }
     };
     // conv window after position `end` of the sequence: its last 3 raw
