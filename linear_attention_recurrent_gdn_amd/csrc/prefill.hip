@@ -101,11 +101,6 @@ __device__ __forceinline__ void split4_store(f32x4v x, __bf16 *hi, __bf16 *lo) {
     *reinterpret_cast<bf16x4 *>(lo) = l;
 }
 
-__device__ __forceinline__ void split1(float x, __bf16 &hi, __bf16 &lo) {
-    hi = (__bf16)x;
-    lo = (__bf16)(x - (float)hi);
-}
-
 __device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
     const float4 b = *reinterpret_cast<const float4 *>(p + 4);
@@ -113,21 +108,12 @@ __device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-// 8 consecutive io-dtype values as fp32 (16-byte aligned)
+// 8 consecutive fp32 values (16-byte aligned)
 __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
     const float4 b = *reinterpret_cast<const float4 *>(p + 4);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void load8(const bf16 *p, float (&x)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
 }
 
 // ------------------------------------------------------------ workspace
