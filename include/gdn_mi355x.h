@@ -34,7 +34,8 @@
  *    GDN_KDA (a decay per key, delta rule), GDN_RWKV6 (a decay per key,
  *    raw-value update u_t = v_t, beta unused and may be NULL) -- [DL]
  *    operator list.
- *  - d_k, d_v must each be 32, 64 or 128.
+ *  - d_k and d_v are each 32, 64 or 128, in any combination (d_k != d_v is
+ *    allowed; any other width returns GDN_ERR_UNSUPPORTED).
  *  - Return value: GDN_OK or a negative status (below). Host-checkable
  *    arguments are validated before any HIP call; a failing call enqueues
  *    nothing. Device-side preconditions (offsets non-decreasing, parents
@@ -54,8 +55,10 @@ extern "C" {
 
 enum gdn_status {
     GDN_OK = 0,
-    GDN_ERR_INVALID_ARG = -1, /* NULL required pointer, negative size, bad enum */
-    GDN_ERR_UNSUPPORTED = -2, /* head size or chunk size not built */
+    GDN_ERR_INVALID_ARG = -1, /* NULL required pointer, negative size, bad enum,
+                                 chunk not 16, 32 or 64 */
+    GDN_ERR_UNSUPPORTED = -2, /* head width not 32/64/128, chunk 16 or 32 (not
+                                 built), Mcap above the on-chip capacity */
     GDN_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
     GDN_ERR_HIP = -4          /* a HIP launch failed: see gdn_last_hip_error() */
 };
@@ -119,11 +122,16 @@ size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k,
  *  final_window [n_seq, 3, CC]       io_dtype or NULL: the last 3 raw
  *                                    inputs (from init_window when the
  *                                    sequence is shorter than 3)
- *  chunk        64
+ *  chunk        the chunk length of the chunked form: the interface takes
+ *               16, 32 or 64 (the result does not depend on it beyond
+ *               rounding); this build computes chunk = 64 only, so 16 and
+ *               32 return GDN_ERR_UNSUPPORTED and any other value
+ *               GDN_ERR_INVALID_ARG
  *  variant      GDN_SCALAR, GDN_KDA or GDN_RWKV6
  *  workspace    >= gdn_prefill_workspace_bytes(n_tokens, n_seq, ...) bytes
  * Errors: INVALID_ARG (NULL required pointer, n_seq < 0, n_tokens < 0,
- * H < 1, bad dtype or variant), UNSUPPORTED (d_k/d_v, chunk), WORKSPACE.
+ * H < 1, bad dtype or variant, chunk not 16/32/64), UNSUPPORTED (d_k or
+ * d_v not 32/64/128, chunk 16 or 32), WORKSPACE, HIP.
  */
 int gdn_prefill_shared(const void *q, const void *k, const void *v,
                        const float *log_alpha, const float *beta,

@@ -38,7 +38,7 @@ int check_decode_common(const void *q, const void *k, const void *v, const float
     if (B < 0 || H < 1 || n_slots < 0) return GDN_ERR_INVALID_ARG;
     if ((long long)B * H > INT_MAX) return GDN_ERR_INVALID_ARG;
     if (!slot_idx && B > n_slots) return GDN_ERR_INVALID_ARG;
-    if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || d_k != d_v) return GDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
@@ -125,7 +125,7 @@ int deltalog_merge(float *base, const float *log_u, const void *log_k, const flo
     if (B < 0 || H < 1 || n_slots < 0 || Mcap < 1) return GDN_ERR_INVALID_ARG;
     if ((long long)B * H > INT_MAX) return GDN_ERR_INVALID_ARG;
     if (!slot_idx && B > n_slots) return GDN_ERR_INVALID_ARG;
-    if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || d_k != d_v) return GDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return GDN_ERR_UNSUPPORTED;
     if (Mcap > kMaxLog) return GDN_ERR_UNSUPPORTED;
     gdn::DecodeArgs a{};
     a.state = base;
@@ -161,7 +161,8 @@ static int prefill_common(const void *q, const void *k, const void *v, const flo
         return GDN_ERR_INVALID_ARG;
     if (variant != GDN_RWKV6 && !beta) return GDN_ERR_INVALID_ARG;
     if (n_seq < 0 || n_tokens < 0 || H < 1 || n_parent < 0) return GDN_ERR_INVALID_ARG;
-    if (!head_dim_ok(d_k) || !head_dim_ok(d_v) || d_k != d_v) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_INVALID_ARG;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return GDN_ERR_UNSUPPORTED;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     const size_t need = gdn::prefill_workspace_bytes(n_tokens, n_seq, H, d_k, d_v, chunk);
     if (need > 0 && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
@@ -187,6 +188,7 @@ static int prefill_common(const void *q, const void *k, const void *v, const flo
     a.H = H;
     a.qk_norm = qk_l2norm ? 1 : 0;
     a.chunk = chunk;
+    a.dv = d_v;
     a.variant = variant;
     a.ckpt_every = ckpt_every;
     a.ckpt_cap = ckpt_cap;

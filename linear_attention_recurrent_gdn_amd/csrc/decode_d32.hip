@@ -1,0 +1,13 @@
+// decode_d32.hip -- the decode-step kernel instances with d_k = 32 (every
+// d_v, variant, io and output type), one translation unit per key width.
+
+#include "decode_kernels.hpp"
+
+namespace gdn {
+
+hipError_t launch_decode_dk32(int mode, int dv, int variant, int io, int out,
+                               const DecodeArgs &a, hipStream_t stream) {
+    return dispatch_dv<32>(mode, dv, variant, io, out, a, stream);
+}
+
+}  // namespace gdn

@@ -102,6 +102,7 @@ struct PrefillArgs {
     void *ws;
     size_t ws_bytes;
     int n_seq, n_parent, n_tokens, H, qk_norm, chunk;
+    int dv;                 // value width (the key width is a template parameter)
     int variant;            // Variant: scalar log a [N, H], or per-key [N, H, dk]
     // checkpoints: state / window after every ckpt_every chunks, at most
     // ckpt_cap per sequence ([n_seq, ckpt_cap, H, dk, dv] / [n_seq, ckpt_cap, 3, CC])

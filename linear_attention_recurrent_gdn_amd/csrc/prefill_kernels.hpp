@@ -1,0 +1,1206 @@
+// prefill_kernels.hpp -- chunked prefill of the GDN recurrence over a flat token
+// stream, used by both calls of the two-call fork: the shared contexts
+// (call 1) and the branches, each started from its own request's saved
+// state and conv window (call 2).
+//
+// Sources: "같은 맥락에서 여러 판단을 빠르게 처리하는 Flide" (yozm.zip summary)
+// -- section "연구방법을 단계별로", step 1 (tokens of all requests packed in
+// one flat stream, membership as GPU metadata), step 2 (call 1 stores the
+// final recurrent state and conv window, call 2 runs every question from
+// its own request's saved state); glossary "Gated DeltaNet" (fixed-size
+// matrix state). The pages do not describe a prefill algorithm: the chunked
+// form below is derived from the recurrence (gated delta rule, Yang et al.,
+// ICLR 2025) and checked against the fp64 step-by-step oracle.
+//
+// Chunked form. In a chunk of L <= C tokens with incoming stored state
+// Sig0 (= S0^T, [d_k][d_v]), g_r = running sum of log a inside the chunk,
+// gamma_r = exp(g_r):
+//   A[r][s] = beta_r exp(g_r - g_s) <k_r, k_s>            (s < r)
+//   T' = (I + A)^-1 diag(beta)
+//   P[r][s] = exp(g_r - g_s) <q_r, k_s>                    (s <= r)
+//   U = T' (V - diag(gamma) K Sig0)       the chunk's rank-1 factors u_r
+//   O = diag(gamma) Q Sig0 + P U          o_r = S_r q_r
+//   Sig_L = gamma_L Sig0 + sum_r exp(g_L - g_r) k_r u_r^T
+// Column j of U, O, Sig depends only on column j of V and Sig0, so value
+// tiles are independent.
+//
+// Every contraction runs on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16)
+// with split-bf16 operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi),
+// and a.b ~ hi.hi + hi.lo + lo.hi accumulated in fp32 -- about 2^-16
+// relative per product, where a single bf16 product (2^-9) would not meet a
+// 2e-3 end-to-end tolerance.
+//
+// Kernels:
+//   plan  -- one workgroup: per-sequence chunk offsets (prefix sum of
+//            ceil(len/C)) into the workspace, from the device offsets.
+//   prep  -- one workgroup per (chunk, head), all chunks in parallel: conv
+//            + q/k norm of the chunk rows, KK^T and QK^T on MFMA, then
+//            T = (I + A)^-1 by per-column forward substitution; writes T'
+//            and P to the workspace.
+//   scan  -- one workgroup per (sequence, head, 32-wide value tile): walks
+//            the sequence's chunks in order. Each of its 4 waves owns 16
+//            chunk rows: it forms the conv'd, normalised K and Q rows
+//            directly in MFMA operand registers, and the state tile Sig^T
+//            [32][d_k] stays in LDS across chunks.
+
+#pragma once
+
+#include <type_traits>
+
+#include "gdn_device.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int C = 64;        // chunk length
+constexpr int TV = 32;       // value-tile width of the scan
+constexpr int RB = 16;       // chunk rows per wave
+constexpr float kNormEps = 1e-6f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ split-bf16 MFMA
+struct Split8 {
+    bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ Split8 split8(const float (&x)[8]) {
+    Split8 s;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)x[e];
+        s.hi[e] = h;
+        s.lo[e] = (__bf16)(x[e] - (float)h);
+    }
+    return s;
+}
+
+// c += a . b for 16x16 tiles with K = 32, fp32-faithful via three products
+__device__ __forceinline__ f32x4v mma3(const Split8 &a, const Split8 &b, f32x4v c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
+    return c;
+}
+
+// 8 consecutive bf16 of a hi plane and the matching lo plane (16-byte aligned)
+__device__ __forceinline__ Split8 read_split8(const __bf16 *hi, const __bf16 *lo) {
+    Split8 s;
+    s.hi = *reinterpret_cast<const bf16x8 *>(hi);
+    s.lo = *reinterpret_cast<const bf16x8 *>(lo);
+    return s;
+}
+
+// 4 consecutive values -> hi / lo bf16 (one 8-byte store each; 8-byte aligned)
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void split4_store(f32x4v x, __bf16 *hi, __bf16 *lo) {
+    const bf16x4 h = __builtin_convertvector(x, bf16x4);
+    const bf16x4 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4v), bf16x4);
+    *reinterpret_cast<bf16x4 *>(hi) = h;
+    *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+
+__device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// 8 consecutive fp32 values (16-byte aligned)
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// ------------------------------------------------------------ workspace
+// Per (chunk, head) record of bf16 hi / lo planes, split once by the prep
+// kernel for the scan:
+//   T'  [C][C], P [C][C]              A operands, in fragment order (frag_off)
+//   K, Q [C][d_k]                     the conv'd, normalised chunk rows (A
+//                                     operands, fragment order)
+//   K~^T [d_k][C]                     exp(g_L - g_r) k_r, transposed (B operand)
+//   fp32 slot of max(d_k, C) floats   scalar decay: gamma_r = exp(g_r) per row;
+//                                     per key: exp(g_L) per key column
+// A-operand planes are stored in the order the 16x16x32 MFMA reads them:
+// the 16-row x 32-column block (w, ks) of a plane is 1 KiB contiguous, lane
+// l's 8 values (row w*16 + l%16, columns ks*32 + (l/16)*8 ..) at element
+// frag_off(nks, w, ks, l), nks = columns / 32. A wave's operand load then
+// covers 8 whole 128-byte lines instead of 16 half lines.
+__host__ __device__ constexpr int frag_off(int nks, int w, int ks, int lane) {
+    return ((w * nks + ks) * kWave + lane) * 8;
+}
+
+struct RecLayout {
+    size_t thi, tlo, phi, plo, khi, klo, qhi, qlo, kthi, ktlo, egl, elems;
+};
+
+__host__ __device__ constexpr RecLayout rec_layout(int dk) {
+    return RecLayout{0,
+                     (size_t)C * C,
+                     2 * (size_t)C * C,
+                     3 * (size_t)C * C,
+                     4 * (size_t)C * C,
+                     4 * (size_t)C * C + (size_t)C * dk,
+                     4 * (size_t)C * C + 2 * (size_t)C * dk,
+                     4 * (size_t)C * C + 3 * (size_t)C * dk,
+                     4 * (size_t)C * C + 4 * (size_t)C * dk,
+                     4 * (size_t)C * C + 5 * (size_t)C * dk,
+                     4 * (size_t)C * C + 6 * (size_t)C * dk,
+                     4 * (size_t)C * C + 6 * (size_t)C * dk + 2 * (size_t)(dk > C ? dk : C)};
+}
+
+struct WsLayout {
+    size_t rec_off;
+    size_t rec_elems;   // bf16 elements per record
+    size_t max_chunks;
+    size_t total;
+};
+
+__host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H, int dk) {
+    WsLayout w{};
+    w.max_chunks = (size_t)n_tokens / C + (size_t)n_seq;
+    w.rec_off = ((sizeof(int32_t) * ((size_t)n_seq + 1)) + 255) & ~size_t(255);
+    w.rec_elems = rec_layout(dk).elems;
+    w.total = w.rec_off + sizeof(__bf16) * w.rec_elems * w.max_chunks * (size_t)H;
+    return w;
+}
+
+struct SeqSpan {
+    int start, len;
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const int32_t *cu, int s, int n_tokens) {
+    const int a = min(max(cu[s], 0), n_tokens);
+    const int b = min(max(cu[s + 1], a), n_tokens);
+    return {a, b - a};
+}
+
+// ------------------------------------------------------------ plan
+// chunk_start[s] = min(sum_{s' < s} ceil(len_s' / C), max_chunks): the
+// first record of sequence s; sequence s owns chunk_start[s+1] -
+// chunk_start[s] chunks. With valid offsets the cap never binds; with
+// overlapping (invalid) offsets it keeps every record inside the workspace.
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n_seq, int n_tokens,
+                                                        long long max_chunks,
+                                                        int32_t *chunk_start) {
+    __shared__ long long s_part[kThreads];
+    const int tid = threadIdx.x;
+    const int per = (n_seq + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
+    long long sum = 0;
+    for (int s = lo; s < hi; ++s) sum += (seq_span(cu, s, n_tokens).len + C - 1) / C;
+    s_part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        long long run = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const long long x = s_part[i];
+            s_part[i] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+    long long run = s_part[tid];
+    for (int s = lo; s < hi; ++s) {
+        chunk_start[s] = (int32_t)min(run, max_chunks);
+        run += (seq_span(cu, s, n_tokens).len + C - 1) / C;
+    }
+    if (tid == kThreads - 1) chunk_start[n_seq] = (int32_t)min(run, max_chunks);
+}
+
+__device__ __forceinline__ int find_seq(const int32_t *chunk_start, int n_seq, int gc) {
+    int lo = 0, hi = n_seq;  // last s in [0, n_seq) with chunk_start[s] <= gc
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (chunk_start[mid] <= gc) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------ chunk inputs
+// Where a chunk's tokens live: sequence start in the stream, position of the
+// chunk's first token in the sequence, live rows, incoming window.
+template <typename TI>
+struct ChunkSrc {
+    int seq0, p0, L;
+    const TI *win;  // [3][CC] or null (zeros)
+};
+
+// Running sum of log a over the chunk rows, one row per lane (rows >= L add
+// nothing): lane l returns g_l. A wave-wide inclusive scan, shared by the
+// prep and scan kernels so both see identical g.
+__device__ __forceinline__ float chunk_g(const float *log_alpha, int H, int h, int seq0, int p0,
+                                         int L) {
+    const int lane = threadIdx.x % kWave;
+    const int r = min(lane, L - 1);  // clamped: the load is unconditional
+    float g = log_alpha[(size_t)(seq0 + p0 + r) * H + h];
+    g = lane < L ? g : 0.f;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(g, off, kWave);
+        if (lane >= off) g += o;
+    }
+    return g;
+}
+
+// Raw io-dtype words of 8 consecutive values: 4 words for bf16, 8 for fp32.
+template <typename TI>
+struct Raw8 {
+    static constexpr int W = 8 * (int)sizeof(TI) / 4;
+    uint32_t w[W];
+};
+
+template <typename TI>
+__device__ __forceinline__ void raw_load(const TI *p, Raw8<TI> &r) {
+#pragma unroll
+    for (int i = 0; i < Raw8<TI>::W / 4; ++i) {
+        const uint4 u = reinterpret_cast<const uint4 *>(p)[i];
+        r.w[4 * i] = u.x;
+        r.w[4 * i + 1] = u.y;
+        r.w[4 * i + 2] = u.z;
+        r.w[4 * i + 3] = u.w;
+    }
+}
+
+__device__ __forceinline__ void raw_unpack(const Raw8<float> &r, float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(r.w[e]);
+}
+__device__ __forceinline__ void raw_unpack(const Raw8<bf16> &r, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(r.w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
+    }
+}
+
+// lane i <- lane (i - N) mod 16 of its 16-lane DPP row (row_ror:N)
+template <int N>
+__device__ __forceinline__ uint32_t ror16(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + N, 0xf, 0xf, false);
+}
+
+// Conv'd (and, for q / k, normalised) rows rb*16 .. rb*16+15 of the chunk in
+// the A-operand layout of a 16x16x32 MFMA: lane l holds row rb*16 + l%16,
+// columns ks*32 + (l/16)*8 + e for ks < D/32, e < 8. Rows >= L are zero.
+// x is the [N][H][D] stream of this part, cwin the part's first channel of
+// head h in the [q | k | v] window rows, s_w the part's taps [D][4] in LDS
+// (null: no convolution). Each lane loads only its own raw row; lanes 13-15
+// also load the 3 rows before the block (from the stream or the incoming
+// window). The three earlier taps of a row then come from the lanes 1-3 rows
+// up through DPP row rotations, which match the 16-row layout exactly.
+template <int D, typename TI>
+struct RawRows {
+    Raw8<TI> own[D / 32], halo[D / 32];
+};
+
+// rows_load issues the loads (two parts' loads can then be in flight
+// together): every load is unconditional from a clamped, in-bounds address
+// (validity is applied in rows_compute) and nothing is consumed here.
+template <int D, typename TI>
+__device__ __forceinline__ void rows_load(const TI *x, int H, int h, const ChunkSrc<TI> &cs,
+                                          int rb, int CC, int cwin, bool conv,
+                                          RawRows<D, TI> &rr) {
+    constexpr int KS = D / 32;
+    const int lane = threadIdx.x % kWave;
+    const int i = lane % 16;
+    const int cq = (lane / 16) * 8;
+    const int row = rb * RB + i;
+    const TI *own_p = x + (size_t)(cs.seq0 + cs.p0 + min(row, cs.L - 1)) * H * D + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw_load(own_p + ks * 32 + cq, rr.own[ks]);
+    if (conv) {
+        // halo rows (lanes 13..15): stream position ph, or window row 3 + ph.
+        // A block with no live row may put ph past the sequence: clamp it (a
+        // block with a live row has its halo inside the sequence).
+        const int ph = cs.p0 + rb * RB + i - RB;
+        const TI *hp = own_p;
+        if (i >= RB - 3) {
+            if (ph >= 0)
+                hp = x + (size_t)(cs.seq0 + min(ph, cs.p0 + cs.L - 1)) * H * D + (size_t)h * D;
+            else if (cs.win)
+                hp = cs.win + (size_t)(3 + max(ph, -3)) * CC + cwin;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) raw_load(hp + ks * 32 + cq, rr.halo[ks]);
+    }
+}
+
+template <int D, typename TI>
+__device__ __forceinline__ void rows_compute(RawRows<D, TI> &rr, const ChunkSrc<TI> &cs, int rb,
+                                             const float *s_w, bool norm,
+                                             float (&out)[D / 32][8]) {
+    constexpr int KS = D / 32;
+    const int lane = threadIdx.x % kWave;
+    const int i = lane % 16;
+    const int cq = (lane / 16) * 8;
+    const int row = rb * RB + i;
+    const bool live = row < cs.L;
+    const bool conv = s_w != nullptr;
+    Raw8<TI>(&own)[KS] = rr.own;
+    Raw8<TI>(&halo)[KS] = rr.halo;
+    if (conv) {
+        const int ph = cs.p0 + rb * RB + i - RB;
+        const bool hvalid = i >= RB - 3 && (ph >= 0 || cs.win != nullptr);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int q = 0; q < Raw8<TI>::W; ++q) halo[ks].w[q] = hvalid ? halo[ks].w[q] : 0u;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = ks * 32 + cq;
+        float y[8];
+        raw_unpack(own[ks], y);
+        if (conv) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= s_w[(d0 + e) * 4 + 3];
+            // taps n = 1, 2, 3 rows up: source lane j = i - n (mod 16) offers
+            // its own row if j <= 15 - n, else its halo row
+#define GDN_TAP(N)                                                                       \
+    {                                                                                    \
+        Raw8<TI> t;                                                                      \
+        _Pragma("unroll") for (int q = 0; q < Raw8<TI>::W; ++q)                          \
+            t.w[q] = ror16<N>(i <= 15 - (N) ? own[ks].w[q] : halo[ks].w[q]);             \
+        float xt[8];                                                                     \
+        raw_unpack(t, xt);                                                               \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e)                                    \
+            y[e] = fmaf(s_w[(d0 + e) * 4 + 3 - (N)], xt[e], y[e]);                       \
+    }
+            GDN_TAP(1)
+            GDN_TAP(2)
+            GDN_TAP(3)
+#undef GDN_TAP
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            out[ks][e] = live ? y[e] : 0.f;
+            ss = fmaf(out[ks][e], out[ks][e], ss);
+        }
+    }
+    if (norm) {
+        ss += __shfl_xor(ss, 16, kWave);
+        ss += __shfl_xor(ss, 32, kWave);
+        const float inv = 1.0f / sqrtf(ss + kNormEps);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[ks][e] *= inv;
+    }
+}
+
+// Stage the conv taps of `n` channels starting at channel c0 into LDS [n][4].
+__device__ __forceinline__ void stage_taps(const float *conv_w, int c0, int n, float *s_w) {
+    for (int idx = threadIdx.x; idx < n; idx += kThreads)
+        reinterpret_cast<float4 *>(s_w)[idx] = reinterpret_cast<const float4 *>(conv_w)[c0 + idx];
+}
+
+// ------------------------------------------------------------ prep
+// DPP row shift within each 16-lane row: lane i gets lane i - N of its row,
+// lanes i < N get 0 (row_shr:N with bound_ctrl).
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+
+// e^x for the decay factors inside a chunk (|x| is at most the chunk's
+// summed log decay): the hardware base-2 exponential of x log2(e), about
+// 1e-6 relative here, in place of the library expf's longer range reduction
+// (per key 128 of these per lane per chunk, 16 with a scalar decay).
+__device__ __forceinline__ float exp_pk(float x) { return __expf(x); }
+
+// Sum over each group of 4 lanes (DPP quad permutations: lane ^ 1, lane ^ 2).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+    return x;
+}
+
+// Rows R0 + 1 .. C - 1 of the column solve of T = (I + A)^-1 (see prep_body):
+// t[q] holds T[4q + part][col]; arow points at this lane's j = part (mod 4)
+// group of row 0 of A (rows of AP floats). Row r needs the terms j < r,
+// i.e. q < ceil(r / 4); A is zero on and above the diagonal, so the last
+// group needs no mask.
+template <int R0, int AP>
+__device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], int col, int part) {
+#pragma unroll
+    for (int r = R0 + 1; r < C; ++r) {
+        const int nq = (r + 3) / 4;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < (nq + 3) / 4; ++i) {
+            const float4 av = *reinterpret_cast<const float4 *>(arow + r * AP + 4 * i);
+            if (4 * i < nq) acc0 = fmaf(av.x, t[4 * i], acc0);
+            if (4 * i + 1 < nq) acc1 = fmaf(av.y, t[4 * i + 1], acc1);
+            if (4 * i + 2 < nq) acc0 = fmaf(av.z, t[4 * i + 2], acc0);
+            if (4 * i + 3 < nq) acc1 = fmaf(av.w, t[4 * i + 3], acc1);
+        }
+        const float acc = quad_sum(acc0 + acc1);
+        if (r > col && r % 4 == part) t[r / 4] = -acc;
+    }
+}
+
+// VAR: the decay / update rule. kScalar: log a [N, H], the gated delta rule.
+// kKda: per-key log a [N, H, d_k], delta rule. kRwkv6: per-key log a, raw
+// value update (u = v: no A, T' = I, no K Sig term, beta unused).
+// Per-key chunk form (g_r[d] running sums per key): with K^ = K . e^{g},
+// K- = K . e^{-g}, Q^ = Q . e^{g}:
+//   A[r][s] = beta_r <K^_r, K-_s> (s < r),  P[r][s] = <Q^_r, K-_s> (s <= r),
+//   U = T' (V - K^ Sig0),  O = Q^ Sig0 + P U,
+//   Sig_L = diag(e^{g_L}) Sig0 + sum_r (k_r . e^{g_L - g_r}) u_r^T,
+// which the scan runs with gamma = 1 and a per-key state decay.
+// Rows x C matrix staged in LDS (rows padded to C + 1 floats) -> hi / lo
+// bf16 planes of the record, 8 elements (16 bytes) per store: row-major
+// [rows][C], or in A-fragment order (FRAG: a lower-triangular C x C matrix,
+// T' or P, whose 16 x 32 blocks above the diagonal are all zero; the scan
+// never reads them, so they are not written).
+template <int ROWS, bool FRAG = false>
+__device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 *lo) {
+    constexpr int G = C / 8;  // 8-element groups per row
+    for (int idx = threadIdx.x; idx < ROWS * G; idx += kThreads) {
+        const int r = idx / G, c0 = (idx % G) * 8;
+        if (FRAG && c0 / 32 > (r / 16 * 16 + 15) / 32) continue;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = src[r * (C + 1) + c0 + e];
+        const Split8 sp = split8(x);
+        const int off = FRAG ? frag_off(C / 32, r / 16, c0 / 32, r % 16 + 16 * ((c0 % 32) / 8))
+                             : r * C + c0;
+        *reinterpret_cast<bf16x8 *>(hi + off) = sp.hi;
+        *reinterpret_cast<bf16x8 *>(lo + off) = sp.lo;
+    }
+}
+
+template <int DK, typename TI, int VAR>
+__device__ __forceinline__ void prep_body(const PrefillArgs &a) {
+    constexpr bool kPerKey = VAR != kScalar;
+    constexpr bool kDelta = VAR != kRwkv6;
+    constexpr int KS = DK / 32;
+    constexpr int KP = DK + 4;  // padded row of the staged K rows
+    // staged K rows [C][KP]; then K~^T [DK][C + 1]; then P and T' [C][C + 1]
+    // side by side
+    constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
+    constexpr int SK = SK0 > 2 * C * (C + 1) ? SK0 : 2 * C * (C + 1);
+    __shared__ __attribute__((aligned(16))) float s_k[SK];
+    // A, strictly lower, rows of AP floats with each row's entries grouped by
+    // j mod 4 (see a_idx), so the substitution reads them as float4
+    constexpr int AP = C + 4;
+    const auto a_idx = [](int r, int j) { return r * AP + (j % 4) * (C / 4) + j / 4; };
+    __shared__ __attribute__((aligned(16))) float s_A[C * AP];
+    // the q / k conv taps live in s_A's space until A is formed
+    static_assert(2 * DK * 4 <= C * AP, "taps fit the A buffer");
+    float *const s_wq = s_A, *const s_wk = s_A + DK * 4;
+    __shared__ float s_gt[kPerKey ? kWaves * DK : 1];  // per-key: each wave's row-block sums
+    __shared__ __attribute__((aligned(16))) float s_gl[kPerKey ? DK : 4];  // per-key: g_L
+
+    const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
+    const int gc = blockIdx.x, h = blockIdx.y;
+    if (gc >= chunk_start[a.n_seq]) return;
+    const int s = find_seq(chunk_start, a.n_seq, gc);
+    const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
+    const int c = gc - chunk_start[s];
+    const int H = a.H;
+    const int CC = H * (2 * DK + a.dv);
+    const int src = a.parent ? a.parent[s] : s;
+    const bool src_ok = src >= 0 && src < a.n_parent;
+    ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C),
+                    (a.win_in && src_ok) ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC
+                                         : nullptr};
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK);
+    constexpr RecLayout RL = rec_layout(DK);
+    __bf16 *rec = reinterpret_cast<__bf16 *>(static_cast<char *>(a.ws) + wl.rec_off) +
+                  ((size_t)gc * H + h) * wl.rec_elems;
+
+    const bool conv = a.conv_w != nullptr;
+    if (conv) {
+        stage_taps(a.conv_w, h * DK, DK, s_wq);
+        stage_taps(a.conv_w, H * DK + h * DK, DK, s_wk);
+    }
+    __syncthreads();
+    const int row = w * RB + lane % 16;  // this lane's row in the A layout
+    const int cq = (lane / 16) * 8;
+    // scalar decay: g of row `lane`; per key: g of this lane's row and
+    // columns (A layout), the factors e^{g}, e^{-g}, e^{g_L - g} taken where
+    // they are used (few registers stay live across the loads)
+    float g = 0.f, gL = 0.f;
+    float gr[KS][8];
+    if constexpr (!kPerKey) {
+        g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
+        gL = __shfl(g, C - 1, kWave);
+        if (w == 0) reinterpret_cast<float *>(rec + RL.egl)[lane] = expf(g);  // gamma_r for the scan
+    } else {
+        // log a of this lane's row (rows >= L add nothing), then an inclusive
+        // scan over the wave's 16 rows (DPP within 16-lane rows) plus the
+        // sums of the earlier waves' row blocks
+        const float *lap =
+            a.log_alpha + ((size_t)(cs.seq0 + cs.p0 + min(row, cs.L - 1)) * H + h) * DK;
+        float gk[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load8(lap + ks * 32 + cq, gk[ks]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = row < cs.L ? gk[ks][e] : 0.f;
+                x += row_shr<1>(x);
+                x += row_shr<2>(x);
+                x += row_shr<4>(x);
+                x += row_shr<8>(x);
+                gk[ks][e] = x;
+            }
+        if (lane % 16 == 15)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_gt[w * DK + ks * 32 + cq + e] = gk[ks][e];
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = ks * 32 + cq + e;
+                float before = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) before += ww < w ? s_gt[ww * DK + d] : 0.f;
+                gr[ks][e] = gk[ks][e] + before;
+            }
+        // g_L per key; e^{g_L} for the scan's state decay
+        if (tid < DK) {
+            float total = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) total += s_gt[ww * DK + tid];
+            s_gl[tid] = total;
+            reinterpret_cast<float *>(rec + RL.egl)[tid] = expf(total);
+        }
+        __syncthreads();
+    }
+    float b_l = 1.f;
+    if constexpr (kDelta) b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
+    b_l = lane < cs.L ? b_l : 0.f;
+
+    // conv'd, normalised Q and K rows; their split A operands go to the
+    // record. With a scalar decay the raw Q and K rows are requested
+    // together (the per-key form has no registers to spare for that).
+    Split8 qa[DK / 32], ka[DK / 32];
+    RawRows<DK, TI> rk;
+    const auto load_k = [&] {
+        rows_load<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK + h * DK, conv,
+                          rk);
+    };
+    {
+        RawRows<DK, TI> rq;
+        rows_load<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, h * DK, conv, rq);
+        if constexpr (!kPerKey) load_k();
+        float qf[DK / 32][8];
+        rows_compute<DK, TI>(rq, cs, w, conv ? s_wq : nullptr, a.qk_norm != 0, qf);
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+            if constexpr (kPerKey)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[ks][e] *= exp_pk(gr[ks][e]);  // Q^
+            qa[ks] = split8(qf[ks]);
+            const int off = frag_off(KS, w, ks, lane);
+            *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
+            *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = qa[ks].lo;
+        }
+    }
+    if constexpr (kPerKey) load_k();
+    float kf[DK / 32][8];
+    rows_compute<DK, TI>(rk, cs, w, conv ? s_wk : nullptr, a.qk_norm != 0, kf);
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+        // A operand of KK^T and the scan's K Sig term: K (scalar decay), K^
+        // (per key), nothing (raw value update: the record row is zero)
+        // per key, kf becomes this row's K~^T column entries k e^{g_L - g}
+        float ak[8], bk[8], glv[8];
+        if constexpr (kPerKey) lds_read8(s_gl + ks * 32 + cq, glv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (kPerKey) {
+                ak[e] = kDelta ? kf[ks][e] * exp_pk(gr[ks][e]) : 0.f;
+                bk[e] = kf[ks][e] * exp_pk(-gr[ks][e]);  // B operand rows: K-
+                kf[ks][e] *= exp_pk(glv[e] - gr[ks][e]);
+            } else {
+                ak[e] = bk[e] = kf[ks][e];
+            }
+        }
+        ka[ks] = split8(ak);
+        const int off = frag_off(KS, w, ks, lane);
+        *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
+        *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
+#pragma unroll
+        for (int e = 0; e < 8; e += 4)  // 16-byte LDS stores (KP, cq keep them aligned)
+            *reinterpret_cast<float4 *>(s_k + row * KP + ks * 32 + cq + e) =
+                make_float4(bk[e], bk[e + 1], bk[e + 2], bk[e + 3]);
+    }
+    __syncthreads();
+
+    // KK^T and QK^T tiles (w, ct), ct <= w, on MFMA; A to LDS, P kept in
+    // registers until s_k is free
+    float pv[C / RB][4];
+#pragma unroll
+    for (int ct = 0; ct < C / RB; ++ct) {
+        f32x4v kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+        if (ct <= w) {
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                float bx[8];
+                lds_read8(s_k + (ct * RB + lane % 16) * KP + ks * 32 + cq, bx);
+                const Split8 bs = split8(bx);
+                kk = mma3(ka[ks], bs, kk);
+                qk = mma3(qa[ks], bs, qk);
+            }
+        }
+        // D layout: rows w*16 + (l/16)*4 + i, column ct*16 + l%16
+        const int col = ct * RB + lane % 16;
+        const float g_c = __shfl(g, col, kWave);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = w * RB + (lane / 16) * 4 + i;
+            const float g_r = __shfl(g, r, kWave);
+            const float b_r = __shfl(b_l, r, kWave);
+            const bool live = r < cs.L && col < cs.L;
+            // the decay between rows: a factor here (scalar), inside the
+            // products already (per key)
+            const float dec = (live && col <= r) ? (kPerKey ? 1.f : exp_pk(g_r - g_c)) : 0.f;
+            s_A[a_idx(r, col)] = (kDelta && col < r) ? b_r * dec * kk[i] : 0.f;
+            pv[ct][i] = dec * qk[i];
+        }
+    }
+    __syncthreads();  // s_A complete; the K rows in s_k are no longer needed
+
+    // K~^T[d][r] = exp(g_L - g_r) k_r[d], staged transposed for coalesced stores
+    {
+        const float f = kPerKey ? 1.f : expf(gL - __shfl(g, row, kWave));
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                s_k[(ks * 32 + cq + e) * (C + 1) + row] = kPerKey ? kf[ks][e] : kf[ks][e] * f;
+    }
+    __syncthreads();
+    put_planes<DK>(s_k, rec + RL.kthi, rec + RL.ktlo);
+
+    // T = (I + A)^-1, one column per group of 4 lanes (columns are
+    // independent): lane (col, part) keeps T[j][col] for j = part (mod 4),
+    // starting from the identity column; rows r <= col leave the column
+    // unchanged, so a wave starts after its first column. It runs while the
+    // K~^T stores drain (it reads only s_A).
+    const int col = w * 16 + lane / 4, part = lane % 4;
+    float t[C / 4];
+#pragma unroll
+    for (int q = 0; q < C / 4; ++q) t[q] = (q * 4 + part == col) ? 1.f : 0.f;
+    {
+        const float *arow = s_A + part * (C / 4);
+        switch (__builtin_amdgcn_readfirstlane(w)) {  // straight-line rows per wave
+            case 0: tri_solve<0, AP>(arow, t, col, part); break;
+            case 1: tri_solve<16, AP>(arow, t, col, part); break;
+            case 2: tri_solve<32, AP>(arow, t, col, part); break;
+            default: tri_solve<48, AP>(arow, t, col, part); break;
+        }
+    }
+    __syncthreads();  // every lane is done with the K~^T copy-out from s_k
+    // P (from registers) and T'[j][col] = T[j][col] beta_col, staged side by
+    // side in s_k for coalesced stores
+    float *const s_P = s_k, *const s_T = s_k + C * (C + 1);
+    static_assert(2 * C * (C + 1) <= SK, "P and T' staging fit s_k");
+#pragma unroll
+    for (int ct = 0; ct < C / RB; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s_P[(w * RB + (lane / 16) * 4 + i) * (C + 1) + ct * RB + lane % 16] = pv[ct][i];
+    const float bcol = __shfl(b_l, col, kWave);
+#pragma unroll
+    for (int q = 0; q < C / 4; ++q) s_T[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
+    __syncthreads();
+    put_planes<C, true>(s_P, rec + RL.phi, rec + RL.plo);
+    put_planes<C, true>(s_T, rec + RL.thi, rec + RL.tlo);
+}
+
+template <int DK, typename TI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void prep_kernel(PrefillArgs a) {
+    prep_body<DK, TI, kScalar>(a);
+}
+
+// Per key the decay factors add registers; capped so two workgroups of the
+// largest head size still share a compute unit (measured faster than one,
+// while the scalar form runs best at its natural allocation).
+template <int DK, typename TI, int VAR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prep_kernel_pk(
+    PrefillArgs a) {
+    prep_body<DK, TI, VAR>(a);
+}
+
+// ------------------------------------------------------------ scan
+// Workgroup -> (sequence-head, value tile): the NT value tiles of one
+// sequence-head get block indices congruent modulo 8, so they are dispatched
+// to the same XCD and share its L2 for the chunk records they all read.
+__device__ __forceinline__ void scan_unit(int b, int NT, int &sh, int &tile) {
+    const int xcd = b % 8, local = b / 8;
+    tile = local % NT;
+    sh = (local / NT) * 8 + xcd;
+}
+
+// Offset (in bf16 elements) of 16-byte chunk `ch` of row `r` in an LDS
+// plane of rows of C bf16 (128 bytes): the chunk index is XOR-swizzled by
+// the row so that 16 lanes reading one chunk of 16 consecutive rows spread
+// over all banks.
+__device__ __forceinline__ int kt_swz(int r, int ch) { return r * C + ((ch ^ (r & 7)) << 3); }
+
+// Registers a chunk step needs from memory, loaded ahead of use: only loads
+// go in here (no arithmetic on the results), so the loads can stay in
+// flight until the step consumes them.
+
+// Two adjacent outputs (pair-aligned) in one store.
+__device__ __forceinline__ void store_pair(float *p, float x, float y) {
+    *reinterpret_cast<float2 *>(p) = make_float2(x, y);
+}
+__device__ __forceinline__ void store_pair(bf16 *p, float x, float y) {
+    *reinterpret_cast<uint32_t *>(p) =
+        (uint32_t)from_f32<bf16>(x).bits | ((uint32_t)from_f32<bf16>(y).bits << 16);
+}
+
+// 16-byte direct-to-LDS load (lane l lands at lds + 8 l elements). Kept out
+// of the kernel templates: with the builtin inside a template the host pass
+// drops the kernel's launch stub without a diagnostic.
+__device__ __forceinline__ void lds_dma16(const __bf16 *g, __bf16 *lds) {
+    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// Two adjacent io-dtype values in one load: the value columns 2n, 2n + 1 of
+// a lane (see vcol).
+template <typename TI> struct VPair;
+template <> struct VPair<bf16> {
+    typedef uint32_t type;
+    static __device__ __forceinline__ float get(type x, int t) {
+        return __uint_as_float(t == 0 ? x << 16 : x & 0xffff0000u);
+    }
+};
+template <> struct VPair<float> {
+    typedef float2 type;
+    static __device__ __forceinline__ float get(type x, int t) { return t == 0 ? x.x : x.y; }
+};
+
+// Value columns of a scan tile: internal column c (sub-tile t = c / 16,
+// MFMA column n = c % 16) is the tile's column 2n + t, so the two columns a
+// lane holds are adjacent in memory (one load / store per row for both).
+__device__ __forceinline__ int vcol(int c) { return 2 * (c % 16) + c / 16; }
+
+template <int KS, int NVT, typename TI>
+struct ChunkRegs {
+    static_assert(NVT == 2, "a lane holds one adjacent pair of value columns");
+    Split8 ka[KS], qa[KS], ta[2], pa[2];
+    typename VPair<TI>::type vraw[7];  // raw V rows r0-3 .. r0+3 of this lane's column pair
+    float4 gam;       // scalar decay: gamma of this lane's 4 rows (C/D layout)
+    float gaml;       // scalar decay: gamma_L
+};
+
+// PK: per-key decay (K and Q arrive pre-scaled, gamma = 1; the state decays
+// by e^{g_L} per key column, staged in LDS with the chunk's K~^T planes).
+// CK: also write checkpoints (state and window every ckpt_every chunks);
+// a separate instance so the plain scan keeps its register budget.
+template <int DK, int DV, typename TI, typename TO, bool PK, bool CK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void scan_kernel(PrefillArgs a) {
+    constexpr int KS = DK / 32;          // k-steps over d_k
+    constexpr int SP = DK + 4;           // padded row of Sig^T (fp32)
+    constexpr int CB = C + 8;            // padded row of the R^T / U^T planes
+    constexpr int NVT = TV / 16;         // 16-wide value sub-tiles
+    constexpr int NFT = NVT * (DK / 16); // output tiles of the state update
+    constexpr int NEG = NFT / kWaves;    // state-update tiles per wave
+    static_assert(NFT % kWaves == 0, "state-update tiles split evenly over the waves");
+    static_assert(DK / 4 <= kWave, "e^{g_L} row fits one wave's 16-byte copies");
+    constexpr RecLayout RL = rec_layout(DK);
+    // Sig^T tile [TV][DK] in fp32; R^T and U^T [TV][C] as hi / lo bf16
+    // planes (split once when written); K~^T [DK][C] hi / lo planes copied
+    // from the chunk record by direct-to-LDS loads (swizzled rows).
+    __shared__ __attribute__((aligned(16))) float s_St[TV * SP];
+    __shared__ __attribute__((aligned(16))) __bf16 s_Rh[TV * CB], s_Rl[TV * CB];
+    __shared__ __attribute__((aligned(16))) __bf16 s_Uh[TV * CB], s_Ul[TV * CB];
+    __shared__ __attribute__((aligned(16))) __bf16 s_Kh[DK * C], s_Kl[DK * C];
+    __shared__ __attribute__((aligned(16))) float s_wv[TV * 4];
+    __shared__ __attribute__((aligned(16))) __bf16 s_eg[PK ? 2 * DK : 8];  // e^{g_L}, fp32 bits
+
+    constexpr int NT = DV / TV;
+    int shd, tile;
+    scan_unit(blockIdx.x, NT, shd, tile);
+    if (shd >= a.n_seq * a.H) return;
+    const int s = shd / a.H, h = shd % a.H;
+    const int H = a.H;
+    const int CC = H * (2 * DK + DV);
+    const int j0 = tile * TV;
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK);
+    const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
+    const int src = a.parent ? a.parent[s] : s;
+    const bool src_ok = src >= 0 && src < a.n_parent;
+
+    if (!src_ok) {  // a branch with an invalid parent: NaN outputs, nothing else
+        if (a.o)
+            for (int idx = tid; idx < sp.len * TV; idx += kThreads)
+                static_cast<TO *>(a.o)[((size_t)(sp.start + idx / TV) * H + h) * DV + j0 + idx % TV] =
+                    from_f32<TO>(quiet_nan());
+        if (a.state_out)
+            for (int idx = tid; idx < DK * TV; idx += kThreads)
+                a.state_out[(((size_t)s * H + h) * DK + idx / TV) * DV + j0 + idx % TV] = quiet_nan();
+        return;
+    }
+    const TI *win = a.win_in ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC : nullptr;
+
+    const bool conv = a.conv_w != nullptr;
+    if (conv) stage_taps(a.conv_w, 2 * H * DK + h * DV + j0, TV, s_wv);
+
+    const bool want_o = a.o != nullptr;
+    const int kmax = (w * RB + RB - 1) / 32;  // T', P lower triangular: k-steps to use
+    const int acol = (lane / 16) * 8;
+    const int r0v = w * RB + (lane / 16) * 4;  // first of this lane's rows in the C/D layout
+    // read once: inside the loop the compiler could not prove these unchanged
+    // across the o stores and would reload them behind a full wait
+    const int cs0 = chunk_start[s];
+    const int nchunks = chunk_start[s + 1] - cs0;  // <= ceil(len / C)
+    const TI *vs = static_cast<const TI *>(a.v);
+    const int cwin_v = 2 * H * DK + h * DV;
+
+    // the state tile [DK][TV] of this workgroup (Sig^T in s_St) into a
+    // [DK][DV] state at dst; valid at a chunk boundary (after the barrier
+    // that closes the previous state update)
+    // (4 consecutive tile columns per 16-byte store; tile column j is
+    // internal column (j % 2) * 16 + j / 2, the inverse of vcol)
+    auto put_state = [&](float *dst) {
+        for (int idx = tid; idx < DK * TV / 4; idx += kThreads) {
+            const int d = idx / (TV / 4), j = 4 * (idx % (TV / 4));
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = s_St[((j + e) % 2 * 16 + (j + e) / 2) * SP + d];
+            *reinterpret_cast<float4 *>(dst + (size_t)d * DV + j0 + j) =
+                make_float4(x[0], x[1], x[2], x[3]);
+        }
+    };
+    // conv window after position `end` of the sequence: its last 3 raw
+    // inputs (from the incoming window where end < 3), head h's channels
+    auto put_window = [&](TI *wo, int end) {
+        const int W = 2 * DK + DV;
+        for (int idx = tid; idx < 3 * W; idx += kThreads) {
+            const int r = idx / W, wc = idx % W;
+            const int p = end - 3 + r;
+            int cch;
+            const TI *xs;
+            size_t col, stride;
+            if (wc < DK) {
+                cch = h * DK + wc; xs = static_cast<const TI *>(a.q);
+                col = (size_t)h * DK + wc; stride = (size_t)H * DK;
+            } else if (wc < 2 * DK) {
+                cch = H * DK + h * DK + (wc - DK); xs = static_cast<const TI *>(a.k);
+                col = (size_t)h * DK + (wc - DK); stride = (size_t)H * DK;
+            } else {
+                cch = 2 * H * DK + h * DV + (wc - 2 * DK); xs = static_cast<const TI *>(a.v);
+                col = (size_t)h * DV + (wc - 2 * DK); stride = (size_t)H * DV;
+            }
+            TI val;
+            if (p >= 0) val = xs[(size_t)(sp.start + p) * stride + col];
+            else if (win) val = win[(size_t)(3 + p) * CC + cch];
+            else val = from_f32<TI>(0.f);
+            wo[(size_t)r * CC + cch] = val;
+        }
+    };
+    // checkpoint k of the sequence: the state and window after
+    // (k + 1) * ckpt_every chunks; `ckpt_at(c)` says whether the boundary
+    // before chunk c is one (k < ckpt_cap)
+    auto ckpt_at = [&](int c) {
+        return a.ckpt_state && a.ckpt_every > 0 && c > 0 && c % a.ckpt_every == 0 &&
+               c / a.ckpt_every - 1 < a.ckpt_cap;
+    };
+    auto put_checkpoint = [&](int c) {
+        const size_t k = (size_t)s * a.ckpt_cap + (c / a.ckpt_every - 1);
+        put_state(a.ckpt_state + (k * H + h) * DK * DV);
+        if (a.ckpt_window && tile == 0) put_window(static_cast<TI *>(a.ckpt_window) + k * 3 * CC, c * C);
+    };
+
+    auto record = [&](int c) {
+        return reinterpret_cast<const __bf16 *>(static_cast<const char *>(a.ws) + wl.rec_off) +
+               ((size_t)(cs0 + c) * H + h) * wl.rec_elems;
+    };
+    // loads only: every address is clamped in bounds, nothing is consumed here
+    auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI> &r) {
+        const __bf16 *rec = record(c);
+        const int p0 = c * C, L = min(C, sp.len - p0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off = frag_off(KS, w, ks, lane);
+            r.ka[ks] = read_split8(rec + RL.khi + off, rec + RL.klo + off);
+            if (want_o) r.qa[ks] = read_split8(rec + RL.qhi + off, rec + RL.qlo + off);
+        }
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+            if (kq <= kmax) {
+                const int off = frag_off(C / 32, w, kq, lane);
+                r.ta[kq] = read_split8(rec + RL.thi + off, rec + RL.tlo + off);
+                if (want_o) r.pa[kq] = read_split8(rec + RL.phi + off, rec + RL.plo + off);
+            }
+        {
+            const int j = j0 + 2 * (lane % 16);  // columns j, j + 1 (even: pair-aligned)
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                const int p = p0 + r0v - 3 + q;  // >= -3
+                const TI *ptr = (p < 0 && win) ? win + (size_t)(3 + p) * CC + cwin_v + j
+                                               : vs + (size_t)(sp.start + min(max(p, 0), p0 + L - 1)) *
+                                                          H * DV + (size_t)h * DV + j;
+                r.vraw[q] = *reinterpret_cast<const typename VPair<TI>::type *>(ptr);
+            }
+        }
+        if constexpr (PK) {
+            r.gam = make_float4(1.f, 1.f, 1.f, 1.f);
+            r.gaml = 1.f;
+        } else {
+            const float *gr = reinterpret_cast<const float *>(rec + RL.egl);
+            r.gam = *reinterpret_cast<const float4 *>(gr + r0v);
+            r.gaml = gr[C - 1];
+        }
+    };
+    // K~^T hi / lo planes of chunk c into LDS (direct-to-LDS, 16 B per lane;
+    // the LDS position of a lane's bytes is fixed, so the swizzle is applied
+    // by choosing which global chunk each lane fetches)
+    auto load_kt = [&](int c) {
+        const __bf16 *rec = record(c);
+        constexpr int PER_WAVE = DK * C * 2 / 16 / kThreads;  // 16-byte pieces per lane, per plane
+#pragma unroll
+        for (int q = 0; q < PER_WAVE; ++q) {
+            const int piece = (q * kWaves + w) * kWave + lane;  // 16-byte piece of the plane
+            const int r = piece / 8, chl = piece % 8;           // LDS row, LDS chunk slot
+            const int chg = chl ^ (r & 7);                      // global chunk stored there
+            const int lds0 = (q * kWaves + w) * kWave * 8;      // wave-uniform LDS element offset
+            lds_dma16(rec + RL.kthi + r * C + chg * 8, s_Kh + lds0);
+            lds_dma16(rec + RL.ktlo + r * C + chg * 8, s_Kl + lds0);
+        }
+        if constexpr (PK)  // DK floats: one 16-byte piece per lane of wave 0
+            if (w == 0 && lane < DK / 4) lds_dma16(rec + RL.egl + lane * 8, s_eg);
+    };
+
+    // the first chunk's operands are requested before the incoming state
+    // tile, so the two round trips overlap (a one-chunk branch pays one)
+    ChunkRegs<KS, NVT, TI> nxt;
+    if (nchunks > 0) load_regs(0, nxt);
+    for (int idx = tid; idx < DK * TV; idx += kThreads) {
+        const int d = idx / TV, c = idx % TV;
+        s_St[c * SP + d] =
+            a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + vcol(c)] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        if constexpr (CK)
+            if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
+        const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
+        const ChunkRegs<KS, NVT, TI> cur = nxt;
+        load_kt(c);
+
+        // gamma_r = exp(g_r) of this lane's rows, from the chunk record (the
+        // prep kernel's running sums; rows >= L add nothing)
+        const float gam[4] = {cur.gam.x, cur.gam.y, cur.gam.z, cur.gam.w};
+
+        // conv'd V entries of this lane (C/D layout), from the raw rows
+        float vf[NVT][4];
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const int jt = vcol(t * 16 + lane % 16);  // the tile column, for its taps
+            float xr[7];
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                const int row = r0v - 3 + q, p = cs.p0 + row;
+                const bool ok = (conv || q >= 3) && ((row < cs.L && p >= 0) || (p < 0 && win));
+                xr[q] = ok ? VPair<TI>::get(cur.vraw[q], t) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float y = xr[i + 3];
+                if (conv) {
+                    y = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) y = fmaf(s_wv[jt * 4 + r], xr[i + r], y);
+                }
+                vf[t][i] = r0v + i < cs.L ? y : 0.f;
+            }
+        }
+
+        // K Sig0 and Q Sig0 share the split Sig^T fragments;
+        // R = V - diag(gamma) K Sig0 goes to LDS, Q Sig0 stays in registers
+        f32x4v acc_o[NVT];
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+            acc_o[t] = acc;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                float bx[8];
+                lds_read8(s_St + (t * 16 + lane % 16) * SP + ks * 32 + acol, bx);
+                const Split8 bs = split8(bx);
+                acc = mma3(cur.ka[ks], bs, acc);
+                if (want_o) acc_o[t] = mma3(cur.qa[ks], bs, acc_o[t]);
+            }
+            // the lane's 4 rows are consecutive in the R^T planes
+            f32x4v rv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rv[i] = vf[t][i] - gam[i] * acc[i];
+            const int ro = (t * 16 + lane % 16) * CB + r0v;
+            split4_store(rv, s_Rh + ro, s_Rl + ro);
+        }
+        // This wave's direct-to-LDS copies of K~^T are its only vector memory
+        // operations in flight here: finish them before this barrier (a
+        // workgroup fence would wait for them here anyway), so the whole
+        // plane is visible to every wave after it and the state update needs
+        // no barrier of its own. Sig^T is last read above (K Sig0, Q Sig0),
+        // so it may be rewritten by the state update after the next barrier.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+
+        // U = T' R
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq)
+                if (kq <= kmax) {
+                    const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                    acc = mma3(cur.ta[kq], read_split8(s_Rh + off, s_Rl + off), acc);
+                }
+            const int uo = (t * 16 + lane % 16) * CB + r0v;
+            split4_store(acc, s_Uh + uo, s_Ul + uo);
+        }
+        __syncthreads();
+
+        // O = diag(gamma) Q Sig0 + P U (stored below, after the next chunk's
+        // operands are requested)
+        if (want_o) {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc_o[t][i] *= gam[i];
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq)
+                    if (kq <= kmax) {
+                        const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                        acc_o[t] = mma3(cur.pa[kq], read_split8(s_Uh + off, s_Ul + off), acc_o[t]);
+                    }
+            }
+        }
+
+        if (c + 1 < nchunks) load_regs(c + 1, nxt);  // prefetch the next step
+        if (want_o) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0v + i;
+                if (r < cs.L)
+                    store_pair(static_cast<TO *>(a.o) + ((size_t)(cs.seq0 + cs.p0 + r) * H + h) * DV +
+                                   j0 + 2 * (lane % 16),
+                               acc_o[0][i], acc_o[1][i]);
+            }
+        }
+
+        // Sig^T <- gamma_L Sig^T + U^T K~   (tiles: value sub-tile x 16 keys)
+        const float gamL = cur.gaml;
+#pragma unroll
+        for (int m = 0; m < NEG; ++m) {
+            const int ft = w + m * kWaves;
+            const int t = ft % NVT, dt = ft / NVT;
+            // per key: e^{g_L} of column dt*16 + lane%16
+            const float dec = PK ? reinterpret_cast<const float *>(s_eg)[dt * 16 + lane % 16] : gamL;
+            f32x4v acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = dec * s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16];
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                const int ok = kt_swz(dt * 16 + lane % 16, kq * 4 + lane / 16);
+                acc = mma3(read_split8(s_Uh + ou, s_Ul + ou), read_split8(s_Kh + ok, s_Kl + ok), acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16] = acc[i];
+        }
+        __syncthreads();
+    }
+
+    if (a.state_out) put_state(a.state_out + ((size_t)s * H + h) * DK * DV);
+    if (a.win_out && tile == 0) put_window(static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
+    // a checkpoint at the end of the sequence (its length a multiple of the
+    // checkpoint spacing)
+    if constexpr (CK)
+        if (ckpt_at(nchunks) && nchunks * C == sp.len) put_checkpoint(nchunks);
+}
+
+template <int DK, int DV, typename TI, typename TO>
+hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
+    auto prep = [&](auto vtag) {
+        constexpr int VAR = decltype(vtag)::value;
+        if constexpr (VAR == kScalar) return prep_kernel<DK, TI>;
+        else return prep_kernel_pk<DK, TI, VAR>;
+    };
+    if (a.n_seq == 0) return hipSuccess;
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK);
+    int32_t *chunk_start = static_cast<int32_t *>(a.ws);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq, a.n_tokens,
+                       (long long)wl.max_chunks, chunk_start);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (wl.max_chunks > 0) {
+        const dim3 grid((unsigned)wl.max_chunks, a.H);
+        if (a.variant == kKda)
+            hipLaunchKernelGGL(prep(std::integral_constant<int, kKda>{}), grid, dim3(kThreads), 0,
+                               stream, a);
+        else if (a.variant == kRwkv6)
+            hipLaunchKernelGGL(prep(std::integral_constant<int, kRwkv6>{}), grid, dim3(kThreads),
+                               0, stream, a);
+        else
+            hipLaunchKernelGGL(prep(std::integral_constant<int, kScalar>{}), grid, dim3(kThreads),
+                               0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const size_t n_sh = (size_t)a.n_seq * a.H;
+    const unsigned blocks = (unsigned)(((n_sh + 7) / 8) * 8 * (DV / TV));  // see scan_unit
+    const bool pk = a.variant != kScalar;
+    const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
+    auto scan = [&](auto pk_tag, auto ck_tag) {
+        hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, decltype(pk_tag)::value,
+                                        decltype(ck_tag)::value>),
+                           dim3(blocks), dim3(kThreads), 0, stream, a);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (pk) ck ? scan(T_{}, T_{}) : scan(T_{}, F_{});
+    else ck ? scan(F_{}, T_{}) : scan(F_{}, F_{});
+    return hipGetLastError();
+}
+
+
+// every value width, io and output type for one key width (one translation
+// unit per key width, so the instances compile in parallel)
+template <int DK>
+hipError_t launch_prefill_dk(int dv, int io, int out, const PrefillArgs &a, hipStream_t stream) {
+    auto go = [&](auto vtag) -> hipError_t {
+        constexpr int DV = decltype(vtag)::value;
+        if (io == kBF16) {
+            if (out == kBF16) return launch_typed<DK, DV, bf16, bf16>(a, stream);
+            return launch_typed<DK, DV, bf16, float>(a, stream);
+        }
+        if (out == kBF16) return launch_typed<DK, DV, float, bf16>(a, stream);
+        return launch_typed<DK, DV, float, float>(a, stream);
+    };
+    switch (dv) {
+        case 32: return go(std::integral_constant<int, 32>{});
+        case 64: return go(std::integral_constant<int, 64>{});
+        default: return go(std::integral_constant<int, 128>{});
+    }
+}
+
+}  // namespace
+}  // namespace gdn

@@ -30,8 +30,8 @@ import statistics
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-DECODE_SOURCES = ("csrc/decode.hip", "csrc/gdn_device.hpp")
-PREFILL_SOURCES = ("csrc/prefill.hip", "csrc/gdn_device.hpp")
+DECODE_SOURCES = ("csrc/decode_kernels.hpp", "csrc/decode_d128.hip", "csrc/gdn_device.hpp")
+PREFILL_SOURCES = ("csrc/prefill_kernels.hpp", "csrc/prefill_d128.hip", "csrc/gdn_device.hpp")
 ATTENTION_SOURCES = ("csrc/attention.hip", "csrc/attention_launch.hpp", "csrc/gdn_device.hpp")
 SOURCES = {"decode": DECODE_SOURCES, "prefill": PREFILL_SOURCES, "attention": ATTENTION_SOURCES}
 

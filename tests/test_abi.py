@@ -76,7 +76,8 @@ def test_decode_validation(lib):
     assert eager(lib, var=7) == INVALID
     assert eager(lib, io=5) == INVALID
     assert eager(lib, dk=96, dv=96) == UNSUPPORTED
-    assert eager(lib, dk=128, dv=64) == UNSUPPORTED
+    assert eager(lib, dk=128, dv=48) == UNSUPPORTED
+    assert eager(lib, dk=16, dv=64) == UNSUPPORTED
 
 
 def test_append_validation(lib):
@@ -114,7 +115,13 @@ def test_prefill_validation_and_workspace(lib):
     # beta is required by the delta-rule variants (may be NULL only for RWKV6)
     assert call(beta=NULL, variant=0) == INVALID
     assert call(beta=NULL, variant=1) == INVALID
-    assert call(chunk=48) == UNSUPPORTED
+    # chunk: 16, 32 and 64 are the interface's sizes, only 64 is built;
+    # anything else is not a chunk size
+    assert call(chunk=48) == INVALID
+    assert call(chunk=0) == INVALID
+    assert call(chunk=-64) == INVALID
+    assert call(chunk=16) == UNSUPPORTED
+    assert call(chunk=32) == UNSUPPORTED
     assert call(d=80) == UNSUPPORTED
     assert call(ws=NULL) == WORKSPACE
     assert call(ws_bytes=need - 1) == WORKSPACE
