@@ -18,8 +18,10 @@
  * Conventions for every call
  *  - Every array argument is a caller-owned DEVICE pointer (HBM), dense
  *    row-major with the layout given, 16-byte aligned. The library never
- *    allocates, frees or keeps a pointer, and holds no global mutable state
- *    apart from a thread-local copy of the last HIP error code.
+ *    allocates, frees or keeps a caller's pointer. Its only global mutable
+ *    state is a thread-local copy of the last HIP error code and, for
+ *    gdn_fork_attention_noalloc, one file-scope device table per GPU (with
+ *    a mutex-guarded cache of its per-device address).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
  *    calls return after enqueue without synchronising. Integer metadata
  *    (offsets, parents, slots, log lengths) lives in device memory, so a
@@ -329,6 +331,34 @@ int gdn_fork_attention(const void *q, const void *k, const void *v,
                        float scale, int trunk_queries, void *o, int io_dtype,
                        int o_dtype, void *workspace, size_t ws_bytes,
                        void *stream);
+
+/*
+ * gdn_fork_attention_noalloc -- gdn_fork_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation and
+ * arguments without a workspace. Its tile table lives in one file-scope
+ * device array of the library, (GDN_FORK_ATTENTION_NOALLOC_MAX_SEGMENTS + 1)
+ * int32 (256 KiB), which every GPU the library runs on holds from the
+ * library's load until the process ends; its address on a device is looked
+ * up on the first call with that device current. The call allocates and
+ * frees nothing. Every call on one GPU shares that GPU's table, so calls
+ * that overlap in time on one GPU (concurrent streams, or host threads
+ * without ordering) race and must not be issued; calls ordered on one
+ * stream are safe. Each call writes the whole part of the table it reads
+ * before reading it, so nothing needs clearing between calls.
+ *  n_req + n_branch  at most GDN_FORK_ATTENTION_NOALLOC_MAX_SEGMENTS
+ *  stream            a stream of the calling thread's current device
+ * Errors: as gdn_fork_attention; WORKSPACE when n_req + n_branch exceeds
+ * the maximum; INVALID_ARG when the stream belongs to another device.
+ */
+#define GDN_FORK_ATTENTION_NOALLOC_MAX_SEGMENTS 65536
+int gdn_fork_attention_noalloc(const void *q, const void *k, const void *v,
+                               const int32_t *cu_seqlens, int n_req,
+                               const int32_t *branch_cu,
+                               const int32_t *branch_parent, int n_branch,
+                               int n_tokens, int H, int H_kv, int d,
+                               float scale, int trunk_queries, void *o,
+                               int io_dtype, int o_dtype, void *stream);
 
 /*
  * gdn_stream_probe -- a measurement aid, not part of the recurrence: streams

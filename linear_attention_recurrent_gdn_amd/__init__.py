@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     fork_attention_workspace_bytes,
     gdn_decode_eager,
     gdn_fork_attention,
+    gdn_fork_attention_noalloc,
     gdn_fork_branches,
     gdn_prefill_checkpointed,
     gdn_prefill_shared,
@@ -34,6 +35,7 @@ __all__ = [
     "deltalog_append_decode",
     "deltalog_merge",
     "gdn_fork_attention",
+    "gdn_fork_attention_noalloc",
     "fork_attention_workspace_bytes",
     "prefill_workspace_bytes",
     "gdn_stream_probe",

@@ -45,8 +45,13 @@ SIGNATURES = {
     "gdn_fork_attention_workspace_bytes": (_S, [_I, _I]),
     "gdn_fork_attention": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float,
                                 _I, _P, _I, _I, _P, _S, _P]),
+    "gdn_fork_attention_noalloc": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                        ctypes.c_float, _I, _P, _I, _I, _P]),
     "gdn_stream_probe": (_I, [_P, _P, _S, _I, _P]),
 }
+
+# segments the allocation-free fork attention's static tile table holds
+FORK_ATTENTION_NOALLOC_MAX_SEGMENTS = 65536
 
 
 class GDNError(RuntimeError):
@@ -322,6 +327,26 @@ def gdn_fork_attention(q, k, v, cu_seqlens, o, branch_cu=None, branch_parent=Non
         sc, int(bool(trunk_queries)), _dev(o, "o", _IO, (N, H, d)), _io_code(q), _io_code(o),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check("gdn_fork_attention", st)
+
+
+def gdn_fork_attention_noalloc(q, k, v, cu_seqlens, o, branch_cu=None, branch_parent=None,
+                               scale=None, trunk_queries=True, stream=None):
+    """gdn_fork_attention without a workspace: the tile table is the
+    library's static per-GPU array (at most FORK_ATTENTION_NOALLOC_MAX_SEGMENTS
+    trunks + branches; calls that overlap on one GPU race)."""
+    N, H, d = q.shape
+    Hkv = k.shape[1]
+    R = cu_seqlens.shape[0] - 1
+    NB = 0 if branch_cu is None else branch_cu.shape[0] - 1
+    sc = float(d) ** -0.5 if scale is None else float(scale)
+    st = load().gdn_fork_attention_noalloc(
+        _dev(q, "q", torch.bfloat16, (N, H, d)), _dev(k, "k", torch.bfloat16, (N, Hkv, d)),
+        _dev(v, "v", torch.bfloat16, (N, Hkv, d)), _dev(cu_seqlens, "cu_seqlens", _I32, (R + 1,)),
+        R, _dev(branch_cu, "branch_cu", _I32, (NB + 1,), optional=NB == 0),
+        _dev(branch_parent, "branch_parent", _I32, (NB,), optional=NB == 0), NB, N, H, Hkv, d,
+        sc, int(bool(trunk_queries)), _dev(o, "o", _IO, (N, H, d)), _io_code(q), _io_code(o),
+        _stream(stream))
+    _check("gdn_fork_attention_noalloc", st)
 
 
 def gdn_stream_probe(src, dst, copy=False, stream=None):

@@ -246,11 +246,11 @@ size_t gdn_fork_attention_workspace_bytes(int n_req, int n_branch) {
     return gdn::attention_workspace_bytes(n_req, n_branch);
 }
 
-int gdn_fork_attention(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
-                       int n_req, const int32_t *branch_cu, const int32_t *branch_parent,
-                       int n_branch, int n_tokens, int H, int H_kv, int d, float scale,
-                       int trunk_queries, void *o, int io_dtype, int o_dtype, void *workspace,
-                       size_t ws_bytes, void *stream) {
+static int attention_common(const void *q, const void *k, const void *v,
+                            const int32_t *cu_seqlens, int n_req, const int32_t *branch_cu,
+                            const int32_t *branch_parent, int n_branch, int n_tokens, int H,
+                            int H_kv, int d, float scale, int trunk_queries, void *o,
+                            int io_dtype, int o_dtype) {
     if (!q || !k || !v || !o) return GDN_ERR_INVALID_ARG;
     if (n_req < 0 || n_branch < 0 || n_tokens < 0 || H < 1 || H_kv < 1 || H % H_kv != 0)
         return GDN_ERR_INVALID_ARG;
@@ -261,8 +261,15 @@ int gdn_fork_attention(const void *q, const void *k, const void *v, const int32_
     if (io_dtype != GDN_BF16 || (d != 64 && d != 128)) return GDN_ERR_UNSUPPORTED;
     // in-kernel row offsets are 32-bit
     if ((long long)n_tokens * H * d >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
-    if (!workspace || ws_bytes < gdn::attention_workspace_bytes(n_req, n_branch))
-        return GDN_ERR_WORKSPACE;
+    (void)trunk_queries;
+    return GDN_OK;
+}
+
+static int attention_launch(const void *q, const void *k, const void *v,
+                            const int32_t *cu_seqlens, int n_req, const int32_t *branch_cu,
+                            const int32_t *branch_parent, int n_branch, int n_tokens, int H,
+                            int H_kv, int d, float scale, int trunk_queries, void *o, int o_dtype,
+                            void *workspace, void *stream) {
     gdn::AttnArgs a{};
     a.q = q;
     a.k = k;
@@ -280,6 +287,49 @@ int gdn_fork_attention(const void *q, const void *k, const void *v, const int32_
     a.scale = scale;
     a.trunk_queries = trunk_queries ? 1 : 0;
     return from_hip(gdn::launch_attention(d, o_dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_fork_attention(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                       int n_req, const int32_t *branch_cu, const int32_t *branch_parent,
+                       int n_branch, int n_tokens, int H, int H_kv, int d, float scale,
+                       int trunk_queries, void *o, int io_dtype, int o_dtype, void *workspace,
+                       size_t ws_bytes, void *stream) {
+    const int st = attention_common(q, k, v, cu_seqlens, n_req, branch_cu, branch_parent,
+                                    n_branch, n_tokens, H, H_kv, d, scale, trunk_queries, o,
+                                    io_dtype, o_dtype);
+    if (st != GDN_OK) return st;
+    if (!workspace || ws_bytes < gdn::attention_workspace_bytes(n_req, n_branch))
+        return GDN_ERR_WORKSPACE;
+    return attention_launch(q, k, v, cu_seqlens, n_req, branch_cu, branch_parent, n_branch,
+                            n_tokens, H, H_kv, d, scale, trunk_queries, o, o_dtype, workspace,
+                            stream);
+}
+
+int gdn_fork_attention_noalloc(const void *q, const void *k, const void *v,
+                               const int32_t *cu_seqlens, int n_req, const int32_t *branch_cu,
+                               const int32_t *branch_parent, int n_branch, int n_tokens, int H,
+                               int H_kv, int d, float scale, int trunk_queries, void *o,
+                               int io_dtype, int o_dtype, void *stream) {
+    const int st = attention_common(q, k, v, cu_seqlens, n_req, branch_cu, branch_parent,
+                                    n_branch, n_tokens, H, H_kv, d, scale, trunk_queries, o,
+                                    io_dtype, o_dtype);
+    if (st != GDN_OK) return st;
+    if ((long long)n_req + n_branch > gdn::kAttnScratchSegments) return GDN_ERR_WORKSPACE;
+    // the tile table is the current device's copy of the file-scope array:
+    // the stream must belong to that device
+    int cur = 0;
+    hipDevice_t sdev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return from_hip(e);
+    if (sdev != cur) return GDN_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    e = gdn::attention_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess) return from_hip(e);
+    if (ws_bytes < gdn::attention_workspace_bytes(n_req, n_branch)) return GDN_ERR_WORKSPACE;
+    return attention_launch(q, k, v, cu_seqlens, n_req, branch_cu, branch_parent, n_branch,
+                            n_tokens, H, H_kv, d, scale, trunk_queries, o, o_dtype, ws, stream);
 }
 
 int gdn_stream_probe(const void *src, void *dst, size_t n_bytes, int mode, void *stream) {

@@ -42,6 +42,8 @@
 // matrix cores (P = P_hi + P_lo to about 2^-17), since one bf16 rounding
 // of P (2^-9 relative) would not hold a 2e-3 end-to-end tolerance.
 
+#include <mutex>
+
 #include "attention_launch.hpp"
 #include "gdn_device.hpp"
 
@@ -474,6 +476,37 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
 
 size_t attention_workspace_bytes(int n_req, int n_branch) {
     return sizeof(int32_t) * ((size_t)n_req + (size_t)n_branch + 1);
+}
+
+// Tile table of the allocation-free entry point: one file-scope device array
+// that every GPU the library runs on holds from module load to process end.
+// In host code `scratch` names a host-side stand-in, not device memory, so
+// host code only ever uses the per-device address hipGetSymbolAddress
+// returns for it (kept in g_scratch_ptr below).
+static __device__ __align__(256) int32_t scratch[kAttnScratchSegments + 1];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device: the address of its copy of `scratch`
+}  // namespace
+
+hipError_t attention_scratch(void **ptr, size_t *bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // once per device, with that device current: its copy's address
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
 }
 
 hipError_t launch_attention(int d, int out, const AttnArgs &a, hipStream_t stream) {

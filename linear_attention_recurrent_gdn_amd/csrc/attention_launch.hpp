@@ -22,6 +22,14 @@ struct AttnArgs {
 };
 
 size_t attention_workspace_bytes(int n_req, int n_branch);
+
+// Segments (n_req + n_branch) the allocation-free entry point's file-scope
+// tile table holds.
+constexpr int kAttnScratchSegments = 65536;
+
+// The calling thread's current device's copy of that table (its address is
+// looked up once per device, with the device current) and its size in bytes.
+hipError_t attention_scratch(void **ptr, size_t *bytes);
 hipError_t launch_attention(int d, int out, const AttnArgs &a, hipStream_t stream);
 
 }  // namespace gdn

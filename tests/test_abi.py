@@ -169,6 +169,28 @@ def test_fork_attention_validation_and_workspace(lib):
     assert call(ws_bytes=need - 1) == WORKSPACE
 
 
+def test_fork_attention_noalloc_validation(lib):
+    """Host-side checks run before any HIP call, including the bound on the
+    static tile table (n_req + n_branch)."""
+    from linear_attention_recurrent_gdn_amd import _lib
+    cap = _lib.FORK_ATTENTION_NOALLOC_MAX_SEGMENTS
+    text = open(HEADER).read()
+    assert f"#define GDN_FORK_ATTENTION_NOALLOC_MAX_SEGMENTS {cap}" in text
+
+    def call(q=FAKE, cu=FAKE, n_req=2, nb=5, H=8, Hkv=2, d=128, scale=0.1, io=1, out=0):
+        return lib.gdn_fork_attention_noalloc(q, FAKE, FAKE, cu, n_req, FAKE, FAKE, nb, 100, H,
+                                              Hkv, d, scale, 1, FAKE, io, out, NULL)
+    assert call(q=NULL) == INVALID
+    assert call(cu=NULL) == INVALID
+    assert call(Hkv=3) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(nb=-1) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(io=0) == UNSUPPORTED
+    assert call(n_req=cap, nb=1) == WORKSPACE       # one segment past the table
+    assert call(n_req=cap // 2, nb=cap - cap // 2 + 7) == WORKSPACE
+
+
 def test_stream_probe_validation(lib):
     assert lib.gdn_stream_probe(NULL, FAKE, 1024, 0, NULL) == INVALID
     assert lib.gdn_stream_probe(FAKE, NULL, 1024, 1, NULL) == INVALID
