@@ -181,7 +181,8 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
     win = torch.empty((R, 3, cc), device=dev, dtype=torch.bfloat16)
     o_p = torch.empty((Np, H, d), device=dev)
     o_b = torch.empty((Nb, H, d), device=dev)
-    ws = torch.empty(max(gdn.prefill_workspace_bytes(max(Np, Nb), max(R, NB), H, d, d), 1),
+    ws = torch.empty(max(gdn.prefill_workspace_bytes(max(Np, Nb), max(R, NB), H, d, d,
+                                                      variant=variant), 1),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 

@@ -79,11 +79,17 @@ int gdn_last_hip_error(void);
 int gdn_max_log_capacity(void);
 
 /* ------------------------------------------------------------------ prefill
- * Workspace bytes gdn_prefill_shared / gdn_fork_branches need for a stream
- * of at most n_tokens tokens in n_seq sequences.
+ * Workspace bytes gdn_prefill_shared / gdn_prefill_checkpointed /
+ * gdn_fork_branches need for a stream of at most n_tokens tokens in n_seq
+ * sequences with the given variant: a 256-byte-aligned table of n_seq + 1
+ * int32, then one record per (chunk, head) for at most
+ * n_tokens / 64 + n_seq chunks -- 25 KiB per chunk-head with GDN_SCALAR
+ * (400 bytes per token-head at d_k = 128), 25 KiB + 12 * 64 * d_k bytes
+ * per chunk-head with the per-key variants. Returns 0 for arguments the
+ * calls reject (negative sizes, H < 1, widths not 32/64/128, bad variant).
  */
 size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k,
-                                   int d_v, int chunk);
+                                   int d_v, int chunk, int variant);
 
 /*
  * gdn_prefill_shared -- call 1 of the two-call fork ([FL] method step 2):
@@ -130,7 +136,8 @@ size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k,
  *               32 return GDN_ERR_UNSUPPORTED and any other value
  *               GDN_ERR_INVALID_ARG
  *  variant      GDN_SCALAR, GDN_KDA or GDN_RWKV6
- *  workspace    >= gdn_prefill_workspace_bytes(n_tokens, n_seq, ...) bytes
+ *  workspace    >= gdn_prefill_workspace_bytes(n_tokens, n_seq, ..., variant)
+ *               bytes
  * Errors: INVALID_ARG (NULL required pointer, n_seq < 0, n_tokens < 0,
  * H < 1, bad dtype or variant, chunk not 16/32/64), UNSUPPORTED (d_k or
  * d_v not 32/64/128, chunk 16 or 32), WORKSPACE, HIP.

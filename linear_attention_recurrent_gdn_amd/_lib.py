@@ -29,7 +29,7 @@ SIGNATURES = {
     "gdn_status_string": (ctypes.c_char_p, [_I]),
     "gdn_last_hip_error": (_I, []),
     "gdn_max_log_capacity": (_I, []),
-    "gdn_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
+    "gdn_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "gdn_prefill_shared": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P,
                                 _P, _P, _P, _I, _I, _I, _P, _S, _P]),
     "gdn_prefill_checkpointed": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I,
@@ -189,12 +189,13 @@ def deltalog_merge(base, log_u, log_k, log_lambda, log_len, min_len=1, slot_idx=
 
 
 # ------------------------------------------------------------------ prefill / fork
-def prefill_workspace_bytes(n_tokens, n_seq, H, dk, dv, chunk=64):
-    return int(load().gdn_prefill_workspace_bytes(n_tokens, n_seq, H, dk, dv, chunk))
+def prefill_workspace_bytes(n_tokens, n_seq, H, dk, dv, chunk=64, variant="gdn"):
+    return int(load().gdn_prefill_workspace_bytes(n_tokens, n_seq, H, dk, dv, chunk,
+                                                  _variant(variant)))
 
 
-def _workspace(n_tokens, n_seq, H, dk, dv, chunk, device, workspace):
-    need = prefill_workspace_bytes(n_tokens, n_seq, H, dk, dv, chunk)
+def _workspace(n_tokens, n_seq, H, dk, dv, chunk, device, workspace, variant):
+    need = prefill_workspace_bytes(n_tokens, n_seq, H, dk, dv, chunk, variant)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     return workspace, need
@@ -216,7 +217,7 @@ def gdn_prefill_shared(q, k, v, log_alpha, beta, cu_seqlens, final_state, o=None
     R = cu_seqlens.shape[0] - 1
     cc = H * (2 * dk + dv)
     io = _io_code(q)
-    ws, _ = _workspace(N, R, H, dk, dv, chunk, q.device, workspace)
+    ws, _ = _workspace(N, R, H, dk, dv, chunk, q.device, workspace, variant)
     st = load().gdn_prefill_shared(
         _dev(q, "q", q.dtype, (N, H, dk)), _dev(k, "k", q.dtype, (N, H, dk)),
         _dev(v, "v", q.dtype, (N, H, dv)),
@@ -248,7 +249,7 @@ def gdn_prefill_checkpointed(q, k, v, log_alpha, beta, cu_seqlens, final_state, 
     cap = ckpt_state.shape[1]
     cc = H * (2 * dk + dv)
     io = _io_code(q)
-    ws, _ = _workspace(N, R, H, dk, dv, chunk, q.device, workspace)
+    ws, _ = _workspace(N, R, H, dk, dv, chunk, q.device, workspace, variant)
     st = load().gdn_prefill_checkpointed(
         _dev(q, "q", q.dtype, (N, H, dk)), _dev(k, "k", q.dtype, (N, H, dk)),
         _dev(v, "v", q.dtype, (N, H, dv)),
@@ -280,7 +281,7 @@ def gdn_fork_branches(q, k, v, log_alpha, beta, branch_cu, branch_parent, parent
     R = parent_state.shape[0]
     cc = H * (2 * dk + dv)
     io = _io_code(q)
-    ws, _ = _workspace(N, NB, H, dk, dv, chunk, q.device, workspace)
+    ws, _ = _workspace(N, NB, H, dk, dv, chunk, q.device, workspace, variant)
     st = load().gdn_fork_branches(
         _dev(q, "q", q.dtype, (N, H, dk)), _dev(k, "k", q.dtype, (N, H, dk)),
         _dev(v, "v", q.dtype, (N, H, dv)),

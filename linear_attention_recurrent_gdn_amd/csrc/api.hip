@@ -143,9 +143,11 @@ int deltalog_merge(float *base, const float *log_u, const void *log_k, const flo
                                        static_cast<hipStream_t>(stream)));
 }
 
-size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k, int d_v, int chunk) {
-    if (n_tokens < 0 || n_seq < 0 || H < 1 || chunk < 1) return 0;
-    return gdn::prefill_workspace_bytes(n_tokens, n_seq, H, d_k, d_v, chunk);
+size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k, int d_v, int chunk,
+                                   int variant) {
+    if (n_tokens < 0 || n_seq < 0 || H < 1 || chunk < 1 || !variant_ok(variant)) return 0;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return 0;
+    return gdn::prefill_workspace_bytes(n_tokens, n_seq, H, d_k, d_v, chunk, variant);
 }
 
 static int prefill_common(const void *q, const void *k, const void *v, const float *log_alpha,
@@ -164,7 +166,8 @@ static int prefill_common(const void *q, const void *k, const void *v, const flo
     if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_INVALID_ARG;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return GDN_ERR_UNSUPPORTED;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
-    const size_t need = gdn::prefill_workspace_bytes(n_tokens, n_seq, H, d_k, d_v, chunk);
+    const size_t need =
+        gdn::prefill_workspace_bytes(n_tokens, n_seq, H, d_k, d_v, chunk, variant);
     if (need > 0 && (!workspace || ws_bytes < need)) return GDN_ERR_WORKSPACE;
     gdn::PrefillArgs a{};
     a.q = q;

@@ -112,7 +112,7 @@ struct PrefillArgs {
 };
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,
-                               int chunk);
+                               int chunk, int variant);
 hipError_t launch_prefill(int dk, int dv, int io, int out, const PrefillArgs &a,
                           hipStream_t stream);
 

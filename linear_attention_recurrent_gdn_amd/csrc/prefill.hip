@@ -13,10 +13,11 @@ hipError_t launch_prefill_dk64(int dv, int io, int out, const PrefillArgs &a,
 hipError_t launch_prefill_dk128(int dv, int io, int out, const PrefillArgs &a,
                                 hipStream_t stream);
 
-size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv, int chunk) {
+size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv, int chunk,
+                               int variant) {
     (void)chunk;
     (void)dv;
-    return ws_layout(n_tokens, n_seq, H, dk).total;
+    return ws_layout(n_tokens, n_seq, H, dk, variant != kScalar).total;
 }
 
 hipError_t launch_prefill(int dk, int dv, int io, int out, const PrefillArgs &a,

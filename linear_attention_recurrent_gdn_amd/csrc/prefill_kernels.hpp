@@ -119,40 +119,51 @@ __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
 }
 
 // ------------------------------------------------------------ workspace
-// Per (chunk, head) record of bf16 hi / lo planes, split once by the prep
-// kernel for the scan:
-//   T'  [C][C], P [C][C]              A operands, in fragment order (frag_off)
-//   K, Q [C][d_k]                     the conv'd, normalised chunk rows (A
-//                                     operands, fragment order)
-//   K~^T [d_k][C]                     exp(g_L - g_r) k_r, transposed (B operand)
-//   fp32 slot of max(d_k, C) floats   scalar decay: gamma_r = exp(g_r) per row;
-//                                     per key: exp(g_L) per key column
-// A-operand planes are stored in the order the 16x16x32 MFMA reads them:
-// the 16-row x 32-column block (w, ks) of a plane is 1 KiB contiguous, lane
-// l's 8 values (row w*16 + l%16, columns ks*32 + (l/16)*8 ..) at element
-// frag_off(nks, w, ks, l), nks = columns / 32. A wave's operand load then
-// covers 8 whole 128-byte lines instead of 16 half lines.
+// Per (chunk, head) record written by the prep kernel for the scan, split
+// once here into hi / lo bf16 planes:
+//   T', P  [C][C] lower triangular, only their 16 x 32 blocks at or below
+//          the diagonal, in the order the 16x16x32 MFMA reads an A operand
+//          (tri_off)
+//   fp32 slot of 4C floats: scalar decay -- per row r the factors the scan
+//          applies to its MFMA rows, gamma_r (for K Sig0 and Q Sig0) and
+//          e^{g_L - g_r} (for the state update), then gamma_L; per-key decay
+//          -- e^{g_L} per key column
+//   K, Q   [C][d_k] the conv'd, normalised chunk rows (per-key decay: the
+//          decayed K^ = K . e^{g}, Q^ = Q . e^{g}), A operands in fragment
+//          order (frag_off)
+//   per-key decay only: K~^T [d_k][C] = (k_r . e^{g_L - g_r})^T (B operand
+//          rows); with a scalar decay the scan forms K^T itself from K
+// 89 KiB per chunk-head with a scalar decay at d_k = 128 (1.4 KiB per
+// token-head), 105 KiB per key.
+//
+// Fragment order: the 16-row x 32-column block (w, ks) of a plane is 1 KiB
+// contiguous, lane l's 8 values (row w*16 + l%16, columns ks*32 + (l/16)*8
+// ..) at element frag_off(nks, w, ks, l), nks = columns / 32. A wave's
+// operand load then covers 8 whole 128-byte lines instead of 16 half lines.
 __host__ __device__ constexpr int frag_off(int nks, int w, int ks, int lane) {
     return ((w * nks + ks) * kWave + lane) * 8;
 }
 
+// Lower-triangular C x C planes keep the blocks (w, kq) with
+// kq <= (16 w + 15) / 32: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+constexpr int kTriBlocks = 6;
+__host__ __device__ constexpr int tri_block(int w, int kq) { return w < 2 ? w : 2 * w - 2 + kq; }
+__host__ __device__ constexpr int tri_off(int w, int kq, int lane) {
+    return (tri_block(w, kq) * kWave + lane) * 8;
+}
+constexpr int kTriElems = kTriBlocks * kWave * 8;  // bf16 per plane
+constexpr int kFacFloats = 4 * C;                 // the fp32 slot
+static_assert(kFacFloats >= 128, "the slot holds e^{g_L} of every key");
+
 struct RecLayout {
-    size_t thi, tlo, phi, plo, khi, klo, qhi, qlo, kthi, ktlo, egl, elems;
+    size_t thi, tlo, phi, plo, fac, khi, klo, qhi, qlo, kthi, ktlo, elems;
 };
 
-__host__ __device__ constexpr RecLayout rec_layout(int dk) {
-    return RecLayout{0,
-                     (size_t)C * C,
-                     2 * (size_t)C * C,
-                     3 * (size_t)C * C,
-                     4 * (size_t)C * C,
-                     4 * (size_t)C * C + (size_t)C * dk,
-                     4 * (size_t)C * C + 2 * (size_t)C * dk,
-                     4 * (size_t)C * C + 3 * (size_t)C * dk,
-                     4 * (size_t)C * C + 4 * (size_t)C * dk,
-                     4 * (size_t)C * C + 5 * (size_t)C * dk,
-                     4 * (size_t)C * C + 6 * (size_t)C * dk,
-                     4 * (size_t)C * C + 6 * (size_t)C * dk + 2 * (size_t)(dk > C ? dk : C)};
+__host__ __device__ constexpr RecLayout rec_layout(int dk, bool per_key) {
+    const size_t t = kTriElems, k0 = 4 * t + 2 * (size_t)kFacFloats, cd = (size_t)C * dk;
+    return RecLayout{0,      t,           2 * t,       3 * t,       4 * t,
+                     k0,     k0 + cd,     k0 + 2 * cd, k0 + 3 * cd, k0 + 4 * cd,
+                     k0 + 5 * cd, k0 + (per_key ? 6 : 4) * cd};
 }
 
 struct WsLayout {
@@ -162,11 +173,11 @@ struct WsLayout {
     size_t total;
 };
 
-__host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H, int dk) {
+__host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H, int dk, bool per_key) {
     WsLayout w{};
     w.max_chunks = (size_t)n_tokens / C + (size_t)n_seq;
     w.rec_off = ((sizeof(int32_t) * ((size_t)n_seq + 1)) + 255) & ~size_t(255);
-    w.rec_elems = rec_layout(dk).elems;
+    w.rec_elems = rec_layout(dk, per_key).elems;
     w.total = w.rec_off + sizeof(__bf16) * w.rec_elems * w.max_chunks * (size_t)H;
     return w;
 }
@@ -307,7 +318,7 @@ struct RawRows {
 template <int D, typename TI>
 __device__ __forceinline__ void rows_load(const TI *x, int H, int h, const ChunkSrc<TI> &cs,
                                           int rb, int CC, int cwin, bool conv,
-                                          RawRows<D, TI> &rr) {
+                                          RawRows<D, TI> &rr, int ks0 = 0, int ks1 = D / 32) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x % kWave;
     const int i = lane % 16;
@@ -315,7 +326,8 @@ __device__ __forceinline__ void rows_load(const TI *x, int H, int h, const Chunk
     const int row = rb * RB + i;
     const TI *own_p = x + (size_t)(cs.seq0 + cs.p0 + min(row, cs.L - 1)) * H * D + (size_t)h * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw_load(own_p + ks * 32 + cq, rr.own[ks]);
+    for (int ks = 0; ks < KS; ++ks)
+        if (ks >= ks0 && ks < ks1) raw_load(own_p + ks * 32 + cq, rr.own[ks]);
     if (conv) {
         // halo rows (lanes 13..15): stream position ph, or window row 3 + ph.
         // A block with no live row may put ph past the sequence: clamp it (a
@@ -329,14 +341,17 @@ __device__ __forceinline__ void rows_load(const TI *x, int H, int h, const Chunk
                 hp = cs.win + (size_t)(3 + max(ph, -3)) * CC + cwin;
         }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) raw_load(hp + ks * 32 + cq, rr.halo[ks]);
+        for (int ks = 0; ks < KS; ++ks)
+            if (ks >= ks0 && ks < ks1) raw_load(hp + ks * 32 + cq, rr.halo[ks]);
     }
 }
 
+// With norm the rows are scaled to unit length and, if inv is given, the
+// scale 1 / sqrt(sum y^2 + eps) of this lane's row is returned there.
 template <int D, typename TI>
 __device__ __forceinline__ void rows_compute(RawRows<D, TI> &rr, const ChunkSrc<TI> &cs, int rb,
                                              const float *s_w, bool norm,
-                                             float (&out)[D / 32][8]) {
+                                             float (&out)[D / 32][8], float *inv_out = nullptr) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x % kWave;
     const int i = lane % 16;
@@ -394,6 +409,9 @@ __device__ __forceinline__ void rows_compute(RawRows<D, TI> &rr, const ChunkSrc<
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[ks][e] *= inv;
+        if (inv_out) *inv_out = inv;
+    } else if (inv_out) {
+        *inv_out = 1.f;
     }
 }
 
@@ -460,8 +478,8 @@ __device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], 
 // Rows x C matrix staged in LDS (rows padded to C + 1 floats) -> hi / lo
 // bf16 planes of the record, 8 elements (16 bytes) per store: row-major
 // [rows][C], or in A-fragment order (FRAG: a lower-triangular C x C matrix,
-// T' or P, whose 16 x 32 blocks above the diagonal are all zero; the scan
-// never reads them, so they are not written).
+// T' or P, of which only the 16 x 32 blocks at or below the diagonal are
+// kept, tri_off).
 template <int ROWS, bool FRAG = false>
 __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 *lo) {
     constexpr int G = C / 8;  // 8-element groups per row
@@ -472,7 +490,7 @@ __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = src[r * (C + 1) + c0 + e];
         const Split8 sp = split8(x);
-        const int off = FRAG ? frag_off(C / 32, r / 16, c0 / 32, r % 16 + 16 * ((c0 % 32) / 8))
+        const int off = FRAG ? tri_off(r / 16, c0 / 32, r % 16 + 16 * ((c0 % 32) / 8))
                              : r * C + c0;
         *reinterpret_cast<bf16x8 *>(hi + off) = sp.hi;
         *reinterpret_cast<bf16x8 *>(lo + off) = sp.lo;
@@ -515,10 +533,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
                     (a.win_in && src_ok) ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC
                                          : nullptr};
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK);
-    constexpr RecLayout RL = rec_layout(DK);
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK, kPerKey);
+    constexpr RecLayout RL = rec_layout(DK, kPerKey);
     __bf16 *rec = reinterpret_cast<__bf16 *>(static_cast<char *>(a.ws) + wl.rec_off) +
                   ((size_t)gc * H + h) * wl.rec_elems;
+    float *const fac = reinterpret_cast<float *>(rec + RL.fac);
 
     const bool conv = a.conv_w != nullptr;
     if (conv) {
@@ -536,7 +555,6 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     if constexpr (!kPerKey) {
         g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
         gL = __shfl(g, C - 1, kWave);
-        if (w == 0) reinterpret_cast<float *>(rec + RL.egl)[lane] = expf(g);  // gamma_r for the scan
     } else {
         // log a of this lane's row (rows >= L add nothing), then an inclusive
         // scan over the wave's 16 rows (DPP within 16-lane rows) plus the
@@ -579,7 +597,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww) total += s_gt[ww * DK + tid];
             s_gl[tid] = total;
-            reinterpret_cast<float *>(rec + RL.egl)[tid] = expf(total);
+            fac[tid] = expf(total);
         }
         __syncthreads();
     }
@@ -587,9 +605,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     if constexpr (kDelta) b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
     b_l = lane < cs.L ? b_l : 0.f;
 
-    // conv'd, normalised Q and K rows; their split A operands go to the
-    // record. With a scalar decay the raw Q and K rows are requested
-    // together (the per-key form has no registers to spare for that).
+    // conv'd, normalised Q and K rows (per key: decayed); their split A
+    // operands go to the record. With a scalar decay the raw Q and K rows
+    // are requested together (the per-key form has no registers to spare).
     Split8 qa[DK / 32], ka[DK / 32];
     RawRows<DK, TI> rk;
     const auto load_k = [&] {
@@ -616,6 +634,14 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     if constexpr (kPerKey) load_k();
     float kf[DK / 32][8];
     rows_compute<DK, TI>(rk, cs, w, conv ? s_wk : nullptr, a.qk_norm != 0, kf);
+    if constexpr (!kPerKey) {
+        // the scan's row factors: gamma_r, e^{g_L - g_r}, and gamma_L
+        if (w == 0) {
+            fac[lane] = expf(g);
+            fac[C + lane] = expf(gL - g);
+        }
+        if (tid == 0) fac[2 * C] = expf(gL);
+    }
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
         // A operand of KK^T and the scan's K Sig term: K (scalar decay), K^
@@ -634,9 +660,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             }
         }
         ka[ks] = split8(ak);
-        const int off = frag_off(KS, w, ks, lane);
-        *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
-        *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
+        {
+            const int off = frag_off(KS, w, ks, lane);
+            *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
+            *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
+        }
 #pragma unroll
         for (int e = 0; e < 8; e += 4)  // 16-byte LDS stores (KP, cq keep them aligned)
             *reinterpret_cast<float4 *>(s_k + row * KP + ks * 32 + cq + e) =
@@ -678,17 +706,15 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     }
     __syncthreads();  // s_A complete; the K rows in s_k are no longer needed
 
-    // K~^T[d][r] = exp(g_L - g_r) k_r[d], staged transposed for coalesced stores
-    {
-        const float f = kPerKey ? 1.f : expf(gL - __shfl(g, row, kWave));
+    if constexpr (kPerKey) {
+        // K~^T[d][r] = k_r[d] e^{g_L - g_r}, staged transposed for coalesced stores
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                s_k[(ks * 32 + cq + e) * (C + 1) + row] = kPerKey ? kf[ks][e] : kf[ks][e] * f;
+            for (int e = 0; e < 8; ++e) s_k[(ks * 32 + cq + e) * (C + 1) + row] = kf[ks][e];
+        __syncthreads();
+        put_planes<DK>(s_k, rec + RL.kthi, rec + RL.ktlo);
     }
-    __syncthreads();
-    put_planes<DK>(s_k, rec + RL.kthi, rec + RL.ktlo);
 
     // T = (I + A)^-1, one column per group of 4 lanes (columns are
     // independent): lane (col, part) keeps T[j][col] for j = part (mod 4),
@@ -708,7 +734,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             default: tri_solve<48, AP>(arow, t, col, part); break;
         }
     }
-    __syncthreads();  // every lane is done with the K~^T copy-out from s_k
+    __syncthreads();  // every lane is done with s_k (the per-key K~^T copy-out)
     // P (from registers) and T'[j][col] = T[j][col] beta_col, staged side by
     // side in s_k for coalesced stores
     float *const s_P = s_k, *const s_T = s_k + C * (C + 1);
@@ -795,17 +821,57 @@ template <> struct VPair<float> {
 // lane holds are adjacent in memory (one load / store per row for both).
 __device__ __forceinline__ int vcol(int c) { return 2 * (c % 16) + c / 16; }
 
+// K^T [d_k][C] in LDS for the scalar-decay state update, formed from the
+// K operands of the chunk record. Rows (key d) hold C = 64 bf16 (128 bytes:
+// eight 16-byte pieces of 8 consecutive chunk rows); the piece index is
+// XOR-swizzled by the key so that the writes (one bf16 per store from the
+// A-operand layout: a lane's chunk row r, 8 keys, 8 apart across the 16-lane
+// groups) and the 16-byte B-operand reads (a lane's key, 8 consecutive
+// chunk rows; 16 consecutive keys per 16 lanes) spread over the banks.
+__device__ __forceinline__ int kt_off(int d, int r) {
+    const int sw = ((d >> 1) & 7) ^ (((d >> 4) & 1) << 1);
+    return d * C + ((((r >> 3) ^ sw) & 7) << 3) + (r & 7);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The 8 split values of a lane's A-operand piece (chunk row r, keys d0 ..
+// d0 + 7, d0 a multiple of 8) into the K^T planes, one bf16 per store (the
+// halves of each 32-bit word are written from the word itself). For such d0
+// the swizzle of key d0 + e is sw(d0) ^ (e >> 1), so the 8 stores of a plane
+// use 4 base offsets and constant displacements.
+__device__ __forceinline__ void put_kt(const Split8 &x, int d0, int r, __bf16 *kh, __bf16 *kl) {
+    const u32x4 h = __builtin_bit_cast(u32x4, x.hi);
+    const u32x4 l = __builtin_bit_cast(u32x4, x.lo);
+    const int sw = ((d0 >> 1) & 7) ^ (((d0 >> 4) & 1) << 1);
+    const int X = ((r >> 3) ^ sw) & 7, base = d0 * C + (r & 7);
+    uint16_t *ph = reinterpret_cast<uint16_t *>(kh) + base;
+    uint16_t *pl = reinterpret_cast<uint16_t *>(kl) + base;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // keys d0 + 2q, d0 + 2q + 1: slot X ^ q
+        const int o = ((X ^ q) << 3) + 2 * q * C;
+        ph[o] = (uint16_t)(h[q] & 0xffffu);
+        ph[o + C] = (uint16_t)(h[q] >> 16);
+        pl[o] = (uint16_t)(l[q] & 0xffffu);
+        pl[o + C] = (uint16_t)(l[q] >> 16);
+    }
+}
+
 template <int KS, int NVT, typename TI>
 struct ChunkRegs {
     static_assert(NVT == 2, "a lane holds one adjacent pair of value columns");
     Split8 ka[KS], qa[KS], ta[2], pa[2];
     typename VPair<TI>::type vraw[7];  // raw V rows r0-3 .. r0+3 of this lane's column pair
-    float4 gam;       // scalar decay: gamma of this lane's 4 rows (C/D layout)
+    f32x4v gam;       // scalar decay: gamma_r of this lane's 4 rows (C/D layout)
+    f32x4v gu;        // scalar decay: e^{g_L - g_r} of the same rows
     float gaml;       // scalar decay: gamma_L
 };
 
-// PK: per-key decay (K and Q arrive pre-scaled, gamma = 1; the state decays
-// by e^{g_L} per key column, staged in LDS with the chunk's K~^T planes).
+// PK: per-key decay (K and Q arrive decayed, gamma = 1; the state decays by
+// e^{g_L} per key column, staged in LDS with the chunk's K~^T planes, which
+// the record holds). Scalar decay: K^T is formed in LDS from the chunk's K
+// operands and the update takes W = diag(e^{g_L - g}) U, since
+// K~^T U = K^T W.
 // CK: also write checkpoints (state and window every ckpt_every chunks);
 // a separate instance so the plain scan keeps its register budget.
 template <int DK, int DV, typename TI, typename TO, bool PK, bool CK>
@@ -818,13 +884,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int NEG = NFT / kWaves;    // state-update tiles per wave
     static_assert(NFT % kWaves == 0, "state-update tiles split evenly over the waves");
     static_assert(DK / 4 <= kWave, "e^{g_L} row fits one wave's 16-byte copies");
-    constexpr RecLayout RL = rec_layout(DK);
-    // Sig^T tile [TV][DK] in fp32; R^T and U^T [TV][C] as hi / lo bf16
-    // planes (split once when written); K~^T [DK][C] hi / lo planes copied
-    // from the chunk record by direct-to-LDS loads (swizzled rows).
+    constexpr RecLayout RL = rec_layout(DK, PK);
+    // Sig^T tile [TV][DK] in fp32; R^T, U^T (and, scalar decay, W^T) [TV][C]
+    // as hi / lo bf16 planes (split once when written); K~^T (per key:
+    // copied from the chunk record by direct-to-LDS loads, swizzled rows) or
+    // K^T (scalar decay: formed from the K operands, kt_off) [DK][C] hi / lo.
     __shared__ __attribute__((aligned(16))) float s_St[TV * SP];
     __shared__ __attribute__((aligned(16))) __bf16 s_Rh[TV * CB], s_Rl[TV * CB];
     __shared__ __attribute__((aligned(16))) __bf16 s_Uh[TV * CB], s_Ul[TV * CB];
+    __shared__ __attribute__((aligned(16))) __bf16 s_Wh[PK ? 8 : TV * CB], s_Wl[PK ? 8 : TV * CB];
     __shared__ __attribute__((aligned(16))) __bf16 s_Kh[DK * C], s_Kl[DK * C];
     __shared__ __attribute__((aligned(16))) float s_wv[TV * 4];
     __shared__ __attribute__((aligned(16))) __bf16 s_eg[PK ? 2 * DK : 8];  // e^{g_L}, fp32 bits
@@ -839,7 +907,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int j0 = tile * TV;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK);
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK, PK);
     const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
     const int src = a.parent ? a.parent[s] : s;
     const bool src_ok = src >= 0 && src < a.n_parent;
@@ -867,7 +935,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // across the o stores and would reload them behind a full wait
     const int cs0 = chunk_start[s];
     const int nchunks = chunk_start[s + 1] - cs0;  // <= ceil(len / C)
-    const TI *vs = static_cast<const TI *>(a.v);
+    // the q / k / v base pointers as locals: every load below indexes one of
+    // them directly (a pointer chosen between them would keep them in
+    // private memory, and loads through it would be flat loads)
+    const TI *const qs = static_cast<const TI *>(a.q);
+    const TI *const ks_ = static_cast<const TI *>(a.k);
+    const TI *const vs = static_cast<const TI *>(a.v);
     const int cwin_v = 2 * H * DK + h * DV;
 
     // the state tile [DK][TV] of this workgroup (Sig^T in s_St) into a
@@ -892,23 +965,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int idx = tid; idx < 3 * W; idx += kThreads) {
             const int r = idx / W, wc = idx % W;
             const int p = end - 3 + r;
-            int cch;
-            const TI *xs;
-            size_t col, stride;
-            if (wc < DK) {
-                cch = h * DK + wc; xs = static_cast<const TI *>(a.q);
-                col = (size_t)h * DK + wc; stride = (size_t)H * DK;
-            } else if (wc < 2 * DK) {
-                cch = H * DK + h * DK + (wc - DK); xs = static_cast<const TI *>(a.k);
-                col = (size_t)h * DK + (wc - DK); stride = (size_t)H * DK;
-            } else {
-                cch = 2 * H * DK + h * DV + (wc - 2 * DK); xs = static_cast<const TI *>(a.v);
-                col = (size_t)h * DV + (wc - 2 * DK); stride = (size_t)H * DV;
+            const int part = wc < DK ? 0 : wc < 2 * DK ? 1 : 2;  // q, k or v
+            const int i = wc - part * DK;
+            const int cch = part == 2 ? 2 * H * DK + h * DV + i : part * H * DK + h * DK + i;
+            TI val = from_f32<TI>(0.f);
+            if (p >= 0) {
+                const size_t row = (size_t)(sp.start + p);
+                if (part == 0) val = qs[row * H * DK + (size_t)h * DK + i];
+                else if (part == 1) val = ks_[row * H * DK + (size_t)h * DK + i];
+                else val = vs[row * H * DV + (size_t)h * DV + i];
+            } else if (win) {
+                val = win[(size_t)(3 + p) * CC + cch];
             }
-            TI val;
-            if (p >= 0) val = xs[(size_t)(sp.start + p) * stride + col];
-            else if (win) val = win[(size_t)(3 + p) * CC + cch];
-            else val = from_f32<TI>(0.f);
             wo[(size_t)r * CC + cch] = val;
         }
     };
@@ -942,7 +1010,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq)
             if (kq <= kmax) {
-                const int off = frag_off(C / 32, w, kq, lane);
+                const int off = tri_off(w, kq, lane);
                 r.ta[kq] = read_split8(rec + RL.thi + off, rec + RL.tlo + off);
                 if (want_o) r.pa[kq] = read_split8(rec + RL.phi + off, rec + RL.plo + off);
             }
@@ -958,17 +1026,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         if constexpr (PK) {
-            r.gam = make_float4(1.f, 1.f, 1.f, 1.f);
+            r.gam = f32x4v{1.f, 1.f, 1.f, 1.f};
+            r.gu = r.gam;
             r.gaml = 1.f;
         } else {
-            const float *gr = reinterpret_cast<const float *>(rec + RL.egl);
-            r.gam = *reinterpret_cast<const float4 *>(gr + r0v);
-            r.gaml = gr[C - 1];
+            const float *fac = reinterpret_cast<const float *>(rec + RL.fac);
+            r.gam = *reinterpret_cast<const f32x4v *>(fac + r0v);
+            r.gu = *reinterpret_cast<const f32x4v *>(fac + C + r0v);
+            r.gaml = fac[2 * C];
         }
     };
-    // K~^T hi / lo planes of chunk c into LDS (direct-to-LDS, 16 B per lane;
-    // the LDS position of a lane's bytes is fixed, so the swizzle is applied
-    // by choosing which global chunk each lane fetches)
+    // per key: K~^T hi / lo planes of chunk c into LDS (direct-to-LDS, 16 B
+    // per lane; the LDS position of a lane's bytes is fixed, so the swizzle
+    // is applied by choosing which global chunk each lane fetches)
     auto load_kt = [&](int c) {
         const __bf16 *rec = record(c);
         constexpr int PER_WAVE = DK * C * 2 / 16 / kThreads;  // 16-byte pieces per lane, per plane
@@ -982,7 +1052,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             lds_dma16(rec + RL.ktlo + r * C + chg * 8, s_Kl + lds0);
         }
         if constexpr (PK)  // DK floats: one 16-byte piece per lane of wave 0
-            if (w == 0 && lane < DK / 4) lds_dma16(rec + RL.egl + lane * 8, s_eg);
+            if (w == 0 && lane < DK / 4) lds_dma16(rec + RL.fac + lane * 8, s_eg);
     };
 
     // the first chunk's operands are requested before the incoming state
@@ -1000,11 +1070,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
         const ChunkRegs<KS, NVT, TI> cur = nxt;
-        load_kt(c);
+        if constexpr (PK) {
+            load_kt(c);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                put_kt(cur.ka[ks], ks * 32 + acol, w * RB + lane % 16, s_Kh, s_Kl);
+        }
 
         // gamma_r = exp(g_r) of this lane's rows, from the chunk record (the
         // prep kernel's running sums; rows >= L add nothing)
-        const float gam[4] = {cur.gam.x, cur.gam.y, cur.gam.z, cur.gam.w};
+        const f32x4v gam = cur.gam;
 
         // conv'd V entries of this lane (C/D layout), from the raw rows
         float vf[NVT][4];
@@ -1052,13 +1128,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const int ro = (t * 16 + lane % 16) * CB + r0v;
             split4_store(rv, s_Rh + ro, s_Rl + ro);
         }
-        // This wave's direct-to-LDS copies of K~^T are its only vector memory
-        // operations in flight here: finish them before this barrier (a
-        // workgroup fence would wait for them here anyway), so the whole
-        // plane is visible to every wave after it and the state update needs
-        // no barrier of its own. Sig^T is last read above (K Sig0, Q Sig0),
-        // so it may be rewritten by the state update after the next barrier.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // Per key, this wave's direct-to-LDS copies of K~^T are its only
+        // vector memory operations in flight here: finish them before this
+        // barrier (a workgroup fence would wait for them here anyway), so the
+        // whole plane is visible to every wave after it and the state update
+        // needs no barrier of its own. Sig^T is last read above (K Sig0,
+        // Q Sig0), so it may be rewritten by the state update after the next
+        // barrier.
+        if constexpr (PK) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
 
         // U = T' R
@@ -1073,6 +1150,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             const int uo = (t * 16 + lane % 16) * CB + r0v;
             split4_store(acc, s_Uh + uo, s_Ul + uo);
+            if constexpr (!PK) {  // W = diag(e^{g_L - g}) U for the state update
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] *= cur.gu[i];
+                split4_store(acc, s_Wh + uo, s_Wl + uo);
+            }
         }
         __syncthreads();
 
@@ -1104,7 +1186,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
 
-        // Sig^T <- gamma_L Sig^T + U^T K~   (tiles: value sub-tile x 16 keys)
+        // Sig^T <- gamma_L Sig^T + U^T K~ = gamma_L Sig^T + W^T K (scalar
+        // decay; per key: diag(e^{g_L}) Sig^T + U^T K~)   (tiles: value
+        // sub-tile x 16 keys)
         const float gamL = cur.gaml;
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
@@ -1119,8 +1203,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
                 const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
-                const int ok = kt_swz(dt * 16 + lane % 16, kq * 4 + lane / 16);
-                acc = mma3(read_split8(s_Uh + ou, s_Ul + ou), read_split8(s_Kh + ok, s_Kl + ok), acc);
+                const int ok = PK ? kt_swz(dt * 16 + lane % 16, kq * 4 + lane / 16)
+                                  : kt_off(dt * 16 + lane % 16, kq * 32 + acol);
+                acc = PK ? mma3(read_split8(s_Uh + ou, s_Ul + ou), read_split8(s_Kh + ok, s_Kl + ok), acc)
+                         : mma3(read_split8(s_Wh + ou, s_Wl + ou), read_split8(s_Kh + ok, s_Kl + ok), acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -1145,7 +1231,8 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
         else return prep_kernel_pk<DK, TI, VAR>;
     };
     if (a.n_seq == 0) return hipSuccess;
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK);
+    const bool pk = a.variant != kScalar;
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, pk);
     int32_t *chunk_start = static_cast<int32_t *>(a.ws);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq, a.n_tokens,
                        (long long)wl.max_chunks, chunk_start);
@@ -1166,18 +1253,20 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const size_t n_sh = (size_t)a.n_seq * a.H;
-    const unsigned blocks = (unsigned)(((n_sh + 7) / 8) * 8 * (DV / TV));  // see scan_unit
-    const bool pk = a.variant != kScalar;
+    const size_t sh_pad = (n_sh + 7) / 8 * 8;  // see scan_unit
     const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
-    auto scan = [&](auto pk_tag, auto ck_tag) {
-        hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, decltype(pk_tag)::value,
-                                        decltype(ck_tag)::value>),
-                           dim3(blocks), dim3(kThreads), 0, stream, a);
+    auto scan = [&](auto ck_tag) {
+        constexpr bool CK = decltype(ck_tag)::value;
+        const dim3 grid((unsigned)(sh_pad * (DV / TV)));
+        if (pk)
+            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, CK>), grid, dim3(kThreads), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, CK>), grid, dim3(kThreads), 0,
+                               stream, a);
     };
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    if (pk) ck ? scan(T_{}, T_{}) : scan(T_{}, F_{});
-    else ck ? scan(F_{}, T_{}) : scan(F_{}, F_{});
+    if (ck) scan(std::true_type{});
+    else scan(std::false_type{});
     return hipGetLastError();
 }
 

@@ -100,7 +100,8 @@ def test_merge_validation(lib):
 
 
 def test_prefill_validation_and_workspace(lib):
-    need = lib.gdn_prefill_workspace_bytes(1000, 3, 4, 128, 128, 64)
+    need = lib.gdn_prefill_workspace_bytes(1000, 3, 4, 128, 128, 64, 0)
+    assert lib.gdn_prefill_workspace_bytes(1000, 3, 4, 128, 128, 64, 1) > need  # per-key record
     assert need > 0
 
     def call(ws=FAKE, ws_bytes=need, chunk=64, final=FAKE, cu=FAKE, d=128, beta=FAKE,
