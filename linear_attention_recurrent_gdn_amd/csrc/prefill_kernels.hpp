@@ -295,7 +295,7 @@ __device__ __forceinline__ void raw_unpack(const Raw8<bf16> &r, float (&x)[8]) {
 // lane i <- lane (i - N) mod 16 of its 16-lane DPP row (row_ror:N)
 template <int N>
 __device__ __forceinline__ uint32_t ror16(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + N, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x120 + N, 0xf, 0xf, false);
 }
 
 // Conv'd (and, for q / k, normalised) rows rb*16 .. rb*16+15 of the chunk in
@@ -508,6 +508,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
     constexpr int SK = SK0 > 2 * C * (C + 1) ? SK0 : 2 * C * (C + 1);
     __shared__ __attribute__((aligned(16))) float s_k[SK];
+    // the split B operand rows of KK^T / QK^T [C][DK] hi / lo, in s_k's space
+    static_assert(C * DK <= SK, "split K rows fit s_k");
+    __bf16 *const s_bh = reinterpret_cast<__bf16 *>(s_k), *const s_bl = s_bh + C * DK;
     // A, strictly lower, rows of AP floats with each row's entries grouped by
     // j mod 4 (see a_idx), so the substitution reads them as float4
     constexpr int AP = C + 4;
@@ -665,15 +668,24 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
             *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
         }
-#pragma unroll
-        for (int e = 0; e < 8; e += 4)  // 16-byte LDS stores (KP, cq keep them aligned)
-            *reinterpret_cast<float4 *>(s_k + row * KP + ks * 32 + cq + e) =
-                make_float4(bk[e], bk[e + 1], bk[e + 2], bk[e + 3]);
+        // the B operand rows of KK^T and QK^T, split once, in fragment order:
+        // the reader of row block ct takes lane l's piece of wave ct
+        const Split8 bs = kPerKey ? split8(bk) : ka[ks];
+        const int off = frag_off(KS, w, ks, lane);
+        *reinterpret_cast<bf16x8 *>(s_bh + off) = bs.hi;
+        *reinterpret_cast<bf16x8 *>(s_bl + off) = bs.lo;
     }
     __syncthreads();
 
     // KK^T and QK^T tiles (w, ct), ct <= w, on MFMA; A to LDS, P kept in
-    // registers until s_k is free
+    // registers until s_k is free. g and beta of this lane's 4 rows are
+    // taken once.
+    float g_rr[4], b_rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        g_rr[i] = __shfl(g, w * RB + (lane / 16) * 4 + i, kWave);
+        b_rr[i] = __shfl(b_l, w * RB + (lane / 16) * 4 + i, kWave);
+    }
     float pv[C / RB][4];
 #pragma unroll
     for (int ct = 0; ct < C / RB; ++ct) {
@@ -681,9 +693,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         if (ct <= w) {
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
-                float bx[8];
-                lds_read8(s_k + (ct * RB + lane % 16) * KP + ks * 32 + cq, bx);
-                const Split8 bs = split8(bx);
+                const int off = frag_off(KS, ct, ks, lane);
+                const Split8 bs = read_split8(s_bh + off, s_bl + off);
                 kk = mma3(ka[ks], bs, kk);
                 qk = mma3(qa[ks], bs, qk);
             }
@@ -694,13 +705,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = w * RB + (lane / 16) * 4 + i;
-            const float g_r = __shfl(g, r, kWave);
-            const float b_r = __shfl(b_l, r, kWave);
             const bool live = r < cs.L && col < cs.L;
             // the decay between rows: a factor here (scalar), inside the
             // products already (per key)
-            const float dec = (live && col <= r) ? (kPerKey ? 1.f : exp_pk(g_r - g_c)) : 0.f;
-            s_A[a_idx(r, col)] = (kDelta && col < r) ? b_r * dec * kk[i] : 0.f;
+            const float dec = (live && col <= r) ? (kPerKey ? 1.f : exp_pk(g_rr[i] - g_c)) : 0.f;
+            s_A[a_idx(r, col)] = (kDelta && col < r) ? b_rr[i] * dec * kk[i] : 0.f;
             pv[ct][i] = dec * qk[i];
         }
     }
@@ -857,6 +866,27 @@ __device__ __forceinline__ void put_kt(const Split8 &x, int d0, int r, __bf16 *k
     }
 }
 
+// The split state planes Sig^T [TV][d_k] (bf16 elements): row = value
+// column, 16-byte pieces of 8 consecutive keys (the B operand of K Sig0 and
+// Q Sig0: 16 lanes read one piece of 16 consecutive rows), written one bf16
+// at a time from the state update's output layout (16 lanes write 16
+// consecutive keys of a row); the piece index is XOR-swizzled by the row.
+template <int DK>
+__device__ __forceinline__ int st_off(int v, int key) {
+    constexpr int P = DK / 8;                            // pieces per row
+    constexpr int S = DK == 128 ? 0 : DK == 64 ? 1 : 2;  // log2(16 / P)
+    return v * DK + ((((key >> 3) ^ (v >> S)) & (P - 1)) << 3) + (key & 7);
+}
+
+// x = hi + lo as bf16 bit patterns (round to nearest even, then the exact
+// residual rounded).
+__device__ __forceinline__ void split1(float x, uint16_t &h, uint16_t &l) {
+    const __bf16 hb = (__bf16)x;
+    const __bf16 lb = (__bf16)(x - (float)hb);
+    h = __builtin_bit_cast(uint16_t, hb);
+    l = __builtin_bit_cast(uint16_t, lb);
+}
+
 template <int KS, int NVT, typename TI>
 struct ChunkRegs {
     static_assert(NVT == 2, "a lane holds one adjacent pair of value columns");
@@ -877,22 +907,29 @@ struct ChunkRegs {
 template <int DK, int DV, typename TI, typename TO, bool PK, bool CK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void scan_kernel(PrefillArgs a) {
     constexpr int KS = DK / 32;          // k-steps over d_k
-    constexpr int SP = DK + 4;           // padded row of Sig^T (fp32)
-    constexpr int CB = C + 8;            // padded row of the R^T / U^T planes
+    constexpr int CB = C + 8;            // padded row of the R^T / U^T / W^T planes
     constexpr int NVT = TV / 16;         // 16-wide value sub-tiles
     constexpr int NFT = NVT * (DK / 16); // output tiles of the state update
     constexpr int NEG = NFT / kWaves;    // state-update tiles per wave
     static_assert(NFT % kWaves == 0, "state-update tiles split evenly over the waves");
     static_assert(DK / 4 <= kWave, "e^{g_L} row fits one wave's 16-byte copies");
     constexpr RecLayout RL = rec_layout(DK, PK);
-    // Sig^T tile [TV][DK] in fp32; R^T, U^T (and, scalar decay, W^T) [TV][C]
-    // as hi / lo bf16 planes (split once when written); K~^T (per key:
-    // copied from the chunk record by direct-to-LDS loads, swizzled rows) or
-    // K^T (scalar decay: formed from the K operands, kt_off) [DK][C] hi / lo.
-    __shared__ __attribute__((aligned(16))) float s_St[TV * SP];
-    __shared__ __attribute__((aligned(16))) __bf16 s_Rh[TV * CB], s_Rl[TV * CB];
-    __shared__ __attribute__((aligned(16))) __bf16 s_Uh[TV * CB], s_Ul[TV * CB];
-    __shared__ __attribute__((aligned(16))) __bf16 s_Wh[PK ? 8 : TV * CB], s_Wl[PK ? 8 : TV * CB];
+    // The fp32 state tile lives in registers: each wave owns NEG 16 x 16
+    // output tiles of the state update (mst). LDS holds it split into hi /
+    // lo bf16 planes Sig^T [TV][DK] (st_off), the B operand of K Sig0 and
+    // Q Sig0; R^T, U^T (and, scalar decay, W^T) [TV][C] as hi / lo bf16
+    // planes (split once when written; the same buffer stages state
+    // write-outs); K~^T (per key: copied from the chunk record by direct-to-
+    // LDS loads, swizzled rows) or K^T (scalar decay: formed from the K
+    // operands, kt_off) [DK][C] hi / lo.
+    constexpr int NPL = PK ? 4 : 6;  // R, U (, W) hi / lo planes
+    __shared__ __attribute__((aligned(16))) __bf16 s_Sh[TV * DK], s_Sl[TV * DK];
+    __shared__ __attribute__((aligned(16))) __bf16 s_pl[NPL * TV * CB];
+    static_assert(DK * TV * 4 <= NPL * TV * CB * 2, "state staging fits the plane buffer");
+    __bf16 *const s_Rh = s_pl, *const s_Rl = s_pl + TV * CB;
+    __bf16 *const s_Uh = s_pl + 2 * TV * CB, *const s_Ul = s_pl + 3 * TV * CB;
+    __bf16 *const s_Wh = s_pl + (PK ? 0 : 4) * TV * CB, *const s_Wl = s_pl + (PK ? 0 : 5) * TV * CB;
+    float *const s_stage = reinterpret_cast<float *>(s_pl);  // [DK][TV] fp32
     __shared__ __attribute__((aligned(16))) __bf16 s_Kh[DK * C], s_Kl[DK * C];
     __shared__ __attribute__((aligned(16))) float s_wv[TV * 4];
     __shared__ __attribute__((aligned(16))) __bf16 s_eg[PK ? 2 * DK : 8];  // e^{g_L}, fp32 bits
@@ -943,20 +980,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const TI *const vs = static_cast<const TI *>(a.v);
     const int cwin_v = 2 * H * DK + h * DV;
 
-    // the state tile [DK][TV] of this workgroup (Sig^T in s_St) into a
-    // [DK][DV] state at dst; valid at a chunk boundary (after the barrier
-    // that closes the previous state update)
-    // (4 consecutive tile columns per 16-byte store; tile column j is
-    // internal column (j % 2) * 16 + j / 2, the inverse of vcol)
+    // The state tiles of this wave: tile m is ft = w + 4 m, value sub-tile
+    // t = ft % NVT, keys dt*16 .. dt*16 + 15 (dt = ft / NVT); the lane holds
+    // the internal value columns t*16 + (l/16)*4 + i (i < 4) of key
+    // dt*16 + l%16.
+    float mst[NEG][4];
+    // the split planes of the state from the registers
+    auto put_split = [&](int lane) {
+        uint16_t *ph = reinterpret_cast<uint16_t *>(s_Sh), *pl = reinterpret_cast<uint16_t *>(s_Sl);
+#pragma unroll
+        for (int m = 0; m < NEG; ++m) {
+            const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = st_off<DK>(t * 16 + (lane / 16) * 4 + i, key);
+                split1(mst[m][i], ph[o], pl[o]);
+            }
+        }
+    };
+    // the state tile [DK][TV] of this workgroup into a [DK][DV] state at
+    // dst, through the staging buffer (4 consecutive tile columns per
+    // 16-byte store); called between barriers, so the plane buffer is free
     auto put_state = [&](float *dst) {
+#pragma unroll
+        for (int m = 0; m < NEG; ++m) {
+            const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_stage[key * TV + vcol(t * 16 + (lane / 16) * 4 + i)] = mst[m][i];
+        }
+        __syncthreads();
         for (int idx = tid; idx < DK * TV / 4; idx += kThreads) {
             const int d = idx / (TV / 4), j = 4 * (idx % (TV / 4));
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = s_St[((j + e) % 2 * 16 + (j + e) / 2) * SP + d];
             *reinterpret_cast<float4 *>(dst + (size_t)d * DV + j0 + j) =
-                make_float4(x[0], x[1], x[2], x[3]);
+                *reinterpret_cast<const float4 *>(s_stage + d * TV + j);
         }
+        __syncthreads();
     };
     // conv window after position `end` of the sequence: its last 3 raw
     // inputs (from the incoming window where end < 3), head h's channels
@@ -1059,17 +1117,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // tile, so the two round trips overlap (a one-chunk branch pays one)
     ChunkRegs<KS, NVT, TI> nxt;
     if (nchunks > 0) load_regs(0, nxt);
-    for (int idx = tid; idx < DK * TV; idx += kThreads) {
-        const int d = idx / TV, c = idx % TV;
-        s_St[c * SP + d] =
-            a.state_in ? a.state_in[(((size_t)src * H + h) * DK + d) * DV + j0 + vcol(c)] : 0.f;
+#pragma unroll
+    for (int m = 0; m < NEG; ++m) {
+        const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mst[m][i] = a.state_in ? a.state_in[(((size_t)src * H + h) * DK + key) * DV + j0 +
+                                                vcol(t * 16 + (lane / 16) * 4 + i)]
+                                   : 0.f;
     }
+    put_split(lane);
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
         if constexpr (CK)
             if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
         const ChunkRegs<KS, NVT, TI> cur = nxt;
+        // The step's lane-derived LDS offsets are formed inside the step from
+        // an opaque copy of the lane index (an identity DPP move): hoisted
+        // out of the loop, the compiler keeps them live and spills.
+        const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
+        const int acol = (lane / 16) * 8, r0v = w * RB + (lane / 16) * 4;
         if constexpr (PK) {
             load_kt(c);
         } else {
@@ -1115,9 +1183,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             acc_o[t] = acc;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                float bx[8];
-                lds_read8(s_St + (t * 16 + lane % 16) * SP + ks * 32 + acol, bx);
-                const Split8 bs = split8(bx);
+                const int so = st_off<DK>(t * 16 + lane % 16, ks * 32 + acol);
+                const Split8 bs = read_split8(s_Sh + so, s_Sl + so);
                 acc = mma3(cur.ka[ks], bs, acc);
                 if (want_o) acc_o[t] = mma3(cur.qa[ks], bs, acc_o[t]);
             }
@@ -1198,8 +1265,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const float dec = PK ? reinterpret_cast<const float *>(s_eg)[dt * 16 + lane % 16] : gamL;
             f32x4v acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[i] = dec * s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16];
+            for (int i = 0; i < 4; ++i) acc[i] = dec * mst[m][i];
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
                 const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
@@ -1209,12 +1275,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                          : mma3(read_split8(s_Wh + ou, s_Wl + ou), read_split8(s_Kh + ok, s_Kl + ok), acc);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s_St[(t * 16 + (lane / 16) * 4 + i) * SP + dt * 16 + lane % 16] = acc[i];
+            for (int i = 0; i < 4; ++i) mst[m][i] = acc[i];
         }
+        put_split(lane);
         __syncthreads();
-    }
-
+            }
     if (a.state_out) put_state(a.state_out + ((size_t)s * H + h) * DK * DV);
     if (a.win_out && tile == 0) put_window(static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
     // a checkpoint at the end of the sequence (its length a multiple of the
