@@ -4,7 +4,8 @@ Thin Python binding over the C ABI of libgdn_mi355x.so (include/gdn_mi355x.h):
 shared-context prefill and forked branches (the two-call GDN fork of the
 Flide page), eager decode, and deferred base + log decode with its merge
 (the DeltaLog page), and the softmax-attention half of the fork (attention
-under the trunk + own-branch visibility rule). Tensors are torch device
+under the trunk + own-branch visibility rule), plus a runner that replays
+pre-captured fork graphs per stream-capacity bucket. Tensors are torch device
 tensors; every step of the computation runs in the HIP kernels.
 """
 
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     prefill_workspace_bytes,
     status_string,
 )
+from .graphs import Bucket, ForkGraphRunner, Replay, plan_round  # noqa: F401
 
 __all__ = [
     "gdn_prefill_shared",
@@ -42,4 +44,8 @@ __all__ = [
     "status_string",
     "load",
     "GDNError",
+    "Bucket",
+    "ForkGraphRunner",
+    "Replay",
+    "plan_round",
 ]

@@ -6,7 +6,12 @@ loop or a two-call fork can be captured once and replayed (the Flide page's
 "연구방법을 단계별로", step 3: counts in device buffers so a captured graph
 serves changing rounds). Each test replays its graph several times, with
 eager work and synchronisations in between, and checks every replay bit for
-bit against the same calls launched one by one.
+bit against the same calls launched one by one and against the fp64 oracle
+(max |gpu - oracle| / max |oracle| per (sequence, head) slice within 2e-3,
+conv windows bitwise). The last tests drive ForkGraphRunner, the binding's
+per-capacity graph runner, through rounds that fit one bucket, overflow
+every bucket (split at request boundaries) and hold a request larger than
+every bucket (run without a graph).
 """
 
 import numpy as np
@@ -15,11 +20,49 @@ import torch
 
 import gdn_inputs as gi
 import linear_attention_recurrent_gdn_amd as gdn
+import oracle
+from test_gpu_prefill import slice_err, window_ref, window_to_bits
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 REPLAYS = 3
+TOL = 2e-3
+
+
+def host(x):
+    return None if x is None else x.float().cpu().numpy()
+
+
+def oracle_fork(t, cu, bcu=None, par=None, Np=None):
+    """fp64 oracle of the two calls on host copies of device inputs t (a
+    torch_seq_inputs dict): prefix tokens [0, Np), branch tokens after."""
+    q, k, v, la, beta = (host(t[n]) for n in ("q", "k", "v", "log_alpha", "beta"))
+    cw = host(t["conv_w"])
+    Np = q.shape[0] if Np is None else Np
+    o_p, st, win = oracle.prefill(q[:Np], k[:Np], v[:Np], la[:Np], beta[:Np], cu, conv_w=cw,
+                                  qk_norm=cw is not None)
+    r = dict(o_p=o_p, st=st, win=win)
+    if bcu is not None:
+        r["o_b"], r["st_b"], r["win_b"] = oracle.fork(
+            q[Np:], k[Np:], v[Np:], la[Np:], beta[Np:], bcu, par, st, win, conv_w=cw,
+            qk_norm=cw is not None)
+    return r
+
+
+def assert_oracle(tag, H, got, ref, cu, bcu=None):
+    """got: device outputs o_p, st, win (and o_b, st_b, win_b) of the same
+    names as oracle_fork's; cu / bcu: the token offsets of o_p / o_b."""
+    e = dict(o_p=slice_err(host(got["o_p"]), ref["o_p"], cu, H),
+             st=oracle.rel_err(host(got["st"]), ref["st"], axes=(2, 3)))
+    if bcu is not None:
+        e["o_b"] = slice_err(host(got["o_b"]), ref["o_b"], bcu, H)
+        e["st_b"] = oracle.rel_err(host(got["st_b"]), ref["st_b"], axes=(2, 3))
+    print(tag, {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
+    assert all(v <= TOL for v in e.values()), (tag, e)
+    for w in ("win", "win_b"):
+        if got.get(w) is not None and w in ref:
+            assert np.array_equal(window_to_bits(got[w]), window_ref(ref[w], "bf16")), (tag, w)
 
 
 def _decode_setup(B=16, H=4, d=128, T=12, M=4, seed=0):
@@ -54,6 +97,8 @@ def test_deferred_decode_loop_replays_bitwise():
     _decode_steps(t, base, logs, o_ref, M)
     torch.cuda.synchronize()
     base_ref = base.clone()
+    o_or, st_or, _ = oracle.decode(host(t["q"]), host(t["k"]), host(t["v"]), host(t["log_alpha"]),
+                                   host(t["beta"]), host(base0), variant="gdn")
     # capture on static buffers
     gb, gl = base0.clone(), {k: v.clone() for k, v in logs0.items()}
     go = torch.empty((T, B, H, d), device=DEV)
@@ -78,6 +123,10 @@ def test_deferred_decode_loop_replays_bitwise():
         assert torch.equal(go, o_ref), f"replay {rep}: o differs"
         assert torch.equal(gb, base_ref), f"replay {rep}: base differs"
         assert (gl["log_len"] == 0).all()
+        eo = oracle.rel_err(host(go), o_or, axes=(0, 3))
+        es = oracle.rel_err(host(gb), st_or, axes=(2, 3))
+        print(f"replay {rep}: oracle o={eo:.2e} state={es:.2e}", flush=True)
+        assert eo <= TOL and es <= TOL, (rep, eo, es)
 
 
 def test_two_call_fork_replays_bitwise():
@@ -113,6 +162,8 @@ def test_two_call_fork_replays_bitwise():
     ref = bufs()
     run(ref)
     torch.cuda.synchronize()
+    cu_h, bcu_h = t["cu_seqlens"].cpu().numpy(), t["branch_cu"].cpu().numpy()
+    orc = oracle_fork(t, cu_h, bcu_h, t["branch_parent"].cpu().numpy(), Np)
     g = bufs()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -132,6 +183,8 @@ def test_two_call_fork_replays_bitwise():
         torch.cuda.synchronize()
         for name in ref:
             assert torch.equal(g[name], ref[name]), f"replay {rep}: {name} differs"
+        assert_oracle(f"replay {rep}", H, dict(o_p=g["o_p"], st=g["st"], win=g["win"],
+                                               o_b=g["o_b"], st_b=g["st_b"]), orc, cu_h, bcu_h)
 
 
 def test_fixed_capacity_graph_serves_changing_rounds():
@@ -182,6 +235,9 @@ def test_fixed_capacity_graph_serves_changing_rounds():
         assert torch.equal(st, st_r), lay
         assert torch.equal(win, win_r), lay
         assert torch.equal(o[:used], o_r[:used]), lay
+        orc = oracle_fork({n: (x[:used] if n in ("q", "k", "v", "log_alpha", "beta") else x)
+                           for n, x in t.items()}, np.asarray(lay, dtype=np.int32))
+        assert_oracle(str(lay), H, dict(o_p=o[:used], st=st, win=win), orc, lay)
 
 
 def test_fork_attention_graph_serves_changing_rounds():
@@ -233,3 +289,124 @@ def test_fork_attention_graph_serves_changing_rounds():
         used = lay[1][-1]
         assert torch.equal(o[:used], o_r[:used]), lay
         assert not torch.isnan(o[:used]).any(), lay
+        ref = oracle.fork_attention(host(t["q"]), host(t["k"]), host(t["v"]),
+                                    np.asarray(lay[0], np.int32), np.asarray(lay[1], np.int32),
+                                    np.asarray(lay[2], np.int32))
+        segs = [(a, b) for cuv in (lay[0], lay[1]) for a, b in zip(cuv[:-1], cuv[1:]) if b > a]
+        e = max(oracle.rel_err(host(o[a:b]), ref[a:b], axes=(0, 2)) for a, b in segs)
+        print(lay, f"oracle {e:.2e}", flush=True)
+        assert e <= TOL, (lay, e)
+
+
+# ------------------------------------------------------------------ runner
+RUNNER_BUCKETS = [gdn.Bucket(tokens=256, requests=2, branch_tokens=192, branches=6),
+                  gdn.Bucket(tokens=512, requests=4, branch_tokens=384, branches=12)]
+
+
+def _round(prefix, branch_counts, branch_lens, H, d, seed):
+    """A round as flat device streams: the prefix tokens by request, then
+    the branch tokens grouped by request."""
+    parent = np.repeat(np.arange(len(prefix)), branch_counts).tolist()
+    inp = gi.seq_inputs(prefix, branch_lens, parent, H, d, d, io="bf16", conv=True, seed=seed)
+    Np = inp.Np
+
+    def dev(name):
+        bits = getattr(inp, name + "_bits")
+        return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+    q, k, v = dev("q"), dev("k"), dev("v")
+    la = torch.from_numpy(inp.log_alpha).to(DEV)
+    beta = torch.from_numpy(inp.beta.astype(np.float32)).to(DEV)
+    pre = dict(q=q[:Np], k=k[:Np], v=v[:Np], log_alpha=la[:Np], beta=beta[:Np])
+    br = dict(q=q[Np:], k=k[Np:], v=v[Np:], log_alpha=la[Np:], beta=beta[Np:])
+    return inp, pre, br
+
+
+def _outputs(inp, H, d):
+    R, NB = len(inp.cu_seqlens) - 1, len(inp.branch_cu) - 1
+    cc = H * 3 * d
+    nan = float("nan")
+    return dict(o=torch.full((inp.Np, H, d), nan, device=DEV),
+                state=torch.full((R, H, d, d), nan, device=DEV),
+                window=torch.zeros((R, 3, cc), device=DEV, dtype=torch.bfloat16),
+                bo=torch.full((inp.Nb, H, d), nan, device=DEV),
+                bstate=torch.full((NB, H, d, d), nan, device=DEV),
+                bwindow=torch.zeros((NB, 3, cc), device=DEV, dtype=torch.bfloat16))
+
+
+def _check_runner(tag, inp, out, orc, H):
+    torch.cuda.synchronize()
+    got = dict(o_p=out["o"], st=out["state"], win=out["window"], o_b=out["bo"],
+               st_b=out["bstate"], win_b=out["bwindow"])
+    assert_oracle(tag, H, got, orc, inp.cu_seqlens, inp.branch_cu)
+
+
+@pytest.fixture(scope="module")
+def runner():
+    H, d = 2, 64
+    cw = torch.from_numpy(gi.seq_inputs([1], [], [], H, d, d, conv=True, seed=77).conv_w).to(DEV)
+    return gdn.ForkGraphRunner(H, d, d, RUNNER_BUCKETS, conv_w=cw, qk_l2norm=True), cw
+
+
+def _with_conv(inp, cw):
+    """The runner's conv weights replace the round's drawn ones (a layer's
+    weights are fixed across rounds)."""
+    inp.conv_w = cw.cpu().numpy()
+    return inp
+
+
+def _round_for_runner(cw, prefix, counts, lens, seed, H=2, d=64):
+    inp, pre, br = _round(prefix, counts, lens, H, d, seed)
+    inp = _with_conv(inp, cw)
+    Np = inp.Np
+    o_p, st, win = oracle.prefill(inp.q[:Np], inp.k[:Np], inp.v[:Np], inp.log_alpha[:Np],
+                                  inp.beta[:Np], inp.cu_seqlens, conv_w=inp.conv_w, qk_norm=True)
+    o_b, st_b, win_b = oracle.fork(inp.q[Np:], inp.k[Np:], inp.v[Np:], inp.log_alpha[Np:],
+                                   inp.beta[Np:], inp.branch_cu, inp.branch_parent, st, win,
+                                   conv_w=inp.conv_w, qk_norm=True)
+    return inp, pre, br, dict(o_p=o_p, st=st, win=win, o_b=o_b, st_b=st_b, win_b=win_b)
+
+
+def test_runner_rounds_in_one_bucket(runner):
+    """Rounds that fit the small or the large bucket, several in a row on
+    the same graphs (tail padding, empty prefixes and branches)."""
+    run, cw = runner
+    rounds = [([100, 130], [2, 1], [64, 9, 33]),
+              ([0, 200, 7], [1, 0, 3], [1, 64, 65, 2]),
+              ([64, 1, 190, 64], [3, 3, 3, 3], [20] * 12),
+              ([100, 130], [2, 1], [5, 0, 70])]
+    for i, (pl, bc, bl) in enumerate(rounds):
+        inp, pre, br, orc = _round_for_runner(cw, pl, bc, bl, seed=100 + i)
+        out = _outputs(inp, 2, 64)
+        plan = run.run(pre, br, pl, bc, bl, out)
+        assert len(plan) == 1 and plan[0].bucket is not None, plan
+        _check_runner(f"round {i} plan {plan}", inp, out, orc, 2)
+
+
+def test_runner_splits_over_capacity_round(runner):
+    """A round of 6 requests (651 prefix tokens) beyond the largest bucket
+    (512 tokens, 4 requests) runs as two replays split at a request
+    boundary."""
+    run, cw = runner
+    pl = [100, 130, 64, 200, 7, 150]
+    bc = [2] * 6
+    bl = [40, 3, 64, 1, 9, 9, 33, 0, 5, 5, 64, 64]
+    inp, pre, br, orc = _round_for_runner(cw, pl, bc, bl, seed=7)
+    out = _outputs(inp, 2, 64)
+    plan = run.run(pre, br, pl, bc, bl, out)
+    assert plan == [gdn.Replay(0, 4, 1), gdn.Replay(4, 6, 0)], plan
+    _check_runner(f"split {plan}", inp, out, orc, 2)
+
+
+def test_runner_oversize_request_runs_graphless(runner):
+    """A 700-token request (beyond every bucket) between two small ones:
+    the small ones replay graphs, the large one runs the calls directly."""
+    run, cw = runner
+    pl = [30, 700, 65]
+    bc = [1, 2, 1]
+    bl = [64, 9, 130, 3]
+    inp, pre, br, orc = _round_for_runner(cw, pl, bc, bl, seed=8)
+    out = _outputs(inp, 2, 64)
+    plan = run.run(pre, br, pl, bc, bl, out)
+    assert plan == [gdn.Replay(0, 1, 0), gdn.Replay(1, 2, None), gdn.Replay(2, 3, 0)], plan
+    _check_runner(f"oversize {plan}", inp, out, orc, 2)
