@@ -111,9 +111,11 @@ size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k,
  *     S_t = S_{t-1} diag(a_t) (I - b_t k_t k_t^T) + b_t v_t k_t^T; GDN_RWKV6
  *     the raw value update S_t = S_{t-1} diag(a_t) + v_t k_t^T ([DL] "커널
  *     구현": the KDA and RWKV6 operators). a_t = exp(log_alpha).
- *     Per-key decay is formed inside each chunk as exp(+-running sum of
- *     log_alpha), so a chunk's total log-decay per key must stay above
- *     about -80 (fp32 range).
+ *     Any decay is allowed (log_alpha finite and <= 0; chunk sums of
+ *     -1000 and single steps of -1000 are tested): every decay factor a
+ *     chunk forms is e^{x} with x <= 0, except a per-key block factor up
+ *     to e^80, beyond which the chunk takes the affected products from
+ *     their definition.
  *
  *  q, k         [n_tokens, H, d_k]   io_dtype
  *  v            [n_tokens, H, d_v]   io_dtype

@@ -442,6 +442,127 @@ __device__ __forceinline__ float quad_sum(float x) {
     return x;
 }
 
+// Per-key running sums: log a of this lane's row (rows >= L add nothing)
+// and keys ks * 32 + cq + e, scanned inclusively over the wave's 16 rows
+// (DPP within 16-lane rows). g_add_earlier then adds the totals of the
+// earlier waves' row blocks (s_gt [kWaves][DK]), giving g_r from the chunk
+// start.
+template <int DK>
+__device__ __forceinline__ void g_scan_rows(const PrefillArgs &a, int h, int row0, int L, int row,
+                                            int cq, float (&g)[DK / 32][8]) {
+    const float *lap = a.log_alpha + ((size_t)(row0 + min(row, L - 1)) * a.H + h) * DK;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) load8(lap + ks * 32 + cq, g[ks]);
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = row < L ? g[ks][e] : 0.f;
+            x += row_shr<1>(x);
+            x += row_shr<2>(x);
+            x += row_shr<4>(x);
+            x += row_shr<8>(x);
+            g[ks][e] = x;
+        }
+}
+
+template <int DK>
+__device__ __forceinline__ void g_add_earlier(const float *s_gt, int w, int cq,
+                                              float (&g)[DK / 32][8]) {
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = ks * 32 + cq + e;
+            float before = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) before += ww < w ? s_gt[ww * DK + d] : 0.f;
+            g[ks][e] += before;
+        }
+}
+
+// Largest exponent of the per-key join factor e^{g0[R] - g15[R]} (a row
+// block's decay across its 16 rows) taken inside a factored product; past
+// it the block's diagonal tile is evaluated from the definition
+// (diag_direct). e^80 and the operands down to e^-80 stay normal in fp32.
+constexpr float kJoinLimit = 80.f;
+
+// Wave w's diagonal 16 x 16 tile of KK^T and QK^T under per-key decay,
+// from the definition: entry (r, s), s <= r, is
+// sum_d k_r[d] k_s[d] e^{g_r[d] - g_s[d]} (q_r in place of k_r for QK^T),
+// every exponent <= 0. The lane's entries are those of the MFMA output
+// layout: rows 16 w + 4 (lane / 16) + i, column 16 w + lane % 16. g holds
+// this lane's sums (row 16 w + lane % 16, keys ks * 32 + cq + e); the Q and
+// K rows are formed here (taps s_wq / s_wk, or null) and pass through
+// s_work (kWaves * 3 * 16 rows of kDirectPitch floats) 32 keys at a time.
+// Every thread of the block calls it (it synchronises).
+constexpr int kDirectPitch = 36;  // staged row: 32 keys + 4 pad floats
+constexpr int kDirectWork = kWaves * 3 * RB * kDirectPitch;
+
+template <int DK, typename TI>
+__device__ __forceinline__ void diag_direct(const PrefillArgs &a, const ChunkSrc<TI> &cs, int h,
+                                            int CC, const float (&g)[DK / 32][8],
+                                            const float *s_wq, const float *s_wk, float *s_work,
+                                            f32x4v &kk, f32x4v &qk) {
+    constexpr int KS = DK / 32, SP = kDirectPitch;
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int cq = (lane / 16) * 8;
+    const int H = a.H;
+    const bool conv = a.conv_w != nullptr;
+    float *const s_st = s_work + w * 3 * RB * SP;  // this wave's K | Q | g rows
+    float qf[KS][8], kf[KS][8];
+    {
+        RawRows<DK, TI> rr;
+        rows_load<DK, TI>(static_cast<const TI *>(a.q), H, h, cs, w, CC, h * DK, conv, rr);
+        rows_compute<DK, TI>(rr, cs, w, s_wq, a.qk_norm != 0, qf);
+    }
+    {
+        RawRows<DK, TI> rr;
+        rows_load<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK + h * DK, conv,
+                          rr);
+        rows_compute<DK, TI>(rr, cs, w, s_wk, a.qk_norm != 0, kf);
+    }
+    kk = f32x4v{0.f, 0.f, 0.f, 0.f};
+    qk = f32x4v{0.f, 0.f, 0.f, 0.f};
+    const int sl = lane % 16, rl = 4 * (lane / 16);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float *const p = s_st + (lane % 16) * SP + cq;
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+            *reinterpret_cast<float4 *>(p + e) = make_float4(kf[ks][e], kf[ks][e + 1],
+                                                             kf[ks][e + 2], kf[ks][e + 3]);
+            *reinterpret_cast<float4 *>(p + RB * SP + e) =
+                make_float4(qf[ks][e], qf[ks][e + 1], qf[ks][e + 2], qf[ks][e + 3]);
+            *reinterpret_cast<float4 *>(p + 2 * RB * SP + e) =
+                make_float4(g[ks][e], g[ks][e + 1], g[ks][e + 2], g[ks][e + 3]);
+        }
+        __syncthreads();
+        const float *const sk = s_st, *const sq = s_st + RB * SP, *const sg = s_st + 2 * RB * SP;
+#pragma unroll 1
+        for (int d = 0; d < 32; d += 4) {
+            const float4 kc = *reinterpret_cast<const float4 *>(sk + sl * SP + d);
+            const float4 gc = *reinterpret_cast<const float4 *>(sg + sl * SP + d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rl + i;
+                const float4 kr = *reinterpret_cast<const float4 *>(sk + r * SP + d);
+                const float4 qr = *reinterpret_cast<const float4 *>(sq + r * SP + d);
+                const float4 gv = *reinterpret_cast<const float4 *>(sg + r * SP + d);
+                const bool in = sl <= r;
+                const float f0 = in ? exp_pk(fminf(gv.x - gc.x, 0.f)) : 0.f;
+                const float f1 = in ? exp_pk(fminf(gv.y - gc.y, 0.f)) : 0.f;
+                const float f2 = in ? exp_pk(fminf(gv.z - gc.z, 0.f)) : 0.f;
+                const float f3 = in ? exp_pk(fminf(gv.w - gc.w, 0.f)) : 0.f;
+                const float t0 = kc.x * f0, t1 = kc.y * f1, t2 = kc.z * f2, t3 = kc.w * f3;
+                kk[i] = fmaf(kr.x, t0, fmaf(kr.y, t1, fmaf(kr.z, t2, fmaf(kr.w, t3, kk[i]))));
+                qk[i] = fmaf(qr.x, t0, fmaf(qr.y, t1, fmaf(qr.z, t2, fmaf(qr.w, t3, qk[i]))));
+            }
+        }
+        __syncthreads();  // before the staging is written again
+    }
+}
+
 // Rows R0 + 1 .. C - 1 of the column solve of T = (I + A)^-1 (see prep_body):
 // t[q] holds T[4q + part][col]; arow points at this lane's j = part (mod 4)
 // group of row 0 of A (rows of AP floats). Row r needs the terms j < r,
@@ -469,12 +590,16 @@ __device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], 
 // VAR: the decay / update rule. kScalar: log a [N, H], the gated delta rule.
 // kKda: per-key log a [N, H, d_k], delta rule. kRwkv6: per-key log a, raw
 // value update (u = v: no A, T' = I, no K Sig term, beta unused).
-// Per-key chunk form (g_r[d] running sums per key): with K^ = K . e^{g},
-// K- = K . e^{-g}, Q^ = Q . e^{g}:
-//   A[r][s] = beta_r <K^_r, K-_s> (s < r),  P[r][s] = <Q^_r, K-_s> (s <= r),
+// Per-key chunk form (g_r[d] running sums per key, <= 0 and
+// non-increasing): with K^ = K . e^{g}, Q^ = Q . e^{g},
+//   A[r][s] = beta_r sum_d k_r[d] k_s[d] e^{g_r[d] - g_s[d]}   (s < r),
+//   P[r][s] = sum_d q_r[d] k_s[d] e^{g_r[d] - g_s[d]}          (s <= r),
 //   U = T' (V - K^ Sig0),  O = Q^ Sig0 + P U,
 //   Sig_L = diag(e^{g_L}) Sig0 + sum_r (k_r . e^{g_L - g_r}) u_r^T,
-// which the scan runs with gamma = 1 and a per-key state decay.
+// which the scan runs with gamma = 1 and a per-key state decay. Every
+// factor the record holds is <= 1. A and P are products against 16-row
+// block references (see prep_body), so no factor leaves fp32's range for
+// any decay: e^{-g_s} alone would overflow once a chunk decays past e^-88.
 // Rows x C matrix staged in LDS (rows padded to C + 1 floats) -> hi / lo
 // bf16 planes of the record, 8 elements (16 bytes) per store: row-major
 // [rows][C], or in A-fragment order (FRAG: a lower-triangular C x C matrix,
@@ -521,6 +646,15 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     float *const s_wq = s_A, *const s_wk = s_A + DK * 4;
     __shared__ float s_gt[kPerKey ? kWaves * DK : 1];  // per-key: each wave's row-block sums
     __shared__ __attribute__((aligned(16))) float s_gl[kPerKey ? DK : 4];  // per-key: g_L
+    // per key, [kWaves][DK] each: the row blocks' first- and last-row sums
+    // g0 and g15, e^{g0}, e^{g_L - g15}; then the join factors
+    // e^{g0[R] - g15[S]} (S <= R, pair R (R + 1) / 2 + S) [kPairs][DK];
+    // s_slow: some block decays past e^{-kJoinLimit} in some key
+    constexpr int kPairs = kWaves * (kWaves + 1) / 2;
+    constexpr int TG0 = 0, TG15 = kWaves * DK, TEG0 = 2 * kWaves * DK, TEL = 3 * kWaves * DK,
+                  TM = 4 * kWaves * DK;
+    __shared__ __attribute__((aligned(16))) float s_tab[kPerKey ? TM + kPairs * DK : 4];
+    __shared__ int s_slow;
 
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
     const int gc = blockIdx.x, h = blockIdx.y;
@@ -547,6 +681,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         stage_taps(a.conv_w, h * DK, DK, s_wq);
         stage_taps(a.conv_w, H * DK + h * DK, DK, s_wk);
     }
+    if (kPerKey && tid == 0) s_slow = 0;
     __syncthreads();
     const int row = w * RB + lane % 16;  // this lane's row in the A layout
     const int cq = (lane / 16) * 8;
@@ -559,41 +694,22 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         g = chunk_g(a.log_alpha, H, h, cs.seq0, cs.p0, cs.L);
         gL = __shfl(g, C - 1, kWave);
     } else {
-        // log a of this lane's row (rows >= L add nothing), then an inclusive
-        // scan over the wave's 16 rows (DPP within 16-lane rows) plus the
-        // sums of the earlier waves' row blocks
-        const float *lap =
-            a.log_alpha + ((size_t)(cs.seq0 + cs.p0 + min(row, cs.L - 1)) * H + h) * DK;
-        float gk[KS][8];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load8(lap + ks * 32 + cq, gk[ks]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = row < cs.L ? gk[ks][e] : 0.f;
-                x += row_shr<1>(x);
-                x += row_shr<2>(x);
-                x += row_shr<4>(x);
-                x += row_shr<8>(x);
-                gk[ks][e] = x;
-            }
+        g_scan_rows<DK>(a, h, cs.seq0 + cs.p0, cs.L, row, cq, gr);
         if (lane % 16 == 15)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) s_gt[w * DK + ks * 32 + cq + e] = gk[ks][e];
+                for (int e = 0; e < 8; ++e) s_gt[w * DK + ks * 32 + cq + e] = gr[ks][e];
         __syncthreads();
+        g_add_earlier<DK>(s_gt, w, cq, gr);
+        // the block's first- and last-row sums
+        if (lane % 16 == 0 || lane % 16 == 15) {
+            float *const dst = s_tab + (lane % 16 == 0 ? TG0 : TG15) + w * DK + cq;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = ks * 32 + cq + e;
-                float before = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < kWaves; ++ww) before += ww < w ? s_gt[ww * DK + d] : 0.f;
-                gr[ks][e] = gk[ks][e] + before;
-            }
+                for (int e = 0; e < 8; ++e) dst[ks * 32 + e] = gr[ks][e];
+        }
         // g_L per key; e^{g_L} for the scan's state decay
         if (tid < DK) {
             float total = 0.f;
@@ -603,6 +719,32 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             fac[tid] = expf(total);
         }
         __syncthreads();
+        for (int idx = tid; idx < kWaves * DK; idx += kThreads) {
+            s_tab[TEG0 + idx] = expf(s_tab[TG0 + idx]);
+            s_tab[TEL + idx] = expf(s_gl[idx % DK] - s_tab[TG15 + idx]);
+        }
+        for (int idx = tid; idx < kPairs * DK; idx += kThreads) {
+            const int pr = idx / DK, d = idx % DK;
+            int R = 0;
+            while ((R + 1) * (R + 2) / 2 <= pr) ++R;
+            const int S = pr - R * (R + 1) / 2;
+            const float x = s_tab[TG0 + R * DK + d] - s_tab[TG15 + S * DK + d];
+            if (S == R && x > kJoinLimit) s_slow = 1;
+            s_tab[TM + idx] = expf(fminf(x, kJoinLimit));
+        }
+        __syncthreads();
+    }
+    // a block decays past e^{-kJoinLimit} in some key: its join factor is
+    // clamped, and every wave takes its diagonal tile from the definition
+    // instead (while s_k is still free and the taps are staged)
+    f32x4v kk_diag = {0.f, 0.f, 0.f, 0.f}, qk_diag = {0.f, 0.f, 0.f, 0.f};
+    bool slow = false;
+    if constexpr (kPerKey) {
+        slow = __builtin_amdgcn_readfirstlane(s_slow) != 0;
+        static_assert(kDirectWork <= SK, "direct staging fits s_k");
+        if (slow)
+            diag_direct<DK, TI>(a, cs, h, CC, gr, conv ? s_wq : nullptr, conv ? s_wk : nullptr,
+                                s_k, kk_diag, qk_diag);
     }
     float b_l = 1.f;
     if constexpr (kDelta) b_l = a.beta[(size_t)(cs.seq0 + cs.p0 + min(lane, cs.L - 1)) * H + h];
@@ -611,7 +753,24 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     // conv'd, normalised Q and K rows (per key: decayed); their split A
     // operands go to the record. With a scalar decay the raw Q and K rows
     // are requested together (the per-key form has no registers to spare).
+    // Per key the matrix products take each row block against its own first
+    // row, e1 = e^{g_r - g0} <= 1 (row operands Q. e1, K. e1), and each
+    // column against its block's last row, e^{g15 - g_s} <= 1 (column
+    // operand, kept in fp32 in s_b32); a tile (R, S) joins the two with the
+    // per-key factor e^{g0[R] - g15[S]} (<= 1 off the diagonal). The record
+    // keeps the forms from the chunk start, Q^ = Q. e^{g}, K^ = K. e^{g}.
     Split8 qa[DK / 32], ka[DK / 32];
+    float *const s_b32 = s_k;  // per key: the column operands [C][DK], fragment order
+    float e1[kPerKey ? DK / 32 : 1][8];
+    if constexpr (kPerKey) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float g0v[8];
+            lds_read8(s_tab + TG0 + w * DK + ks * 32 + cq, g0v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) e1[ks][e] = exp_pk(gr[ks][e] - g0v[e]);
+        }
+    }
     RawRows<DK, TI> rk;
     const auto load_k = [&] {
         rows_load<DK, TI>(static_cast<const TI *>(a.k), H, h, cs, w, CC, H * DK + h * DK, conv,
@@ -625,13 +784,24 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         rows_compute<DK, TI>(rq, cs, w, conv ? s_wq : nullptr, a.qk_norm != 0, qf);
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks) {
-            if constexpr (kPerKey)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qf[ks][e] *= exp_pk(gr[ks][e]);  // Q^
-            qa[ks] = split8(qf[ks]);
             const int off = frag_off(KS, w, ks, lane);
-            *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
-            *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = qa[ks].lo;
+            if constexpr (kPerKey) {
+                float eg[8], qr[8];
+                lds_read8(s_tab + TEG0 + w * DK + ks * 32 + cq, eg);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    qf[ks][e] *= e1[ks][e];
+                    qr[e] = qf[ks][e] * eg[e];  // Q^
+                }
+                qa[ks] = split8(qf[ks]);
+                const Split8 rs = split8(qr);
+                *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = rs.hi;
+                *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = rs.lo;
+            } else {
+                qa[ks] = split8(qf[ks]);
+                *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
+                *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = qa[ks].lo;
+            }
         }
     }
     if constexpr (kPerKey) load_k();
@@ -647,33 +817,35 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     }
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-        // A operand of KK^T and the scan's K Sig term: K (scalar decay), K^
-        // (per key), nothing (raw value update: the record row is zero)
-        // per key, kf becomes this row's K~^T column entries k e^{g_L - g}
-        float ak[8], bk[8], glv[8];
-        if constexpr (kPerKey) lds_read8(s_gl + ks * 32 + cq, glv);
+        const int off = frag_off(KS, w, ks, lane);
+        if constexpr (kPerKey) {
+            // row operand K. e1; the record's K^ (the scan's K Sig term; zero
+            // for the raw value update); the column operand K. e^{g15 - g}
+            float g15v[8], eg[8], ak[8], kr[8], bk[8];
+            lds_read8(s_tab + TG15 + w * DK + ks * 32 + cq, g15v);
+            lds_read8(s_tab + TEG0 + w * DK + ks * 32 + cq, eg);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (kPerKey) {
-                ak[e] = kDelta ? kf[ks][e] * exp_pk(gr[ks][e]) : 0.f;
-                bk[e] = kf[ks][e] * exp_pk(-gr[ks][e]);  // B operand rows: K-
-                kf[ks][e] *= exp_pk(glv[e] - gr[ks][e]);
-            } else {
-                ak[e] = bk[e] = kf[ks][e];
+            for (int e = 0; e < 8; ++e) {
+                ak[e] = kf[ks][e] * e1[ks][e];
+                kr[e] = kDelta ? ak[e] * eg[e] : 0.f;
+                bk[e] = kf[ks][e] * exp_pk(g15v[e] - gr[ks][e]);
             }
-        }
-        ka[ks] = split8(ak);
-        {
-            const int off = frag_off(KS, w, ks, lane);
+            ka[ks] = split8(ak);
+            const Split8 rs = split8(kr);
+            *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = rs.hi;
+            *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = rs.lo;
+            *reinterpret_cast<f32x4v *>(s_b32 + off) = f32x4v{bk[0], bk[1], bk[2], bk[3]};
+            *reinterpret_cast<f32x4v *>(s_b32 + off + 4) = f32x4v{bk[4], bk[5], bk[6], bk[7]};
+        } else {
+            // A operand of KK^T and the scan's K Sig term: K; the B operand
+            // rows of KK^T and QK^T, split once, in fragment order: the
+            // reader of row block ct takes lane l's piece of wave ct
+            ka[ks] = split8(kf[ks]);
             *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
             *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
+            *reinterpret_cast<bf16x8 *>(s_bh + off) = ka[ks].hi;
+            *reinterpret_cast<bf16x8 *>(s_bl + off) = ka[ks].lo;
         }
-        // the B operand rows of KK^T and QK^T, split once, in fragment order:
-        // the reader of row block ct takes lane l's piece of wave ct
-        const Split8 bs = kPerKey ? split8(bk) : ka[ks];
-        const int off = frag_off(KS, w, ks, lane);
-        *reinterpret_cast<bf16x8 *>(s_bh + off) = bs.hi;
-        *reinterpret_cast<bf16x8 *>(s_bl + off) = bs.lo;
     }
     __syncthreads();
 
@@ -687,19 +859,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         b_rr[i] = __shfl(b_l, w * RB + (lane / 16) * 4 + i, kWave);
     }
     float pv[C / RB][4];
-#pragma unroll
-    for (int ct = 0; ct < C / RB; ++ct) {
-        f32x4v kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
-        if (ct <= w) {
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
-                const int off = frag_off(KS, ct, ks, lane);
-                const Split8 bs = read_split8(s_bh + off, s_bl + off);
-                kk = mma3(ka[ks], bs, kk);
-                qk = mma3(qa[ks], bs, qk);
-            }
-        }
-        // D layout: rows w*16 + (l/16)*4 + i, column ct*16 + l%16
+    // D layout: rows w*16 + (l/16)*4 + i, column ct*16 + l%16
+    const auto put_tile = [&](int ct, const f32x4v &kk, const f32x4v &qk, float (&pvc)[4]) {
         const int col = ct * RB + lane % 16;
         const float g_c = __shfl(g, col, kWave);
 #pragma unroll
@@ -710,7 +871,47 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             // products already (per key)
             const float dec = (live && col <= r) ? (kPerKey ? 1.f : exp_pk(g_rr[i] - g_c)) : 0.f;
             s_A[a_idx(r, col)] = (kDelta && col < r) ? b_rr[i] * dec * kk[i] : 0.f;
-            pv[ct][i] = dec * qk[i];
+            pvc[i] = dec * qk[i];
+        }
+    };
+#pragma unroll
+    for (int ct = 0; ct < C / RB; ++ct) {
+        f32x4v kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+        if (ct <= w) {
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const int off = frag_off(KS, ct, ks, lane);
+                Split8 bs;
+                if constexpr (kPerKey) {
+                    float bv[8], mv[8];
+                    lds_read8(s_b32 + off, bv);
+                    lds_read8(s_tab + TM + (w * (w + 1) / 2 + ct) * DK + ks * 32 + cq, mv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bv[e] *= mv[e];
+                    bs = split8(bv);
+                } else {
+                    bs = read_split8(s_bh + off, s_bl + off);
+                }
+                if constexpr (kDelta) kk = mma3(ka[ks], bs, kk);
+                qk = mma3(qa[ks], bs, qk);
+            }
+        }
+        if (kPerKey && slow && ct == w) {
+            kk = kk_diag;
+            qk = qk_diag;
+        }
+        put_tile(ct, kk, qk, pv[ct]);
+    }
+    if constexpr (kPerKey) {
+        // this row's K~ = K. e^{g_L - g} = (column operand) e^{g_L - g15},
+        // read back before s_k is reused
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float bv[8], ev[8];
+            lds_read8(s_b32 + frag_off(KS, w, ks, lane), bv);
+            lds_read8(s_tab + TEL + w * DK + ks * 32 + cq, ev);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kf[ks][e] = bv[e] * ev[e];
         }
     }
     __syncthreads();  // s_A complete; the K rows in s_k are no longer needed

@@ -182,6 +182,57 @@ def test_ragged_fork_per_key(variant, d, io):
     compare(g, r, inp, TOL if io == "bf16" else TOL_F32)
 
 
+def _decays(case, shape, rng):
+    """Per-key log a for the any-decay tests: 'strong' U(-3, -0.5) (a chunk
+    decays by up to e^-190, the join factors stay in range); 'sum_1000'
+    U(-16, -15.2) (chunk sums near -1000: every row block takes the direct
+    diagonal); 'resets' U(-0.1, -0.001) with 5% of entries at -1000; 'one_key'
+    key 0 at U(-40, -30), the rest U(-0.1, -0.001)."""
+    if case == "strong":
+        return rng.uniform(-3.0, -0.5, shape)
+    if case == "sum_1000":
+        return rng.uniform(-16.0, -15.2, shape)
+    mild = rng.uniform(-0.1, -0.001, shape)
+    if case == "resets":
+        return np.where(rng.random(shape) < 0.05, -1000.0, mild)
+    mild[..., 0] = rng.uniform(-40.0, -30.0, shape[:-1])
+    return mild
+
+
+@pytest.mark.parametrize("variant", ["kda", "rwkv6"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("case", ["strong", "sum_1000", "resets", "one_key"])
+def test_per_key_any_decay(variant, d, case):
+    """Per-key prefill + branches stay within the bar for any decay: the
+    ragged layout with random initial states, conv + q/k norm, bf16, and
+    per-key log a from _decays (down to chunk sums of -1000 and single
+    steps of -1000)."""
+    prefix = [0, 1, 3, 64, 65, 130, 200]
+    branches = [5, 1, 64, 70, 9, 128]
+    parent = [0, 1, 2, 3, 4, 6]
+    H = 2
+    inp = gi.seq_inputs(prefix, branches, parent, H, d, d, io="bf16", conv=True, per_key=True,
+                        seed=d + 31)
+    rng = np.random.default_rng(d + 32)
+    inp.log_alpha = _decays(case, inp.log_alpha.shape, rng).astype(np.float32)
+    s0 = (rng.standard_normal((len(prefix), H, d, d)) * 0.1).astype(np.float32)
+    g = run_fork(inp, init_state=s0, variant=variant)
+    r = run_oracle(inp, init_state=s0, variant=variant)
+    compare(g, r, inp, TOL)
+
+
+@pytest.mark.parametrize("variant", ["kda", "rwkv6"])
+def test_per_key_strong_decay_f32(variant):
+    """fp32 I/O at per-key log a ~ U(-3, -0.5), d = 128, held to the fp32
+    bar."""
+    prefix = [64, 130, 200]
+    branches = [64, 7, 70]
+    parent = [0, 1, 2]
+    inp = gi.seq_inputs(prefix, branches, parent, 2, 128, 128, io="f32", conv=True,
+                        per_key=True, la_range=(-3.0, -0.5), seed=41)
+    compare(run_fork(inp, variant=variant), run_oracle(inp, variant=variant), inp, TOL_F32)
+
+
 @pytest.mark.parametrize("variant", ["kda", "rwkv6"])
 def test_long_context_per_key(variant):
     """Per-key decay over long contexts (16+ chunks per sequence), H=4,
