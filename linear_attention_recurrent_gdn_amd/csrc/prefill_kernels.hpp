@@ -24,11 +24,13 @@
 // Column j of U, O, Sig depends only on column j of V and Sig0, so value
 // tiles are independent.
 //
-// Every contraction runs on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16)
-// with split-bf16 operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi),
-// and a.b ~ hi.hi + hi.lo + lo.hi accumulated in fp32 -- about 2^-16
-// relative per product, where a single bf16 product (2^-9) would not meet a
-// 2e-3 end-to-end tolerance.
+// Every contraction runs on the gfx950 matrix cores. With bf16 I/O the
+// operands are split bf16 (v_mfma_f32_16x16x32_bf16): x = hi + lo with
+// hi = bf16(x), lo = bf16(x - hi), and a.b ~ hi.hi + hi.lo + lo.hi
+// accumulated in fp32 -- about 2^-16 relative per product, where a single
+// bf16 product (2^-9) would not meet a 2e-3 end-to-end tolerance. With fp32
+// I/O they are the fp32 values (v_mfma_f32_16x16x4f32, eight per 16x16x32
+// step), in the same 4 bytes per element (see Frag).
 //
 // Kernels:
 //   plan  -- one workgroup: per-sequence chunk offsets (prefix sum of
@@ -62,45 +64,98 @@ constexpr float kNormEps = 1e-6f;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-// ------------------------------------------------------------ split-bf16 MFMA
-struct Split8 {
+// ------------------------------------------------------------ MFMA operands
+// A lane's piece of a 16x16x32 MFMA operand: 8 values (A layout: row l % 16,
+// k = 8 (l / 16) + e; B layout the same with column for row). Two forms,
+// both 32 bytes, kept in two "planes" (hi, lo) of 16 bytes per 8 elements:
+//  - F = false (bf16 I/O): x = hi + lo split into bf16 (round to nearest
+//    even, then the residual rounded); products take three bf16 MFMAs
+//    (hi hi + hi lo + lo hi), about 16 bits of each operand;
+//  - F = true (fp32 I/O): the fp32 values themselves, elements 0..3 in the
+//    hi plane's 16 bytes and 4..7 in the lo plane's; products take eight
+//    fp32 MFMAs (16x16x4, k split by e: the e-th takes k = 8 g + e of the
+//    four lane groups g), exact fp32 products.
+template <bool F> struct Frag;
+template <> struct Frag<false> {
     bf16x8 hi, lo;
 };
+template <> struct Frag<true> {
+    f32x4v hi, lo;
+};
 
-__device__ __forceinline__ Split8 split8(const float (&x)[8]) {
-    Split8 s;
+template <bool F>
+__device__ __forceinline__ Frag<F> frag(const float (&x)[8]) {
+    Frag<F> s;
+    if constexpr (F) {
+        s.hi = f32x4v{x[0], x[1], x[2], x[3]};
+        s.lo = f32x4v{x[4], x[5], x[6], x[7]};
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)x[e];
-        s.hi[e] = h;
-        s.lo[e] = (__bf16)(x[e] - (float)h);
+        for (int e = 0; e < 8; ++e) {
+            const __bf16 h = (__bf16)x[e];
+            s.hi[e] = h;
+            s.lo[e] = (__bf16)(x[e] - (float)h);
+        }
     }
     return s;
 }
 
-// c += a . b for 16x16 tiles with K = 32, fp32-faithful via three products
-__device__ __forceinline__ f32x4v mma3(const Split8 &a, const Split8 &b, f32x4v c) {
+// c += a . b for 16x16 tiles with K = 32
+__device__ __forceinline__ f32x4v mma(const Frag<false> &a, const Frag<false> &b, f32x4v c) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
     return c;
 }
-
-// 8 consecutive bf16 of a hi plane and the matching lo plane (16-byte aligned)
-__device__ __forceinline__ Split8 read_split8(const __bf16 *hi, const __bf16 *lo) {
-    Split8 s;
-    s.hi = *reinterpret_cast<const bf16x8 *>(hi);
-    s.lo = *reinterpret_cast<const bf16x8 *>(lo);
-    return s;
+__device__ __forceinline__ f32x4v mma(const Frag<true> &a, const Frag<true> &b, f32x4v c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+    return c;
 }
 
-// 4 consecutive values -> hi / lo bf16 (one 8-byte store each; 8-byte aligned)
+// The 8 elements at element offset o (a multiple of 8) of a plane pair
+// (16-byte aligned): read, written.
+template <bool F>
+__device__ __forceinline__ Frag<F> read_frag(const __bf16 *hi, const __bf16 *lo) {
+    Frag<F> s;
+    s.hi = *reinterpret_cast<const decltype(s.hi) *>(hi);
+    s.lo = *reinterpret_cast<const decltype(s.lo) *>(lo);
+    return s;
+}
+template <bool F>
+__device__ __forceinline__ void store_frag(__bf16 *hi, __bf16 *lo, const Frag<F> &s) {
+    *reinterpret_cast<decltype(s.hi) *>(hi) = s.hi;
+    *reinterpret_cast<decltype(s.lo) *>(lo) = s.lo;
+}
+
+// One element at element offset o of a plane pair.
+template <bool F>
+__device__ __forceinline__ void put1(__bf16 *hi, __bf16 *lo, int o, float x) {
+    if constexpr (F) {
+        float *const p = reinterpret_cast<float *>(((o & 7) < 4 ? hi : lo) + (o & ~7));
+        p[o & 3] = x;
+    } else {
+        const __bf16 h = (__bf16)x;
+        hi[o] = h;
+        lo[o] = (__bf16)(x - (float)h);
+    }
+}
+
+// 4 consecutive elements at element offset o (a multiple of 4) of a plane
+// pair: one 8-byte store per plane (bf16), one 16-byte store (fp32).
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void split4_store(f32x4v x, __bf16 *hi, __bf16 *lo) {
-    const bf16x4 h = __builtin_convertvector(x, bf16x4);
-    const bf16x4 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4v), bf16x4);
-    *reinterpret_cast<bf16x4 *>(hi) = h;
-    *reinterpret_cast<bf16x4 *>(lo) = l;
+template <bool F>
+__device__ __forceinline__ void put4(__bf16 *hi, __bf16 *lo, int o, f32x4v x) {
+    if constexpr (F) {
+        *reinterpret_cast<f32x4v *>(((o & 7) < 4 ? hi : lo) + (o & ~7)) = x;
+    } else {
+        const bf16x4 h = __builtin_convertvector(x, bf16x4);
+        const bf16x4 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4v), bf16x4);
+        *reinterpret_cast<bf16x4 *>(hi + o) = h;
+        *reinterpret_cast<bf16x4 *>(lo + o) = l;
+    }
 }
 
 __device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
@@ -119,8 +174,8 @@ __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
 }
 
 // ------------------------------------------------------------ workspace
-// Per (chunk, head) record written by the prep kernel for the scan, split
-// once here into hi / lo bf16 planes:
+// Per (chunk, head) record written by the prep kernel for the scan, as
+// hi / lo plane pairs of MFMA operands (split bf16, or fp32, see Frag):
 //   T', P  [C][C] lower triangular, only their 16 x 32 blocks at or below
 //          the diagonal, in the order the 16x16x32 MFMA reads an A operand
 //          (tri_off)
@@ -605,7 +660,7 @@ __device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], 
 // [rows][C], or in A-fragment order (FRAG: a lower-triangular C x C matrix,
 // T' or P, of which only the 16 x 32 blocks at or below the diagonal are
 // kept, tri_off).
-template <int ROWS, bool FRAG = false>
+template <int ROWS, bool F, bool FRAG = false>
 __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 *lo) {
     constexpr int G = C / 8;  // 8-element groups per row
     for (int idx = threadIdx.x; idx < ROWS * G; idx += kThreads) {
@@ -614,11 +669,9 @@ __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = src[r * (C + 1) + c0 + e];
-        const Split8 sp = split8(x);
         const int off = FRAG ? tri_off(r / 16, c0 / 32, r % 16 + 16 * ((c0 % 32) / 8))
                              : r * C + c0;
-        *reinterpret_cast<bf16x8 *>(hi + off) = sp.hi;
-        *reinterpret_cast<bf16x8 *>(lo + off) = sp.lo;
+        store_frag<F>(hi + off, lo + off, frag<F>(x));
     }
 }
 
@@ -626,6 +679,7 @@ template <int DK, typename TI, int VAR>
 __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     constexpr bool kPerKey = VAR != kScalar;
     constexpr bool kDelta = VAR != kRwkv6;
+    constexpr bool F = std::is_same<TI, float>::value;  // fp32 operands (see Frag)
     constexpr int KS = DK / 32;
     constexpr int KP = DK + 4;  // padded row of the staged K rows
     // staged K rows [C][KP]; then K~^T [DK][C + 1]; then P and T' [C][C + 1]
@@ -759,7 +813,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     // operand, kept in fp32 in s_b32); a tile (R, S) joins the two with the
     // per-key factor e^{g0[R] - g15[S]} (<= 1 off the diagonal). The record
     // keeps the forms from the chunk start, Q^ = Q. e^{g}, K^ = K. e^{g}.
-    Split8 qa[DK / 32], ka[DK / 32];
+    Frag<F> qa[DK / 32], ka[DK / 32];
     float *const s_b32 = s_k;  // per key: the column operands [C][DK], fragment order
     float e1[kPerKey ? DK / 32 : 1][8];
     if constexpr (kPerKey) {
@@ -793,14 +847,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
                     qf[ks][e] *= e1[ks][e];
                     qr[e] = qf[ks][e] * eg[e];  // Q^
                 }
-                qa[ks] = split8(qf[ks]);
-                const Split8 rs = split8(qr);
-                *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = rs.hi;
-                *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = rs.lo;
+                qa[ks] = frag<F>(qf[ks]);
+                store_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off, frag<F>(qr));
             } else {
-                qa[ks] = split8(qf[ks]);
-                *reinterpret_cast<bf16x8 *>(rec + RL.qhi + off) = qa[ks].hi;
-                *reinterpret_cast<bf16x8 *>(rec + RL.qlo + off) = qa[ks].lo;
+                qa[ks] = frag<F>(qf[ks]);
+                store_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off, qa[ks]);
             }
         }
     }
@@ -830,21 +881,17 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
                 kr[e] = kDelta ? ak[e] * eg[e] : 0.f;
                 bk[e] = kf[ks][e] * exp_pk(g15v[e] - gr[ks][e]);
             }
-            ka[ks] = split8(ak);
-            const Split8 rs = split8(kr);
-            *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = rs.hi;
-            *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = rs.lo;
+            ka[ks] = frag<F>(ak);
+            store_frag<F>(rec + RL.khi + off, rec + RL.klo + off, frag<F>(kr));
             *reinterpret_cast<f32x4v *>(s_b32 + off) = f32x4v{bk[0], bk[1], bk[2], bk[3]};
             *reinterpret_cast<f32x4v *>(s_b32 + off + 4) = f32x4v{bk[4], bk[5], bk[6], bk[7]};
         } else {
             // A operand of KK^T and the scan's K Sig term: K; the B operand
             // rows of KK^T and QK^T, split once, in fragment order: the
             // reader of row block ct takes lane l's piece of wave ct
-            ka[ks] = split8(kf[ks]);
-            *reinterpret_cast<bf16x8 *>(rec + RL.khi + off) = ka[ks].hi;
-            *reinterpret_cast<bf16x8 *>(rec + RL.klo + off) = ka[ks].lo;
-            *reinterpret_cast<bf16x8 *>(s_bh + off) = ka[ks].hi;
-            *reinterpret_cast<bf16x8 *>(s_bl + off) = ka[ks].lo;
+            ka[ks] = frag<F>(kf[ks]);
+            store_frag<F>(rec + RL.khi + off, rec + RL.klo + off, ka[ks]);
+            store_frag<F>(s_bh + off, s_bl + off, ka[ks]);
         }
     }
     __syncthreads();
@@ -881,19 +928,19 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
                 const int off = frag_off(KS, ct, ks, lane);
-                Split8 bs;
+                Frag<F> bs;
                 if constexpr (kPerKey) {
                     float bv[8], mv[8];
                     lds_read8(s_b32 + off, bv);
                     lds_read8(s_tab + TM + (w * (w + 1) / 2 + ct) * DK + ks * 32 + cq, mv);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) bv[e] *= mv[e];
-                    bs = split8(bv);
+                    bs = frag<F>(bv);
                 } else {
-                    bs = read_split8(s_bh + off, s_bl + off);
+                    bs = read_frag<F>(s_bh + off, s_bl + off);
                 }
-                if constexpr (kDelta) kk = mma3(ka[ks], bs, kk);
-                qk = mma3(qa[ks], bs, qk);
+                if constexpr (kDelta) kk = mma(ka[ks], bs, kk);
+                qk = mma(qa[ks], bs, qk);
             }
         }
         if (kPerKey && slow && ct == w) {
@@ -923,7 +970,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) s_k[(ks * 32 + cq + e) * (C + 1) + row] = kf[ks][e];
         __syncthreads();
-        put_planes<DK>(s_k, rec + RL.kthi, rec + RL.ktlo);
+        put_planes<DK, F>(s_k, rec + RL.kthi, rec + RL.ktlo);
     }
 
     // T = (I + A)^-1, one column per group of 4 lanes (columns are
@@ -958,8 +1005,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
 #pragma unroll
     for (int q = 0; q < C / 4; ++q) s_T[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
     __syncthreads();
-    put_planes<C, true>(s_P, rec + RL.phi, rec + RL.plo);
-    put_planes<C, true>(s_T, rec + RL.thi, rec + RL.tlo);
+    put_planes<C, F, true>(s_P, rec + RL.phi, rec + RL.plo);
+    put_planes<C, F, true>(s_T, rec + RL.thi, rec + RL.tlo);
 }
 
 template <int DK, typename TI>
@@ -1045,12 +1092,17 @@ __device__ __forceinline__ int kt_off(int d, int r) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The 8 split values of a lane's A-operand piece (chunk row r, keys d0 ..
-// d0 + 7, d0 a multiple of 8) into the K^T planes, one bf16 per store (the
-// halves of each 32-bit word are written from the word itself). For such d0
-// the swizzle of key d0 + e is sw(d0) ^ (e >> 1), so the 8 stores of a plane
-// use 4 base offsets and constant displacements.
-__device__ __forceinline__ void put_kt(const Split8 &x, int d0, int r, __bf16 *kh, __bf16 *kl) {
+// The 8 values of a lane's A-operand piece (chunk row r, keys d0 .. d0 + 7,
+// d0 a multiple of 8) into the K^T planes. Split bf16: one bf16 per store
+// (the halves of each 32-bit word are written from the word itself); for
+// such d0 the swizzle of key d0 + e is sw(d0) ^ (e >> 1), so the 8 stores
+// of a plane use 4 base offsets and constant displacements. fp32: one
+// element per store (put1).
+__device__ __forceinline__ void put_kt(const Frag<true> &x, int d0, int r, __bf16 *kh, __bf16 *kl) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) put1<true>(kh, kl, kt_off(d0 + e, r), e < 4 ? x.hi[e] : x.lo[e - 4]);
+}
+__device__ __forceinline__ void put_kt(const Frag<false> &x, int d0, int r, __bf16 *kh, __bf16 *kl) {
     const u32x4 h = __builtin_bit_cast(u32x4, x.hi);
     const u32x4 l = __builtin_bit_cast(u32x4, x.lo);
     const int sw = ((d0 >> 1) & 7) ^ (((d0 >> 4) & 1) << 1);
@@ -1079,19 +1131,10 @@ __device__ __forceinline__ int st_off(int v, int key) {
     return v * DK + ((((key >> 3) ^ (v >> S)) & (P - 1)) << 3) + (key & 7);
 }
 
-// x = hi + lo as bf16 bit patterns (round to nearest even, then the exact
-// residual rounded).
-__device__ __forceinline__ void split1(float x, uint16_t &h, uint16_t &l) {
-    const __bf16 hb = (__bf16)x;
-    const __bf16 lb = (__bf16)(x - (float)hb);
-    h = __builtin_bit_cast(uint16_t, hb);
-    l = __builtin_bit_cast(uint16_t, lb);
-}
-
 template <int KS, int NVT, typename TI>
 struct ChunkRegs {
     static_assert(NVT == 2, "a lane holds one adjacent pair of value columns");
-    Split8 ka[KS], qa[KS], ta[2], pa[2];
+    Frag<std::is_same<TI, float>::value> ka[KS], qa[KS], ta[2], pa[2];
     typename VPair<TI>::type vraw[7];  // raw V rows r0-3 .. r0+3 of this lane's column pair
     f32x4v gam;       // scalar decay: gamma_r of this lane's 4 rows (C/D layout)
     f32x4v gu;        // scalar decay: e^{g_L - g_r} of the same rows
@@ -1107,6 +1150,7 @@ struct ChunkRegs {
 // a separate instance so the plain scan keeps its register budget.
 template <int DK, int DV, typename TI, typename TO, bool PK, bool CK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void scan_kernel(PrefillArgs a) {
+    constexpr bool F = std::is_same<TI, float>::value;  // fp32 operands (see Frag)
     constexpr int KS = DK / 32;          // k-steps over d_k
     constexpr int CB = C + 8;            // padded row of the R^T / U^T / W^T planes
     constexpr int NVT = TV / 16;         // 16-wide value sub-tiles
@@ -1188,15 +1232,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     float mst[NEG][4];
     // the split planes of the state from the registers
     auto put_split = [&](int lane) {
-        uint16_t *ph = reinterpret_cast<uint16_t *>(s_Sh), *pl = reinterpret_cast<uint16_t *>(s_Sl);
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
             const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = st_off<DK>(t * 16 + (lane / 16) * 4 + i, key);
-                split1(mst[m][i], ph[o], pl[o]);
-            }
+            for (int i = 0; i < 4; ++i)
+                put1<F>(s_Sh, s_Sl, st_off<DK>(t * 16 + (lane / 16) * 4 + i, key), mst[m][i]);
         }
     };
     // the state tile [DK][TV] of this workgroup into a [DK][DV] state at
@@ -1263,15 +1304,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int off = frag_off(KS, w, ks, lane);
-            r.ka[ks] = read_split8(rec + RL.khi + off, rec + RL.klo + off);
-            if (want_o) r.qa[ks] = read_split8(rec + RL.qhi + off, rec + RL.qlo + off);
+            r.ka[ks] = read_frag<F>(rec + RL.khi + off, rec + RL.klo + off);
+            if (want_o) r.qa[ks] = read_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off);
         }
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq)
             if (kq <= kmax) {
                 const int off = tri_off(w, kq, lane);
-                r.ta[kq] = read_split8(rec + RL.thi + off, rec + RL.tlo + off);
-                if (want_o) r.pa[kq] = read_split8(rec + RL.phi + off, rec + RL.plo + off);
+                r.ta[kq] = read_frag<F>(rec + RL.thi + off, rec + RL.tlo + off);
+                if (want_o) r.pa[kq] = read_frag<F>(rec + RL.phi + off, rec + RL.plo + off);
             }
         {
             const int j = j0 + 2 * (lane % 16);  // columns j, j + 1 (even: pair-aligned)
@@ -1385,16 +1426,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int so = st_off<DK>(t * 16 + lane % 16, ks * 32 + acol);
-                const Split8 bs = read_split8(s_Sh + so, s_Sl + so);
-                acc = mma3(cur.ka[ks], bs, acc);
-                if (want_o) acc_o[t] = mma3(cur.qa[ks], bs, acc_o[t]);
+                const Frag<F> bs = read_frag<F>(s_Sh + so, s_Sl + so);
+                acc = mma(cur.ka[ks], bs, acc);
+                if (want_o) acc_o[t] = mma(cur.qa[ks], bs, acc_o[t]);
             }
             // the lane's 4 rows are consecutive in the R^T planes
             f32x4v rv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) rv[i] = vf[t][i] - gam[i] * acc[i];
             const int ro = (t * 16 + lane % 16) * CB + r0v;
-            split4_store(rv, s_Rh + ro, s_Rl + ro);
+            put4<F>(s_Rh, s_Rl, ro, rv);
         }
         // Per key, this wave's direct-to-LDS copies of K~^T are its only
         // vector memory operations in flight here: finish them before this
@@ -1414,14 +1455,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int kq = 0; kq < 2; ++kq)
                 if (kq <= kmax) {
                     const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
-                    acc = mma3(cur.ta[kq], read_split8(s_Rh + off, s_Rl + off), acc);
+                    acc = mma(cur.ta[kq], read_frag<F>(s_Rh + off, s_Rl + off), acc);
                 }
             const int uo = (t * 16 + lane % 16) * CB + r0v;
-            split4_store(acc, s_Uh + uo, s_Ul + uo);
+            put4<F>(s_Uh, s_Ul, uo, acc);
             if constexpr (!PK) {  // W = diag(e^{g_L - g}) U for the state update
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] *= cur.gu[i];
-                split4_store(acc, s_Wh + uo, s_Wl + uo);
+                put4<F>(s_Wh, s_Wl, uo, acc);
             }
         }
         __syncthreads();
@@ -1437,7 +1478,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int kq = 0; kq < 2; ++kq)
                     if (kq <= kmax) {
                         const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
-                        acc_o[t] = mma3(cur.pa[kq], read_split8(s_Uh + off, s_Ul + off), acc_o[t]);
+                        acc_o[t] = mma(cur.pa[kq], read_frag<F>(s_Uh + off, s_Ul + off), acc_o[t]);
                     }
             }
         }
@@ -1472,8 +1513,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
                 const int ok = PK ? kt_swz(dt * 16 + lane % 16, kq * 4 + lane / 16)
                                   : kt_off(dt * 16 + lane % 16, kq * 32 + acol);
-                acc = PK ? mma3(read_split8(s_Uh + ou, s_Ul + ou), read_split8(s_Kh + ok, s_Kl + ok), acc)
-                         : mma3(read_split8(s_Wh + ou, s_Wl + ou), read_split8(s_Kh + ok, s_Kl + ok), acc);
+                acc = PK ? mma(read_frag<F>(s_Uh + ou, s_Ul + ou), read_frag<F>(s_Kh + ok, s_Kl + ok), acc)
+                         : mma(read_frag<F>(s_Wh + ou, s_Wl + ou), read_frag<F>(s_Kh + ok, s_Kl + ok), acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) mst[m][i] = acc[i];

@@ -28,3 +28,10 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    path = os.environ.get("GDN_PARITY_JSON")
+    if path:
+        import _parity
+        _parity.write(path)

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import _parity
 import gdn_inputs as gi
 import linear_attention_recurrent_gdn_amd as gdn
 import oracle
@@ -43,6 +44,16 @@ def test_decode_small_whole_workload():
     for t in range(T):
         gdn.gdn_decode_eager(q[t], k[t], v[t], la[t], beta[t], state, o[t])
     torch.cuda.synchronize()
+    cfg = "C2 decode_small (whole workload)"
+
+    def rec(sched, o_g, st_g):
+        og, sg = host64(o_g), host64(st_g)
+        _parity.record(cfg, f"o {sched}", _parity.rel_err(og, o_ref, (0, 3)),
+                       _parity.elementwise(og, o_ref, (0, 3)), TOL)
+        _parity.record(cfg, f"state {sched}", _parity.rel_err(sg, st_ref, (2, 3)),
+                       _parity.elementwise(sg, st_ref, (2, 3)), TOL)
+
+    rec("eager", o, state)
     errs = {"eager": (oracle.rel_err(host64(o), o_ref, (0, 3)),
                       oracle.rel_err(host64(state), st_ref, (2, 3)))}
     for M in w["Ms"]:
@@ -58,11 +69,12 @@ def test_decode_small_whole_workload():
         torch.cuda.synchronize()
         errs[f"M={M}"] = (oracle.rel_err(host64(o), o_ref, (0, 3)),
                           oracle.rel_err(host64(base), st_ref, (2, 3)))
+        rec(f"M={M}", o, base)
     print({k_: f"o {a:.2e} state {b:.2e}" for k_, (a, b) in errs.items()}, flush=True)
     assert all(max(e) <= TOL for e in errs.values()), errs
 
 
-def _sampled_deferred(B, H, d, T, M, *, per_key, variant, phases, sample, seed=0):
+def _sampled_deferred(B, H, d, T, M, *, per_key, variant, phases, sample, seed=0, config=None):
     t_in = gi.torch_decode_inputs(B, H, d, d, T, per_key=per_key, seed=seed)
     rng = np.random.default_rng(seed + 1)
     phase = rng.integers(0, M, size=B) if phases else np.zeros(B, dtype=np.int64)
@@ -98,8 +110,12 @@ def _sampled_deferred(B, H, d, T, M, *, per_key, variant, phases, sample, seed=0
                                      pick(t_in["log_alpha"]),
                                      None if beta is None else pick(t_in["beta"]), s0,
                                      variant=variant)
-    e_o = oracle.rel_err(host64(o_s), o_ref, (0, 3))
-    e_s = oracle.rel_err(host64(base.index_select(0, sel)), st_ref, (2, 3))
+    og, sg = host64(o_s), host64(base.index_select(0, sel))
+    e_o = oracle.rel_err(og, o_ref, (0, 3))
+    e_s = oracle.rel_err(sg, st_ref, (2, 3))
+    if config is not None:
+        _parity.record(config, "o", e_o, _parity.elementwise(og, o_ref, (0, 3)), TOL)
+        _parity.record(config, "state", e_s, _parity.elementwise(sg, st_ref, (2, 3)), TOL)
     return e_o, e_s
 
 
@@ -109,7 +125,8 @@ def test_decode_large_sampled():
     w = gi.WORKLOADS["decode_large"]
     sample = [0, 37, 101, 128, 170, 203, 241, 255]
     e_o, e_s = _sampled_deferred(w["B"], w["H"], w["d"], w["steps"], w["M"], per_key=False,
-                                 variant="gdn", phases=True, sample=sample)
+                                 variant="gdn", phases=True, sample=sample,
+                                 config="C4 decode_large (8 of 256 slots, all heads and steps)")
     print(f"decode_large: o {e_o:.2e} state {e_s:.2e}", flush=True)
     assert e_o <= TOL and e_s <= TOL
 
@@ -120,6 +137,7 @@ def test_perkey_sampled(variant):
     w = gi.WORKLOADS["perkey"]
     sample = [0, 19, 50, 64, 77, 99, 111, 127]
     e_o, e_s = _sampled_deferred(w["B"], w["H"], w["d"], w["steps"], w["M"], per_key=True,
-                                 variant=variant, phases=True, sample=sample)
+                                 variant=variant, phases=True, sample=sample,
+                                 config=f"C5 perkey {variant} (8 of 128 slots, all heads and steps)")
     print(f"perkey {variant}: o {e_o:.2e} state {e_s:.2e}", flush=True)
     assert e_o <= TOL and e_s <= TOL
