@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--only-attention", action="store_true",
                     help="profiling aid: run only the fork-attention round (warmup + steps "
                          "calls), report its time on stderr, print no JSON line")
+    ap.add_argument("--attention-requests", type=int, default=None,
+                    help="with --only-attention: requests of the fork_prefill shape (default 8)")
     ap.add_argument("--only-fork", action="store_true",
                     help="profiling aid: run only the two-call fork (fork-reps timed rounds) "
                          "and the device-copy probe, report on stderr, print no JSON line")
@@ -224,7 +226,19 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
     C = w["chunk"]
     mac = 5 * C * d + 3 * d * d + C * C / 6
     pre_tflops = Np * H * 2 * mac / (tp_ms / 1e3) / 1e12
-    return dict(branches=NB, prefill_ms=tp_ms, fork_ms=tf_ms,
+    # roofline of call 1 (plan + prep + scan): HBM-bound at the algorithmic
+    # level (about 141 issued FLOP per byte against the bf16 ridge of
+    # 2500 / 8 = 312): bytes the recurrence must move per token-head are q,
+    # k, v (bf16), log a and beta (fp32), o (fp32)
+    alg_bytes = Np * H * (3 * d * 2 + 8 + d * 4)
+    achieved = alg_bytes / (tp_ms / 1e3) / 1e9
+    traffic = prefill_traffic() if variant == "gdn" else None
+    roofline = {"bound": "hbm", "kernels": "plan + prep + scan (the prefix prefill call)",
+                "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "algorithmic_bytes": alg_bytes,
+                "traffic": traffic,
+                "traffic_over_algorithmic": None if traffic is None else traffic / alg_bytes}
+    return dict(branches=NB, prefill_ms=tp_ms, fork_ms=tf_ms, prefill_roofline=roofline,
                 fork_with_states_ms=tfs_ms,
                 branches_per_s_with_states=NB / ((tp_ms + tfs_ms) / 1e3),
                 prefill_dense_tile_tflops=pre_tflops,
@@ -239,13 +253,16 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD public figure
 
 
-def bench_fork_attention(torch, gdn, gi, reps, warmup=1, branches_only=True):
+def bench_fork_attention(torch, gdn, gi, reps, warmup=1, branches_only=True, requests=None):
     """The softmax-attention half of the fork on the fork_prefill stream (8
     requests x 8192-token trunks, 20 branches of 64 tokens each, H=16, d=128,
     bf16): one gdn_fork_attention call over the whole stream (trunks and
-    branches), and the branch round alone (trunks as keys only)."""
+    branches), and the branch round alone (trunks as keys only). `requests`
+    takes fewer requests of the same shape (a shorter launch, e.g. for
+    counters that would saturate on the full round)."""
     w = gi.WORKLOADS["fork_prefill"]
     R, H, d, P, Lb = w["R"], w["H"], w["d"], w["prefix"], w["branch_len"]
+    R = R if requests is None else requests
     pl, bl, par = gi.fork_layout(R, P, w["branches_per_req"], Lb)
     t = gi.torch_attention_inputs(pl, bl, par, H=H, Hkv=H, d=d, seed=0)
     N, NB = t["q"].shape[0], len(bl)
@@ -275,7 +292,7 @@ def bench_fork_attention(torch, gdn, gi, reps, warmup=1, branches_only=True):
         out[name] = dict(ms=ms, branches_per_s=NB / (ms / 1e3), useful_tflops=useful,
                          mfma_issued_tflops=1.5 * useful,
                          frac_of_bf16_peak=1.5 * useful / BF16_MFMA_PEAK_TFLOPS)
-    out["workload"] = ("fork attention: 8 x 8192-token trunks + 160 branches x 64 tokens, "
+    out["workload"] = (f"fork attention: {R} x 8192-token trunks + {NB} branches x 64 tokens, "
                        "H=16, d=128, bf16 q/k/v, fp32 o; split-bf16 probabilities (the "
                        "p.v products issue 2 MFMAs, so issued = 1.5 x useful)")
     return out
@@ -497,6 +514,22 @@ def cpu_fork_baseline(torch, gi):
                        f"{w['branch_len']} tokens, H={w['H']}, d={w['d']} ({dt:.1f} s)")
 
 
+def prefill_traffic():
+    """HBM bytes of one prefix prefill call on fork_prefill (prep + scan)
+    from the committed counter summaries, or None when the prefill sources
+    changed since the counters were taken."""
+    from linear_attention_recurrent_gdn_amd import profiling
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    total = 0.0
+    for name in ("fork_prefill_prep_traffic.md", "fork_prefill_scan_traffic.md"):
+        prof = profiling.read_profile_block(os.path.join(here, "profiles", name))
+        if not prof or prof.get("source_hash") != profiling.source_hash(profiling.PREFILL_SOURCES):
+            return None
+        total += prof["traffic_bytes"]
+    return total
+
+
 def measured_traffic(ms_per_launch):
     """HBM bytes per launch of the deferred kernel from the committed
     counter summary (two rocprofv3 --pmc passes, copy-calibrated), or None
@@ -536,7 +569,7 @@ def main():
         return
     if args.only_attention:
         res = bench_fork_attention(torch, gdn, gi, max(args.steps, 1), warmup=args.warmup,
-                                   branches_only=False)
+                                   branches_only=False, requests=args.attention_requests)
         log(json.dumps(res))
         return
     B, H, M, NSTEP = 256, 32, 8, 512

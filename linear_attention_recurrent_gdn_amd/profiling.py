@@ -2,7 +2,8 @@
 
     python -m linear_attention_recurrent_gdn_amd.profiling trace <kernel_trace.csv> <out.md> "<command>"
     python -m linear_attention_recurrent_gdn_amd.profiling counters <out.md> "<command>" \
-        <kernel-substring> <pass_dir> [<pass_dir> ...] [--sources attention|decode|prefill]
+        <kernel-substring> <pass_dir> [<pass_dir> ...] [--sources attention|decode|prefill] \
+        [--grid N]
     python -m linear_attention_recurrent_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
         <out.md> "<command>" <kernel-substring> [--grid N] [--copy-bytes B] [--sources decode|prefill]
 
@@ -134,11 +135,14 @@ def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_byte
     open(out_md, "w").write("\n".join(lines))
 
 
-def counters_summary(out_md, command, kernel_sub, pass_dirs, sources=ATTENTION_SOURCES):
+def counters_summary(out_md, command, kernel_sub, pass_dirs, sources=ATTENTION_SOURCES,
+                     grid=None):
     vals, kname = {}, None
     for d in pass_dirs:
         for r in _counter_rows(d):
             if kernel_sub not in r["Kernel_Name"]:
+                continue
+            if grid is not None and int(r["Grid_Size"]) != grid:
                 continue
             kname = kname or r["Kernel_Name"]
             vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
@@ -147,10 +151,11 @@ def counters_summary(out_md, command, kernel_sub, pass_dirs, sources=ATTENTION_S
     data = {c: statistics.mean(v) for c, v in sorted(vals.items())}
     lines = [f"# Counters: {os.path.basename(out_md)[:-3]}", "",
              "Command (one --pmc pass per counter group):", "", f"    {command}", "",
-             f"Kernel: `{_short(kname, 200)}` (mean per dispatch).", "",
+             f"Kernel: `{_short(kname, 200)}`" + (f", grid {grid}" if grid is not None else "")
+             + " (mean per dispatch).", "",
              "| counter | per dispatch |", "|---|---|"]
     lines += [f"| {c} | {v:.4g} |" for c, v in data.items()]
-    block = dict(kernel=kname, counters=data, source_hash=source_hash(sources))
+    block = dict(kernel=kname, grid=grid, counters=data, source_hash=source_hash(sources))
     lines += ["", "```json", json.dumps(block, indent=1), "```", ""]
     open(out_md, "w").write("\n".join(lines))
 
@@ -176,11 +181,13 @@ def main(argv):
     c.add_argument("kernel_sub")
     c.add_argument("pass_dirs", nargs="+")
     c.add_argument("--sources", choices=tuple(SOURCES), default="attention")
+    c.add_argument("--grid", type=int, default=None)
     a = ap.parse_args(argv)
     if a.mode == "trace":
         trace_summary(a.trace_csv, a.out_md, a.command)
     elif a.mode == "counters":
-        counters_summary(a.out_md, a.command, a.kernel_sub, a.pass_dirs, SOURCES[a.sources])
+        counters_summary(a.out_md, a.command, a.kernel_sub, a.pass_dirs, SOURCES[a.sources],
+                         grid=a.grid)
     else:
         traffic_summary(a.fetch_dir, a.write_dir, a.out_md, a.command, a.kernel_sub,
                         copy_bytes=a.copy_bytes, grid=a.grid,
