@@ -158,6 +158,42 @@ __device__ __forceinline__ void put4(__bf16 *hi, __bf16 *lo, int o, f32x4v x) {
     }
 }
 
+// 16x16x16 products (the blocked triangular inverse): a lane's piece is 4
+// values, k = 4 (l / 16) + e; split bf16 (three 16x16x16 bf16 MFMAs) or
+// fp32 (four 16x16x4 fp32 MFMAs, k split by e as in Frag).
+template <bool F> struct Frag4;
+template <> struct Frag4<false> {
+    bf16x4 hi, lo;
+};
+template <> struct Frag4<true> {
+    f32x4v v;
+};
+template <bool F>
+__device__ __forceinline__ Frag4<F> frag4(f32x4v x) {
+    Frag4<F> s;
+    if constexpr (F) {
+        s.v = x;
+    } else {
+        s.hi = __builtin_convertvector(x, bf16x4);
+        s.lo = __builtin_convertvector(x - __builtin_convertvector(s.hi, f32x4v), bf16x4);
+    }
+    return s;
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4v mma16(const Frag4<false> &a, const Frag4<false> &b, f32x4v c) {
+    const s16x4 ah = __builtin_bit_cast(s16x4, a.hi), al = __builtin_bit_cast(s16x4, a.lo);
+    const s16x4 bh = __builtin_bit_cast(s16x4, b.hi), bl = __builtin_bit_cast(s16x4, b.lo);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ f32x4v mma16(const Frag4<true> &a, const Frag4<true> &b, f32x4v c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+    return c;
+}
+
 __device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
     const float4 b = *reinterpret_cast<const float4 *>(p + 4);
@@ -618,30 +654,6 @@ __device__ __forceinline__ void diag_direct(const PrefillArgs &a, const ChunkSrc
     }
 }
 
-// Rows R0 + 1 .. C - 1 of the column solve of T = (I + A)^-1 (see prep_body):
-// t[q] holds T[4q + part][col]; arow points at this lane's j = part (mod 4)
-// group of row 0 of A (rows of AP floats). Row r needs the terms j < r,
-// i.e. q < ceil(r / 4); A is zero on and above the diagonal, so the last
-// group needs no mask.
-template <int R0, int AP>
-__device__ __forceinline__ void tri_solve(const float *arow, float (&t)[C / 4], int col, int part) {
-#pragma unroll
-    for (int r = R0 + 1; r < C; ++r) {
-        const int nq = (r + 3) / 4;
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < (nq + 3) / 4; ++i) {
-            const float4 av = *reinterpret_cast<const float4 *>(arow + r * AP + 4 * i);
-            if (4 * i < nq) acc0 = fmaf(av.x, t[4 * i], acc0);
-            if (4 * i + 1 < nq) acc1 = fmaf(av.y, t[4 * i + 1], acc1);
-            if (4 * i + 2 < nq) acc0 = fmaf(av.z, t[4 * i + 2], acc0);
-            if (4 * i + 3 < nq) acc1 = fmaf(av.w, t[4 * i + 3], acc1);
-        }
-        const float acc = quad_sum(acc0 + acc1);
-        if (r > col && r % 4 == part) t[r / 4] = -acc;
-    }
-}
-
 // VAR: the decay / update rule. kScalar: log a [N, H], the gated delta rule.
 // kKda: per-key log a [N, H, d_k], delta rule. kRwkv6: per-key log a, raw
 // value update (u = v: no A, T' = I, no K Sig term, beta unused).
@@ -973,37 +985,79 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         put_planes<DK, F>(s_k, rec + RL.kthi, rec + RL.ktlo);
     }
 
-    // T = (I + A)^-1, one column per group of 4 lanes (columns are
-    // independent): lane (col, part) keeps T[j][col] for j = part (mod 4),
-    // starting from the identity column; rows r <= col leave the column
-    // unchanged, so a wave starts after its first column. It runs while the
-    // K~^T stores drain (it reads only s_A).
-    const int col = w * 16 + lane / 4, part = lane % 4;
-    float t[C / 4];
-#pragma unroll
-    for (int q = 0; q < C / 4; ++q) t[q] = (q * 4 + part == col) ? 1.f : 0.f;
-    {
-        const float *arow = s_A + part * (C / 4);
-        switch (__builtin_amdgcn_readfirstlane(w)) {  // straight-line rows per wave
-            case 0: tri_solve<0, AP>(arow, t, col, part); break;
-            case 1: tri_solve<16, AP>(arow, t, col, part); break;
-            case 2: tri_solve<32, AP>(arow, t, col, part); break;
-            default: tri_solve<48, AP>(arow, t, col, part); break;
-        }
-    }
-    __syncthreads();  // every lane is done with s_k (the per-key K~^T copy-out)
-    // P (from registers) and T'[j][col] = T[j][col] beta_col, staged side by
-    // side in s_k for coalesced stores
+    // T = (I + A)^-1 by 16-row blocks (block row R = wave R), staged
+    // unscaled in s_T (the blocks at or below the diagonal; the two blocks
+    // above it that share a stored 16 x 32 block are zero):
+    //  1. T_RR = (I + A_RR)^-1 by forward substitution, one column per group
+    //     of 4 lanes: lane (cl, part) keeps T_RR[j][cl] for j = part (mod 4),
+    //     from the identity column (rows r <= cl leave it unchanged);
+    //  2. level by level (R - S = 1, 2, 3), T_RS = -T_RR sum_{S<=K<R} A_RK T_KS
+    //     on MFMA (16 x 16 x 16 products; the sum's output layout is the B
+    //     operand of the left product as it stands).
+    // Then T' = T diag(beta) in place.
+    if constexpr (kPerKey) __syncthreads();  // the K~^T copy-out has read s_k
     float *const s_P = s_k, *const s_T = s_k + C * (C + 1);
     static_assert(2 * C * (C + 1) <= SK, "P and T' staging fit s_k");
+    constexpr int TP = C + 1;  // s_T row pitch
+    {
+        const int cl = lane / 4, part = lane % 4;
+        float t[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = (4 * q + part == cl) ? 1.f : 0.f;
+        // A[16w + r][16w + 4q + part] = arow[r * AP + q] (a_idx groups j by j % 4)
+        const float *arow = s_A + (w * RB) * AP + part * (C / 4) + 4 * w;
+#pragma unroll
+        for (int r = 1; r < RB; ++r) {
+            const float4 av = *reinterpret_cast<const float4 *>(arow + r * AP);
+            float acc = 0.f;
+            if (part < r) acc = fmaf(av.x, t[0], acc);
+            if (4 + part < r) acc = fmaf(av.y, t[1], acc);
+            if (8 + part < r) acc = fmaf(av.z, t[2], acc);
+            if (12 + part < r) acc = fmaf(av.w, t[3], acc);
+            acc = quad_sum(acc);
+            if (r > cl && r % 4 == part) t[r / 4] = -acc;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_T[(w * RB + 4 * q + part) * TP + w * RB + cl] = t[q];
+        if (w % 2 == 0)  // the block above the diagonal in this row block's 16 x 32 pair
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s_T[(w * RB + 4 * q + part) * TP + (w + 1) * RB + cl] = 0.f;
+    }
+    __syncthreads();
+    {
+        const int g = lane / 16, n = lane % 16;
+#pragma unroll
+        for (int level = 1; level < kWaves; ++level) {
+            if (w >= level) {
+                const int R = w, S = w - level;
+                f32x4v x = {0.f, 0.f, 0.f, 0.f};
+                for (int K = S; K < R; ++K) {
+                    f32x4v av, bv;  // A_RK (row 16R + n, k = 16K + 4g + e); T_KS (col 16S + n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        av[e] = s_A[(R * RB + n) * AP + e * (C / 4) + 4 * K + g];
+                        bv[e] = s_T[(K * RB + 4 * g + e) * TP + S * RB + n];
+                    }
+                    x = mma16(frag4<F>(av), frag4<F>(bv), x);
+                }
+                f32x4v tv;  // T_RR (row 16R + n, k = 16R + 4g + e)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tv[e] = s_T[(R * RB + n) * TP + R * RB + 4 * g + e];
+                const f32x4v y = mma16(frag4<F>(tv), frag4<F>(x), f32x4v{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_T[(R * RB + 4 * g + i) * TP + S * RB + n] = -y[i];
+            }
+            __syncthreads();
+        }
+    }
+    // P (from registers) beside T, for coalesced stores; T' = T diag(beta):
+    // a thread's column is its lane, whose beta it holds
 #pragma unroll
     for (int ct = 0; ct < C / RB; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             s_P[(w * RB + (lane / 16) * 4 + i) * (C + 1) + ct * RB + lane % 16] = pv[ct][i];
-    const float bcol = __shfl(b_l, col, kWave);
-#pragma unroll
-    for (int q = 0; q < C / 4; ++q) s_T[(q * 4 + part) * (C + 1) + col] = t[q] * bcol;
+    for (int idx = tid; idx < C * C; idx += kThreads) s_T[(idx / C) * TP + idx % C] *= b_l;
     __syncthreads();
     put_planes<C, F, true>(s_P, rec + RL.phi, rec + RL.plo);
     put_planes<C, F, true>(s_T, rec + RL.thi, rec + RL.tlo);
@@ -1370,7 +1424,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     put_split(lane);
     __syncthreads();
+    // the state after the last chunk is needed only as an output (a branch
+    // call may not ask for it): the last step then skips the state update
+    const bool need_final = a.state_out != nullptr || CK;
     for (int c = 0; c < nchunks; ++c) {
+        const bool upd = need_final || c + 1 < nchunks;
         if constexpr (CK)
             if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
@@ -1380,12 +1438,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // out of the loop, the compiler keeps them live and spills.
         const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
         const int acol = (lane / 16) * 8, r0v = w * RB + (lane / 16) * 4;
-        if constexpr (PK) {
-            load_kt(c);
-        } else {
+        if (upd) {
+            if constexpr (PK) {
+                load_kt(c);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                put_kt(cur.ka[ks], ks * 32 + acol, w * RB + lane % 16, s_Kh, s_Kl);
+                for (int ks = 0; ks < KS; ++ks)
+                    put_kt(cur.ka[ks], ks * 32 + acol, w * RB + lane % 16, s_Kh, s_Kl);
+            }
         }
 
         // gamma_r = exp(g_r) of this lane's rows, from the chunk record (the
@@ -1459,7 +1519,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             const int uo = (t * 16 + lane % 16) * CB + r0v;
             put4<F>(s_Uh, s_Ul, uo, acc);
-            if constexpr (!PK) {  // W = diag(e^{g_L - g}) U for the state update
+            if (!PK && upd) {  // W = diag(e^{g_L - g}) U for the state update
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] *= cur.gu[i];
                 put4<F>(s_Wh, s_Wl, uo, acc);
@@ -1495,6 +1555,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
 
+        if (!upd) break;  // the last chunk, no final state wanted
         // Sig^T <- gamma_L Sig^T + U^T K~ = gamma_L Sig^T + W^T K (scalar
         // decay; per key: diag(e^{g_L}) Sig^T + U^T K~)   (tiles: value
         // sub-tile x 16 keys)
@@ -1521,7 +1582,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         put_split(lane);
         __syncthreads();
-            }
+    }
     if (a.state_out) put_state(a.state_out + ((size_t)s * H + h) * DK * DV);
     if (a.win_out && tile == 0) put_window(static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
     // a checkpoint at the end of the sequence (its length a multiple of the
