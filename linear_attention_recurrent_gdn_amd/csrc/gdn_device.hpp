@@ -109,6 +109,9 @@ struct PrefillArgs {
     float *ckpt_state;      // or null
     void *ckpt_window;      // or null
     int ckpt_every, ckpt_cap;
+    // set by the launcher for branch calls: [count, first branch of each
+    // group..., n_seq] (groups of branches of one parent), or null
+    const int32_t *groups;
 };
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,

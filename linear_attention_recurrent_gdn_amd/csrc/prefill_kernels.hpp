@@ -56,6 +56,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr long long kScanResident = 2 * 256;  // scan workgroups resident at once (2 per CU)
 constexpr int C = 64;        // chunk length
 constexpr int TV = 32;       // value-tile width of the scan
 constexpr int RB = 16;       // chunk rows per wave
@@ -258,6 +259,7 @@ __host__ __device__ constexpr RecLayout rec_layout(int dk, bool per_key) {
 }
 
 struct WsLayout {
+    size_t grp_off;     // int32 offset of the branch group table (after chunk_start)
     size_t rec_off;
     size_t rec_elems;   // bf16 elements per record
     size_t max_chunks;
@@ -267,7 +269,8 @@ struct WsLayout {
 __host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H, int dk, bool per_key) {
     WsLayout w{};
     w.max_chunks = (size_t)n_tokens / C + (size_t)n_seq;
-    w.rec_off = ((sizeof(int32_t) * ((size_t)n_seq + 1)) + 255) & ~size_t(255);
+    w.grp_off = (size_t)n_seq + 1;
+    w.rec_off = ((sizeof(int32_t) * (2 * (size_t)n_seq + 4)) + 255) & ~size_t(255);
     w.rec_elems = rec_layout(dk, per_key).elems;
     w.total = w.rec_off + sizeof(__bf16) * w.rec_elems * w.max_chunks * (size_t)H;
     return w;
@@ -314,6 +317,59 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n
         run += (seq_span(cu, s, n_tokens).len + C - 1) / C;
     }
     if (tid == kThreads - 1) chunk_start[n_seq] = (int32_t)min(run, max_chunks);
+}
+
+// Branch groups for the scan: the maximal runs of consecutive branches with
+// one parent, cut into pieces of at most G branches (a workgroup of the scan
+// then runs a group's branches from one load of the parent state).
+// groups[0] = the count, groups[1 + g] = the first branch of group g,
+// groups[1 + count] = n_seq. One workgroup: per-thread slices of the
+// branches, with the run start carried across slices by a max-scan.
+__global__ __launch_bounds__(kThreads) void plan_groups_kernel(const int32_t *parent, int n_seq,
+                                                               int G, int32_t *groups) {
+    __shared__ int s_run[kThreads], s_cnt[kThreads];
+    const int tid = threadIdx.x;
+    const int per = (n_seq + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
+    const auto starts_run = [&](int b) { return b == 0 || parent[b] != parent[b - 1]; };
+    int last = -1;
+    for (int b = lo; b < hi; ++b)
+        if (starts_run(b)) last = b;
+    s_run[tid] = last;
+    __syncthreads();
+    if (tid == 0) {  // the run start in effect where each slice begins
+        int run = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const int x = s_run[i];
+            s_run[i] = run;
+            if (x >= 0) run = x;
+        }
+    }
+    __syncthreads();
+    int rs = s_run[tid], cnt = 0;
+    for (int b = lo; b < hi; ++b) {
+        if (starts_run(b)) rs = b;
+        cnt += (b - rs) % G == 0;
+    }
+    s_cnt[tid] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const int x = s_cnt[i];
+            s_cnt[i] = run;
+            run += x;
+        }
+        groups[0] = run;
+        groups[1 + run] = n_seq;
+    }
+    __syncthreads();
+    int gi = s_cnt[tid];
+    rs = s_run[tid];
+    for (int b = lo; b < hi; ++b) {
+        if (starts_run(b)) rs = b;
+        if ((b - rs) % G == 0) groups[1 + gi++] = b;
+    }
 }
 
 __device__ __forceinline__ int find_seq(const int32_t *chunk_start, int n_seq, int gc) {
@@ -1202,7 +1258,9 @@ struct ChunkRegs {
 // K~^T U = K^T W.
 // CK: also write checkpoints (state and window every ckpt_every chunks);
 // a separate instance so the plain scan keeps its register budget.
-template <int DK, int DV, typename TI, typename TO, bool PK, bool CK>
+// GRP: branch groups (a.groups set); else one sequence per workgroup, so
+// the sequence loop below runs once and compiles away.
+template <int DK, int DV, typename TI, typename TO, bool PK, bool CK, bool GRP = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void scan_kernel(PrefillArgs a) {
     constexpr bool F = std::is_same<TI, float>::value;  // fp32 operands (see Frag)
     constexpr int KS = DK / 32;          // k-steps over d_k
@@ -1237,28 +1295,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int shd, tile;
     scan_unit(blockIdx.x, NT, shd, tile);
     if (shd >= a.n_seq * a.H) return;
-    const int s = shd / a.H, h = shd % a.H;
+    const int unit = shd / a.H, h = shd % a.H;
+    // this workgroup's sequences: one, or (branch calls) a group of branches
+    // of one parent, which run one after another from one load of the
+    // parent's state while no branch changes it
+    int s_first = unit, s_last = unit + 1;
+    if constexpr (GRP) {
+        if (unit >= a.groups[0]) return;
+        s_first = a.groups[1 + unit];
+        s_last = a.groups[2 + unit];
+    }
     const int H = a.H;
     const int CC = H * (2 * DK + DV);
     const int j0 = tile * TV;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
     const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK, PK);
-    const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
-    const int src = a.parent ? a.parent[s] : s;
-    const bool src_ok = src >= 0 && src < a.n_parent;
-
-    if (!src_ok) {  // a branch with an invalid parent: NaN outputs, nothing else
-        if (a.o)
-            for (int idx = tid; idx < sp.len * TV; idx += kThreads)
-                static_cast<TO *>(a.o)[((size_t)(sp.start + idx / TV) * H + h) * DV + j0 + idx % TV] =
-                    from_f32<TO>(quiet_nan());
-        if (a.state_out)
-            for (int idx = tid; idx < DK * TV; idx += kThreads)
-                a.state_out[(((size_t)s * H + h) * DK + idx / TV) * DV + j0 + idx % TV] = quiet_nan();
-        return;
-    }
-    const TI *win = a.win_in ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC : nullptr;
+    // the current sequence (set per sequence below; the helpers read them)
+    int s = s_first, src = 0, cs0 = 0, nchunks = 0;
+    SeqSpan sp{0, 0};
+    const TI *win = nullptr;
 
     const bool conv = a.conv_w != nullptr;
     if (conv) stage_taps(a.conv_w, 2 * H * DK + h * DV + j0, TV, s_wv);
@@ -1267,10 +1323,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int kmax = (w * RB + RB - 1) / 32;  // T', P lower triangular: k-steps to use
     const int acol = (lane / 16) * 8;
     const int r0v = w * RB + (lane / 16) * 4;  // first of this lane's rows in the C/D layout
-    // read once: inside the loop the compiler could not prove these unchanged
-    // across the o stores and would reload them behind a full wait
-    const int cs0 = chunk_start[s];
-    const int nchunks = chunk_start[s + 1] - cs0;  // <= ceil(len / C)
     // the q / k / v base pointers as locals: every load below indexes one of
     // them directly (a pointer chosen between them would keep them in
     // private memory, and loads through it would be flat loads)
@@ -1298,6 +1350,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // dst, through the staging buffer (4 consecutive tile columns per
     // 16-byte store); called between barriers, so the plane buffer is free
     auto put_state = [&](float *dst) {
+        const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
             const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
@@ -1355,6 +1408,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI> &r) {
         const __bf16 *rec = record(c);
         const int p0 = c * C, L = min(C, sp.len - p0);
+        // lane-derived offsets formed at each call from an opaque copy of the
+        // lane (hoisted, they would stay live across the sequence loop)
+        const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
+        const int r0v = w * RB + (lane / 16) * 4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int off = frag_off(KS, w, ks, lane);
@@ -1409,21 +1466,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if (w == 0 && lane < DK / 4) lds_dma16(rec + RL.fac + lane * 8, s_eg);
     };
 
+    bool have = false;  // the registers and planes hold the parent's state
+    for (; s < s_last; ++s) {
+    sp = seq_span(a.cu, s, a.n_tokens);
+    src = a.parent ? a.parent[s] : s;
+    ChunkRegs<KS, NVT, TI> nxt;
+    if (!(src >= 0 && src < a.n_parent)) {  // invalid parent: NaN outputs, nothing else
+        if (a.o)
+            for (int idx = tid; idx < sp.len * TV; idx += kThreads)
+                static_cast<TO *>(a.o)[((size_t)(sp.start + idx / TV) * H + h) * DV + j0 + idx % TV] =
+                    from_f32<TO>(quiet_nan());
+        if (a.state_out)
+            for (int idx = tid; idx < DK * TV; idx += kThreads)
+                a.state_out[(((size_t)s * H + h) * DK + idx / TV) * DV + j0 + idx % TV] = quiet_nan();
+        continue;
+    }
+    win = a.win_in ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC : nullptr;
+    // read once: inside the loop the compiler could not prove these unchanged
+    // across the o stores and would reload them behind a full wait
+    cs0 = chunk_start[s];
+    nchunks = chunk_start[s + 1] - cs0;  // <= ceil(len / C)
+
     // the first chunk's operands are requested before the incoming state
     // tile, so the two round trips overlap (a one-chunk branch pays one)
-    ChunkRegs<KS, NVT, TI> nxt;
     if (nchunks > 0) load_regs(0, nxt);
+    if (!have) {
+        const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
 #pragma unroll
-    for (int m = 0; m < NEG; ++m) {
-        const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
+        for (int m = 0; m < NEG; ++m) {
+            const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            mst[m][i] = a.state_in ? a.state_in[(((size_t)src * H + h) * DK + key) * DV + j0 +
-                                                vcol(t * 16 + (lane / 16) * 4 + i)]
-                                   : 0.f;
+            for (int i = 0; i < 4; ++i)
+                mst[m][i] = a.state_in ? a.state_in[(((size_t)src * H + h) * DK + key) * DV + j0 +
+                                                    vcol(t * 16 + (lane / 16) * 4 + i)]
+                                       : 0.f;
+        }
+        put_split(lane);
+        __syncthreads();
+        have = true;
     }
-    put_split(lane);
-    __syncthreads();
     // the state after the last chunk is needed only as an output (a branch
     // call may not ask for it): the last step then skips the state update
     const bool need_final = a.state_out != nullptr || CK;
@@ -1589,6 +1670,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // checkpoint spacing)
     if constexpr (CK)
         if (ckpt_at(nchunks) && nchunks * C == sp.len) put_checkpoint(nchunks);
+    // a state update ran: the next branch of the group reloads the parent's
+    if (nchunks > 1 || (need_final && nchunks > 0)) have = false;
+    }
 }
 
 template <int DK, int DV, typename TI, typename TO>
@@ -1623,16 +1707,44 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const size_t n_sh = (size_t)a.n_seq * a.H;
     const size_t sh_pad = (n_sh + 7) / 8 * 8;  // see scan_unit
     const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
+    // Branch calls: groups of up to G consecutive branches of one parent per
+    // scan workgroup, G chosen so that about two workgroups per compute unit
+    // have work (fewer, longer workgroups amortise the parent-state load and
+    // keep the next branch's operands in flight).
+    PrefillArgs sa = a;
+    if (a.parent) {
+        const long long units = (long long)a.H * (DV / TV);
+        const long long target = std::max(1LL, (kScanResident + units - 1) / units);
+        const int G = (int)std::max(1LL, ((long long)a.n_seq + target - 1) / target);
+        if (G > 1) {
+            int32_t *groups = chunk_start + wl.grp_off;
+            hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(kThreads), 0, stream, a.parent,
+                               a.n_seq, G, groups);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            sa.groups = groups;
+        }
+    }
     auto scan = [&](auto ck_tag) {
         constexpr bool CK = decltype(ck_tag)::value;
         const dim3 grid((unsigned)(sh_pad * (DV / TV)));
         if (pk)
             hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, CK>), grid, dim3(kThreads), 0,
-                               stream, a);
+                               stream, sa);
         else
             hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, CK>), grid, dim3(kThreads), 0,
-                               stream, a);
+                               stream, sa);
     };
+    if (sa.groups) {  // branch calls never take checkpoints
+        const dim3 grid((unsigned)(sh_pad * (DV / TV)));
+        if (pk)
+            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, false, true>), grid,
+                               dim3(kThreads), 0, stream, sa);
+        else
+            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, false, true>), grid,
+                               dim3(kThreads), 0, stream, sa);
+        return hipGetLastError();
+    }
     if (ck) scan(std::true_type{});
     else scan(std::false_type{});
     return hipGetLastError();
