@@ -131,6 +131,17 @@ __device__ __forceinline__ void store_frag(__bf16 *hi, __bf16 *lo, const Frag<F>
     *reinterpret_cast<decltype(s.lo) *>(lo) = s.lo;
 }
 
+// base + an unsigned 32-bit byte offset: with base wave-uniform, global
+// accesses through it take the scalar-base form (no 64-bit lane math).
+template <class T>
+__device__ __forceinline__ T *byte_at(T *base, unsigned bytes) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + bytes);
+}
+template <class T>
+__device__ __forceinline__ const T *byte_at(const T *base, unsigned bytes) {
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + bytes);
+}
+
 // One element at element offset o of a plane pair.
 template <bool F>
 __device__ __forceinline__ void put1(__bf16 *hi, __bf16 *lo, int o, float x) {
@@ -1405,6 +1416,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                ((size_t)(cs0 + c) * H + h) * wl.rec_elems;
     };
     // loads only: every address is clamped in bounds, nothing is consumed here
+    // Addresses: a wave-uniform base per chunk plus an unsigned 32-bit lane
+    // offset (the scalar-base form of the global loads, no 64-bit lane math).
     auto load_regs = [&](int c, ChunkRegs<KS, NVT, TI> &r) {
         const __bf16 *rec = record(c);
         const int p0 = c * C, L = min(C, sp.len - p0);
@@ -1414,18 +1427,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int r0v = w * RB + (lane / 16) * 4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int off = frag_off(KS, w, ks, lane);
-            r.ka[ks] = read_frag<F>(rec + RL.khi + off, rec + RL.klo + off);
-            if (want_o) r.qa[ks] = read_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off);
+            const unsigned ob = 2u * frag_off(KS, w, ks, lane);  // bytes
+            // Q and P unconditionally (a branch here would keep their
+            // addresses out of the scalar-base form)
+            r.ka[ks] = read_frag<F>(byte_at(rec + RL.khi, ob), byte_at(rec + RL.klo, ob));
+            r.qa[ks] = read_frag<F>(byte_at(rec + RL.qhi, ob), byte_at(rec + RL.qlo, ob));
         }
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq)
             if (kq <= kmax) {
-                const int off = tri_off(w, kq, lane);
-                r.ta[kq] = read_frag<F>(rec + RL.thi + off, rec + RL.tlo + off);
-                if (want_o) r.pa[kq] = read_frag<F>(rec + RL.phi + off, rec + RL.plo + off);
+                const unsigned ob = 2u * tri_off(w, kq, lane);
+                r.ta[kq] = read_frag<F>(byte_at(rec + RL.thi, ob), byte_at(rec + RL.tlo, ob));
+                r.pa[kq] = read_frag<F>(byte_at(rec + RL.phi, ob), byte_at(rec + RL.plo, ob));
             }
-        {
+        if (c == 0) {  // rows before the sequence come from the incoming window
             const int j = j0 + 2 * (lane % 16);  // columns j, j + 1 (even: pair-aligned)
 #pragma unroll
             for (int q = 0; q < 7; ++q) {
@@ -1435,6 +1450,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                                                           H * DV + (size_t)h * DV + j;
                 r.vraw[q] = *reinterpret_cast<const typename VPair<TI>::type *>(ptr);
             }
+        } else {  // rows p0 - 3 .. p0 + L - 1 all lie inside the sequence
+            const TI *base = vs + ((size_t)(sp.start + p0 - 3) * H + h) * DV + j0;
+            const unsigned stride = (unsigned)H * DV;
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                const unsigned row = (unsigned)min(r0v + q, L + 2);
+                r.vraw[q] = *reinterpret_cast<const typename VPair<TI>::type *>(
+                    byte_at(base, (row * stride + 2u * (lane % 16)) * (unsigned)sizeof(TI)));
+            }
         }
         if constexpr (PK) {
             r.gam = f32x4v{1.f, 1.f, 1.f, 1.f};
@@ -1442,8 +1466,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             r.gaml = 1.f;
         } else {
             const float *fac = reinterpret_cast<const float *>(rec + RL.fac);
-            r.gam = *reinterpret_cast<const f32x4v *>(fac + r0v);
-            r.gu = *reinterpret_cast<const f32x4v *>(fac + C + r0v);
+            r.gam = *reinterpret_cast<const f32x4v *>(byte_at(fac, 4u * r0v));
+            r.gu = *reinterpret_cast<const f32x4v *>(byte_at(fac + C, 4u * r0v));
             r.gaml = fac[2 * C];
         }
     };
@@ -1626,12 +1650,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
         if (c + 1 < nchunks) load_regs(c + 1, nxt);  // prefetch the next step
         if (want_o) {
+            TO *const obase = static_cast<TO *>(a.o) + ((size_t)(cs.seq0 + cs.p0) * H + h) * DV + j0;
+            const unsigned ostride = (unsigned)H * DV;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = r0v + i;
                 if (r < cs.L)
-                    store_pair(static_cast<TO *>(a.o) + ((size_t)(cs.seq0 + cs.p0 + r) * H + h) * DV +
-                                   j0 + 2 * (lane % 16),
+                    store_pair(byte_at(obase, ((unsigned)r * ostride + 2u * (lane % 16)) *
+                                                  (unsigned)sizeof(TO)),
                                acc_o[0][i], acc_o[1][i]);
             }
         }
