@@ -1344,17 +1344,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     // The state tiles of this wave: tile m is ft = w + 4 m, value sub-tile
     // t = ft % NVT, keys dt*16 .. dt*16 + 15 (dt = ft / NVT); the lane holds
-    // the internal value columns t*16 + (l/16)*4 + i (i < 4) of key
-    // dt*16 + l%16.
+    // the keys dt*16 + (l/16)*4 + i (i < 4) of the internal value column
+    // t*16 + l%16 (the output layout of the update Sig = K^T W, rows = keys).
     float mst[NEG][4];
-    // the split planes of the state from the registers
+    // the split planes of the state from the registers: a lane's 4 keys are
+    // consecutive in a plane row (one 8-byte store per plane and tile)
     auto put_split = [&](int lane) {
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
-            const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                put1<F>(s_Sh, s_Sl, st_off<DK>(t * 16 + (lane / 16) * 4 + i, key), mst[m][i]);
+            const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
+            put4<F>(s_Sh, s_Sl, st_off<DK>(t * 16 + lane % 16, key0),
+                    f32x4v{mst[m][0], mst[m][1], mst[m][2], mst[m][3]});
         }
     };
     // the state tile [DK][TV] of this workgroup into a [DK][DV] state at
@@ -1364,9 +1364,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
-            const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
+            const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
+            const int col = vcol(t * 16 + lane % 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_stage[key * TV + vcol(t * 16 + (lane / 16) * 4 + i)] = mst[m][i];
+            for (int i = 0; i < 4; ++i) s_stage[(key0 + i) * TV + col] = mst[m][i];
         }
         __syncthreads();
         for (int idx = tid; idx < DK * TV / 4; idx += kThreads) {
@@ -1518,11 +1519,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
-            const int ft = w + m * kWaves, t = ft % NVT, key = (ft / NVT) * 16 + lane % 16;
+            const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
+            const int col = j0 + vcol(t * 16 + lane % 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                mst[m][i] = a.state_in ? a.state_in[(((size_t)src * H + h) * DK + key) * DV + j0 +
-                                                    vcol(t * 16 + (lane / 16) * 4 + i)]
+                mst[m][i] = a.state_in ? a.state_in[(((size_t)src * H + h) * DK + key0 + i) * DV + col]
                                        : 0.f;
         }
         put_split(lane);
@@ -1663,26 +1664,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
 
         if (!upd) break;  // the last chunk, no final state wanted
-        // Sig^T <- gamma_L Sig^T + U^T K~ = gamma_L Sig^T + W^T K (scalar
-        // decay; per key: diag(e^{g_L}) Sig^T + U^T K~)   (tiles: value
-        // sub-tile x 16 keys)
+        // Sig <- gamma_L Sig + K~^T U = gamma_L Sig + K^T W (scalar decay;
+        // per key: diag(e^{g_L}) Sig + K~^T U)   (tiles: 16 keys x value
+        // sub-tile; A = the key rows of K^T, B = the value rows of W^T)
         const float gamL = cur.gaml;
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
             const int ft = w + m * kWaves;
             const int t = ft % NVT, dt = ft / NVT;
-            // per key: e^{g_L} of column dt*16 + lane%16
-            const float dec = PK ? reinterpret_cast<const float *>(s_eg)[dt * 16 + lane % 16] : gamL;
+            // per key: e^{g_L} of this lane's keys dt*16 + (l/16)*4 + i
+            f32x4v dec = {gamL, gamL, gamL, gamL};
+            if constexpr (PK)
+                dec = *reinterpret_cast<const f32x4v *>(reinterpret_cast<const float *>(s_eg) + dt * 16 +
+                                                        (lane / 16) * 4);
             f32x4v acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = dec * mst[m][i];
+            for (int i = 0; i < 4; ++i) acc[i] = dec[i] * mst[m][i];
 #pragma unroll
             for (int kq = 0; kq < 2; ++kq) {
                 const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
                 const int ok = PK ? kt_swz(dt * 16 + lane % 16, kq * 4 + lane / 16)
                                   : kt_off(dt * 16 + lane % 16, kq * 32 + acol);
-                acc = PK ? mma(read_frag<F>(s_Uh + ou, s_Ul + ou), read_frag<F>(s_Kh + ok, s_Kl + ok), acc)
-                         : mma(read_frag<F>(s_Wh + ou, s_Wl + ou), read_frag<F>(s_Kh + ok, s_Kl + ok), acc);
+                acc = PK ? mma(read_frag<F>(s_Kh + ok, s_Kl + ok), read_frag<F>(s_Uh + ou, s_Ul + ou), acc)
+                         : mma(read_frag<F>(s_Kh + ok, s_Kl + ok), read_frag<F>(s_Wh + ou, s_Wl + ou), acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) mst[m][i] = acc[i];
