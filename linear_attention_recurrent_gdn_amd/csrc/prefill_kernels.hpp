@@ -1558,29 +1558,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // prep kernel's running sums; rows >= L add nothing)
         const f32x4v gam = cur.gam;
 
-        // conv'd V entries of this lane (C/D layout), from the raw rows
+        // conv'd V entries of this lane (C/D layout), from the raw rows; a
+        // full chunk past the first has every row inside the sequence, so it
+        // takes the rows without validity masks
         float vf[NVT][4];
+        const auto conv_v = [&](auto masked) {
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) {
-            const int jt = vcol(t * 16 + lane % 16);  // the tile column, for its taps
-            float xr[7];
+            for (int t = 0; t < NVT; ++t) {
+                const int jt = vcol(t * 16 + lane % 16);  // the tile column, for its taps
+                float xr[7];
 #pragma unroll
-            for (int q = 0; q < 7; ++q) {
-                const int row = r0v - 3 + q, p = cs.p0 + row;
-                const bool ok = (conv || q >= 3) && ((row < cs.L && p >= 0) || (p < 0 && win));
-                xr[q] = ok ? VPair<TI>::get(cur.vraw[q], t) : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float y = xr[i + 3];
-                if (conv) {
-                    y = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) y = fmaf(s_wv[jt * 4 + r], xr[i + r], y);
+                for (int q = 0; q < 7; ++q) {
+                    xr[q] = VPair<TI>::get(cur.vraw[q], t);
+                    if constexpr (decltype(masked)::value) {
+                        const int row = r0v - 3 + q, p = cs.p0 + row;
+                        const bool ok = (conv || q >= 3) && ((row < cs.L && p >= 0) || (p < 0 && win));
+                        xr[q] = ok ? xr[q] : 0.f;
+                    }
                 }
-                vf[t][i] = r0v + i < cs.L ? y : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float y = xr[i + 3];
+                    if (conv) {
+                        y = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) y = fmaf(s_wv[jt * 4 + r], xr[i + r], y);
+                    }
+                    if constexpr (decltype(masked)::value) y = r0v + i < cs.L ? y : 0.f;
+                    vf[t][i] = y;
+                }
             }
-        }
+        };
+        if (cs.p0 > 0 && cs.L == C) conv_v(std::false_type{});
+        else conv_v(std::true_type{});
 
         // K Sig0 and Q Sig0 share the split Sig^T fragments;
         // R = V - diag(gamma) K Sig0 goes to LDS, Q Sig0 stays in registers
