@@ -853,8 +853,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
         }
         __syncthreads();
         for (int idx = tid; idx < kWaves * DK; idx += kThreads) {
-            s_tab[TEG0 + idx] = expf(s_tab[TG0 + idx]);
-            s_tab[TEL + idx] = expf(s_gl[idx % DK] - s_tab[TG15 + idx]);
+            s_tab[TEG0 + idx] = exp_pk(s_tab[TG0 + idx]);
+            s_tab[TEL + idx] = exp_pk(s_gl[idx % DK] - s_tab[TG15 + idx]);
         }
         for (int idx = tid; idx < kPairs * DK; idx += kThreads) {
             const int pr = idx / DK, d = idx % DK;
@@ -863,7 +863,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             const int S = pr - R * (R + 1) / 2;
             const float x = s_tab[TG0 + R * DK + d] - s_tab[TG15 + S * DK + d];
             if (S == R && x > kJoinLimit) s_slow = 1;
-            s_tab[TM + idx] = expf(fminf(x, kJoinLimit));
+            s_tab[TM + idx] = exp_pk(fminf(x, kJoinLimit));
         }
         __syncthreads();
     }
