@@ -297,47 +297,14 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t *cu, int s, int n_toke
     return {a, b - a};
 }
 
-// ------------------------------------------------------------ plan
-// chunk_start[s] = min(sum_{s' < s} ceil(len_s' / C), max_chunks): the
-// first record of sequence s; sequence s owns chunk_start[s+1] -
-// chunk_start[s] chunks. With valid offsets the cap never binds; with
-// overlapping (invalid) offsets it keeps every record inside the workspace.
-__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n_seq, int n_tokens,
-                                                        long long max_chunks,
-                                                        int32_t *chunk_start) {
-    __shared__ long long s_part[kThreads];
-    const int tid = threadIdx.x;
-    const int per = (n_seq + kThreads - 1) / kThreads;
-    const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
-    long long sum = 0;
-    for (int s = lo; s < hi; ++s) sum += (seq_span(cu, s, n_tokens).len + C - 1) / C;
-    s_part[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        long long run = 0;
-        for (int i = 0; i < kThreads; ++i) {
-            const long long x = s_part[i];
-            s_part[i] = run;
-            run += x;
-        }
-    }
-    __syncthreads();
-    long long run = s_part[tid];
-    for (int s = lo; s < hi; ++s) {
-        chunk_start[s] = (int32_t)min(run, max_chunks);
-        run += (seq_span(cu, s, n_tokens).len + C - 1) / C;
-    }
-    if (tid == kThreads - 1) chunk_start[n_seq] = (int32_t)min(run, max_chunks);
-}
-
 // Branch groups for the scan: the maximal runs of consecutive branches with
 // one parent, cut into pieces of at most G branches (a workgroup of the scan
 // then runs a group's branches from one load of the parent state).
 // groups[0] = the count, groups[1 + g] = the first branch of group g,
 // groups[1 + count] = n_seq. One workgroup: per-thread slices of the
 // branches, with the run start carried across slices by a max-scan.
-__global__ __launch_bounds__(kThreads) void plan_groups_kernel(const int32_t *parent, int n_seq,
-                                                               int G, int32_t *groups) {
+__device__ __forceinline__ void plan_groups(const int32_t *parent, int n_seq, int G,
+                                            int32_t *groups) {
     __shared__ int s_run[kThreads], s_cnt[kThreads];
     const int tid = threadIdx.x;
     const int per = (n_seq + kThreads - 1) / kThreads;
@@ -381,6 +348,42 @@ __global__ __launch_bounds__(kThreads) void plan_groups_kernel(const int32_t *pa
         if (starts_run(b)) rs = b;
         if ((b - rs) % G == 0) groups[1 + gi++] = b;
     }
+}
+
+// ------------------------------------------------------------ plan
+// chunk_start[s] = min(sum_{s' < s} ceil(len_s' / C), max_chunks): the
+// first record of sequence s; sequence s owns chunk_start[s+1] -
+// chunk_start[s] chunks. With valid offsets the cap never binds; with
+// overlapping (invalid) offsets it keeps every record inside the workspace.
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n_seq, int n_tokens,
+                                                        long long max_chunks,
+                                                        int32_t *chunk_start,
+                                                        const int32_t *parent, int G,
+                                                        int32_t *groups) {
+    __shared__ long long s_part[kThreads];
+    const int tid = threadIdx.x;
+    const int per = (n_seq + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
+    long long sum = 0;
+    for (int s = lo; s < hi; ++s) sum += (seq_span(cu, s, n_tokens).len + C - 1) / C;
+    s_part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        long long run = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const long long x = s_part[i];
+            s_part[i] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+    long long run = s_part[tid];
+    for (int s = lo; s < hi; ++s) {
+        chunk_start[s] = (int32_t)min(run, max_chunks);
+        run += (seq_span(cu, s, n_tokens).len + C - 1) / C;
+    }
+    if (tid == kThreads - 1) chunk_start[n_seq] = (int32_t)min(run, max_chunks);
+    if (groups) plan_groups(parent, n_seq, G, groups);  // branch calls
 }
 
 __device__ __forceinline__ int find_seq(const int32_t *chunk_start, int n_seq, int gc) {
@@ -1726,8 +1729,21 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const bool pk = a.variant != kScalar;
     const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, pk);
     int32_t *chunk_start = static_cast<int32_t *>(a.ws);
+    // Branch calls: groups of up to G consecutive branches of one parent per
+    // scan workgroup, G chosen so that about two workgroups per compute unit
+    // have work (fewer, longer workgroups amortise the parent-state load);
+    // the plan kernel forms them.
+    PrefillArgs sa = a;
+    int G = 1;
+    if (a.parent) {
+        const long long units = (long long)a.H * (DV / TV);
+        const long long target = std::max(1LL, (kScanResident + units - 1) / units);
+        G = (int)std::max(1LL, ((long long)a.n_seq + target - 1) / target);
+        if (G > 1) sa.groups = chunk_start + wl.grp_off;
+    }
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq, a.n_tokens,
-                       (long long)wl.max_chunks, chunk_start);
+                       (long long)wl.max_chunks, chunk_start, a.parent, G,
+                       sa.groups ? chunk_start + wl.grp_off : nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wl.max_chunks > 0) {
@@ -1747,24 +1763,6 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const size_t n_sh = (size_t)a.n_seq * a.H;
     const size_t sh_pad = (n_sh + 7) / 8 * 8;  // see scan_unit
     const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
-    // Branch calls: groups of up to G consecutive branches of one parent per
-    // scan workgroup, G chosen so that about two workgroups per compute unit
-    // have work (fewer, longer workgroups amortise the parent-state load and
-    // keep the next branch's operands in flight).
-    PrefillArgs sa = a;
-    if (a.parent) {
-        const long long units = (long long)a.H * (DV / TV);
-        const long long target = std::max(1LL, (kScanResident + units - 1) / units);
-        const int G = (int)std::max(1LL, ((long long)a.n_seq + target - 1) / target);
-        if (G > 1) {
-            int32_t *groups = chunk_start + wl.grp_off;
-            hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(kThreads), 0, stream, a.parent,
-                               a.n_seq, G, groups);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            sa.groups = groups;
-        }
-    }
     auto scan = [&](auto ck_tag) {
         constexpr bool CK = decltype(ck_tag)::value;
         const dim3 grid((unsigned)(sh_pad * (DV / TV)));
