@@ -83,9 +83,10 @@ def test_prefill_traffic_against_algorithmic_bytes():
     to move: q, k, v bf16 (768), log a and beta fp32 (8), o fp32 (512). The
     chunk record (written by prep, read back by the scan) is overhead; each
     kernel's reads and writes are held to their parts: prep reads q, k, log
-    a, beta plus the conv halo (3 rows per 16-row block of q and k) and writes
-    the record once; the scan reads V and the record once and writes o and
-    the final states."""
+    a, beta plus the conv halo (3 rows per 16-row block of q and k) and the
+    q / k conv taps (4 KiB per workgroup, one workgroup per chunk-head) and
+    writes the record once; the scan reads V and the record once and writes
+    o and the final states."""
     w = gi.WORKLOADS["fork_prefill"]
     d, C, H, R, P = w["d"], w["chunk"], w["H"], w["R"], w["prefix"]
     token_heads = R * P * H
@@ -94,7 +95,7 @@ def test_prefill_traffic_against_algorithmic_bytes():
     scan = prefill_block("fork_prefill_scan_traffic.md")
     rec = chunk_heads * record_bytes(d, C)
     qk = token_heads * 2 * d * 2
-    prep_reads = qk * (1 + 3 / 16) + token_heads * 8
+    prep_reads = qk * (1 + 3 / 16) + token_heads * 8 + chunk_heads * 2 * d * 4 * 4
     scan_reads = token_heads * d * 2 + rec
     scan_writes = token_heads * d * 4 + R * H * d * d * 4
     assert 0.98 <= prep["read_bytes"] / prep_reads <= 1.10, prep["read_bytes"] / prep_reads
