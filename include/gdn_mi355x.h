@@ -81,12 +81,22 @@ int gdn_max_log_capacity(void);
 /* ------------------------------------------------------------------ prefill
  * Workspace bytes gdn_prefill_shared / gdn_prefill_checkpointed /
  * gdn_fork_branches need for a stream of at most n_tokens tokens in n_seq
- * sequences with the given variant: a 256-byte-aligned table of n_seq + 1
- * int32, then one record per (chunk, head) for at most
- * n_tokens / 64 + n_seq chunks -- 25 KiB per chunk-head with GDN_SCALAR
- * (400 bytes per token-head at d_k = 128), 25 KiB + 12 * 64 * d_k bytes
- * per chunk-head with the per-key variants. Returns 0 for arguments the
- * calls reject (negative sizes, H < 1, widths not 32/64/128, bad variant).
+ * sequences with the given variant. The calls run in S segments, segment k
+ * taking chunks [k n / S, (k + 1) n / S) of each sequence of n chunks, with
+ * S the smallest count (at most one per chunk of an average sequence, at
+ * most 64) whose records fit 512 MiB (the environment variable
+ * GDN_PREFILL_SEGMENT_RECORD_BYTES replaces that bound when it holds a
+ * positive integer; the calls read it as this function does, so set it
+ * before sizing and leave it while the calls run). The workspace holds a
+ * 256-byte-aligned int32 table of 3 n_seq + 4 entries, for S > 1 the state
+ * carried between segments (n_seq * H * d_k * d_v fp32), and the records of
+ * one segment: (n_tokens / 64 + n_seq) / S + n_seq chunk rows (rounded up;
+ * n_tokens / 64 + n_seq for S = 1) of H records each, 25 KiB + 512 * d_k
+ * bytes per record with GDN_SCALAR (89 KiB at d_k = 128) and 25 KiB +
+ * 768 * d_k bytes with the per-key variants. The fork_prefill prefix
+ * (65,536 tokens, 8 sequences, H = 16, d_k = d_v = 128) runs in 3 segments
+ * with 0.49 KiB per token-head. Returns 0 for arguments the calls reject
+ * (negative sizes, H < 1, widths not 32/64/128, bad variant).
  */
 size_t gdn_prefill_workspace_bytes(int n_tokens, int n_seq, int H, int d_k,
                                    int d_v, int chunk, int variant);

@@ -109,9 +109,11 @@ struct PrefillArgs {
     float *ckpt_state;      // or null
     void *ckpt_window;      // or null
     int ckpt_every, ckpt_cap;
-    // set by the launcher for branch calls: [count, first branch of each
-    // group..., n_seq] (groups of branches of one parent), or null
+    // set by the launcher: for branch calls [count, first branch of each
+    // group..., n_seq] (groups of branches of one parent), or null; the
+    // segment being run and the number of segments of the prefill
     const int32_t *groups;
+    int seg, nseg;
 };
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,

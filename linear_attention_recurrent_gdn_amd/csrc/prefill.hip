@@ -16,8 +16,9 @@ hipError_t launch_prefill_dk128(int dv, int io, int out, const PrefillArgs &a,
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv, int chunk,
                                int variant) {
     (void)chunk;
-    (void)dv;
-    return ws_layout(n_tokens, n_seq, H, dk, variant != kScalar).total;
+    const bool pk = variant != kScalar;
+    return ws_layout(n_tokens, n_seq, H, dk, dv, pk, prefill_segments(n_tokens, n_seq, H, dk, pk))
+        .total;
 }
 
 hipError_t launch_prefill(int dk, int dv, int io, int out, const PrefillArgs &a,

@@ -47,6 +47,8 @@
 
 #pragma once
 
+#include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -269,22 +271,60 @@ __host__ __device__ constexpr RecLayout rec_layout(int dk, bool per_key) {
                      k0 + 5 * cd, k0 + (per_key ? 6 : 4) * cd};
 }
 
+// Workspace: int32 header (chunk_start [n_seq + 1], the branch group table
+// [n_seq + 3], each sequence's first chunk in the current segment [n_seq]),
+// then, when the prefill runs in segments, the fp32 state carried from one
+// segment to the next [n_seq][H][dk][dv], then the records of one segment.
+// A prefill of nseg segments gives segment k of every sequence the chunks
+// [k n / nseg, (k + 1) n / nseg) of its n chunks, so one segment needs at
+// most all_chunks / nseg + n_seq records.
 struct WsLayout {
-    size_t grp_off;     // int32 offset of the branch group table (after chunk_start)
-    size_t rec_off;
+    size_t grp_off;     // int32 index of the branch group table
+    size_t win_off;     // int32 index of the per-sequence segment start chunks
+    size_t carry_off;   // byte offset of the carried state (nseg > 1)
+    size_t rec_off;     // byte offset of the records
     size_t rec_elems;   // bf16 elements per record
-    size_t max_chunks;
+    size_t max_chunks;  // records of one segment
     size_t total;
 };
 
-__host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H, int dk, bool per_key) {
+__host__ __device__ WsLayout ws_layout(int n_tokens, int n_seq, int H, int dk, int dv, bool per_key,
+                                       int nseg) {
     WsLayout w{};
-    w.max_chunks = (size_t)n_tokens / C + (size_t)n_seq;
+    const size_t all = (size_t)n_tokens / C + (size_t)n_seq;
+    w.max_chunks = nseg <= 1 ? all : (all + nseg - 1) / nseg + (size_t)n_seq;
     w.grp_off = (size_t)n_seq + 1;
-    w.rec_off = ((sizeof(int32_t) * (2 * (size_t)n_seq + 4)) + 255) & ~size_t(255);
+    w.win_off = 2 * (size_t)n_seq + 4;
+    w.carry_off = ((sizeof(int32_t) * (3 * (size_t)n_seq + 4)) + 255) & ~size_t(255);
+    const size_t carry = nseg > 1 ? sizeof(float) * (size_t)n_seq * H * dk * dv : 0;
+    w.rec_off = (w.carry_off + carry + 255) & ~size_t(255);
     w.rec_elems = rec_layout(dk, per_key).elems;
     w.total = w.rec_off + sizeof(__bf16) * w.rec_elems * w.max_chunks * (size_t)H;
     return w;
+}
+
+// Segments of a prefill: enough that one segment's records stay within
+// kSegmentRecordBytes (512 MiB: the fork_prefill prefix, 1.5 GB of records
+// in one segment, runs in 3 and needs 0.49 KiB of workspace per token-head),
+// at most one per chunk of an average sequence and at most kMaxSegments.
+// Each segment past the first costs about 25-45 us (launches, the scan's
+// restart and the carried state). The environment variable
+// GDN_PREFILL_SEGMENT_RECORD_BYTES overrides the bound (a smaller value
+// forces segments on small inputs, for tests; a large one a single
+// segment); the workspace size and the launcher read it alike.
+constexpr size_t kSegmentRecordBytes = size_t(512) << 20;
+constexpr int kMaxSegments = 64;
+inline int prefill_segments(int n_tokens, int n_seq, int H, int dk, bool per_key) {
+    size_t bound = kSegmentRecordBytes;
+    if (const char *env = std::getenv("GDN_PREFILL_SEGMENT_RECORD_BYTES")) {
+        const long long v = std::atoll(env);
+        if (v > 0) bound = (size_t)v;
+    }
+    const size_t all = (size_t)n_tokens / C + (size_t)n_seq;
+    const size_t rec = sizeof(__bf16) * rec_layout(dk, per_key).elems * (size_t)H;
+    const long long want = (long long)((all * rec + bound - 1) / bound);
+    const long long avg = n_seq > 0 ? (long long)n_tokens / ((long long)C * n_seq) : 1;
+    return (int)std::max(1LL, std::min({want, avg, (long long)kMaxSegments}));
 }
 
 struct SeqSpan {
@@ -351,21 +391,30 @@ __device__ __forceinline__ void plan_groups(const int32_t *parent, int n_seq, in
 }
 
 // ------------------------------------------------------------ plan
-// chunk_start[s] = min(sum_{s' < s} ceil(len_s' / C), max_chunks): the
-// first record of sequence s; sequence s owns chunk_start[s+1] -
-// chunk_start[s] chunks. With valid offsets the cap never binds; with
-// overlapping (invalid) offsets it keeps every record inside the workspace.
+// Segment seg of nseg: sequence s of n = ceil(len / C) chunks takes its
+// chunks [n seg / nseg, n (seg + 1) / nseg) (win0[s] = the first);
+// chunk_start[s] = min(sum of the earlier sequences' counts, max_chunks) is
+// its first record, and it owns chunk_start[s+1] - chunk_start[s]. With
+// valid offsets the cap never binds; with overlapping (invalid) offsets it
+// keeps every record inside the workspace.
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n_seq, int n_tokens,
                                                         long long max_chunks,
                                                         int32_t *chunk_start,
                                                         const int32_t *parent, int G,
-                                                        int32_t *groups) {
+                                                        int32_t *groups, int seg, int nseg,
+                                                        int32_t *win0) {
     __shared__ long long s_part[kThreads];
     const int tid = threadIdx.x;
     const int per = (n_seq + kThreads - 1) / kThreads;
     const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
-    long long sum = 0;
-    for (int s = lo; s < hi; ++s) sum += (seq_span(cu, s, n_tokens).len + C - 1) / C;
+    // sequence s's chunks in this segment: [first, first + count)
+    const auto window = [&](int s, long long &first) {
+        const long long n = (seq_span(cu, s, n_tokens).len + C - 1) / C;
+        first = n * seg / nseg;
+        return n * (seg + 1) / nseg - first;
+    };
+    long long sum = 0, first;
+    for (int s = lo; s < hi; ++s) sum += window(s, first);
     s_part[tid] = sum;
     __syncthreads();
     if (tid == 0) {
@@ -380,7 +429,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n
     long long run = s_part[tid];
     for (int s = lo; s < hi; ++s) {
         chunk_start[s] = (int32_t)min(run, max_chunks);
-        run += (seq_span(cu, s, n_tokens).len + C - 1) / C;
+        run += window(s, first);
+        win0[s] = (int32_t)first;
     }
     if (tid == kThreads - 1) chunk_start[n_seq] = (int32_t)min(run, max_chunks);
     if (groups) plan_groups(parent, n_seq, G, groups);  // branch calls
@@ -797,7 +847,9 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     if (gc >= chunk_start[a.n_seq]) return;
     const int s = find_seq(chunk_start, a.n_seq, gc);
     const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
-    const int c = gc - chunk_start[s];
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, a.dv, kPerKey, a.nseg);
+    // the chunk's index in its sequence (the segment's window starts there)
+    const int c = gc - chunk_start[s] + chunk_start[wl.win_off + s];
     const int H = a.H;
     const int CC = H * (2 * DK + a.dv);
     const int src = a.parent ? a.parent[s] : s;
@@ -806,7 +858,6 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
                     (a.win_in && src_ok) ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC
                                          : nullptr};
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK, kPerKey);
     constexpr RecLayout RL = rec_layout(DK, kPerKey);
     __bf16 *rec = reinterpret_cast<__bf16 *>(static_cast<char *>(a.ws) + wl.rec_off) +
                   ((size_t)gc * H + h) * wl.rec_elems;
@@ -1324,9 +1375,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int j0 = tile * TV;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK, PK);
-    // the current sequence (set per sequence below; the helpers read them)
-    int s = s_first, src = 0, cs0 = 0, nchunks = 0;
+    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, H, DK, DV, PK, a.nseg);
+    // a prefill in segments carries each sequence's state through the
+    // workspace from one segment to the next
+    const bool carry_in = a.seg > 0, carry_out = a.seg + 1 < a.nseg;
+    float *const carry = reinterpret_cast<float *>(static_cast<char *>(a.ws) + wl.carry_off);
+    // the current sequence (set per sequence below; the helpers read them):
+    // chunks c_beg .. c_end - 1 of it in this segment, chunk c's record at
+    // cs0 + c
+    int s = s_first, src = 0, cs0 = 0, nchunks = 0, c_beg = 0, c_end = 0;
     SeqSpan sp{0, 0};
     const TI *win = nullptr;
 
@@ -1512,22 +1569,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     win = a.win_in ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC : nullptr;
     // read once: inside the loop the compiler could not prove these unchanged
     // across the o stores and would reload them behind a full wait
-    cs0 = chunk_start[s];
-    nchunks = chunk_start[s + 1] - cs0;  // <= ceil(len / C)
+    c_beg = chunk_start[wl.win_off + s];
+    nchunks = chunk_start[s + 1] - chunk_start[s];  // <= ceil(len / C)
+    c_end = c_beg + nchunks;
+    cs0 = chunk_start[s] - c_beg;
 
     // the first chunk's operands are requested before the incoming state
     // tile, so the two round trips overlap (a one-chunk branch pays one)
-    if (nchunks > 0) load_regs(0, nxt);
+    if (nchunks > 0) load_regs(c_beg, nxt);
     if (!have) {
         const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
+        // the incoming state: the carried one past the first segment
+        const float *sin = carry_in ? carry + (size_t)s * H * DK * DV
+                                    : (a.state_in ? a.state_in + (size_t)src * H * DK * DV : nullptr);
 #pragma unroll
         for (int m = 0; m < NEG; ++m) {
             const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
             const int col = j0 + vcol(t * 16 + lane % 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                mst[m][i] = a.state_in ? a.state_in[(((size_t)src * H + h) * DK + key0 + i) * DV + col]
-                                       : 0.f;
+                mst[m][i] = sin ? sin[((size_t)h * DK + key0 + i) * DV + col] : 0.f;
         }
         put_split(lane);
         __syncthreads();
@@ -1535,9 +1596,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     // the state after the last chunk is needed only as an output (a branch
     // call may not ask for it): the last step then skips the state update
-    const bool need_final = a.state_out != nullptr || CK;
-    for (int c = 0; c < nchunks; ++c) {
-        const bool upd = need_final || c + 1 < nchunks;
+    const bool need_final = a.state_out != nullptr || CK || carry_out;
+    for (int c = c_beg; c < c_end; ++c) {
+        const bool upd = need_final || c + 1 < c_end;
         if constexpr (CK)
             if (ckpt_at(c)) put_checkpoint(c);  // the state after c chunks
         const ChunkSrc<TI> cs{sp.start, c * C, min(C, sp.len - c * C), win};
@@ -1662,7 +1723,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
 
-        if (c + 1 < nchunks) load_regs(c + 1, nxt);  // prefetch the next step
+        if (c + 1 < c_end) load_regs(c + 1, nxt);  // prefetch the next step
         if (want_o) {
             TO *const obase = static_cast<TO *>(a.o) + ((size_t)(cs.seq0 + cs.p0) * H + h) * DV + j0;
             const unsigned ostride = (unsigned)H * DV;
@@ -1707,87 +1768,98 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         put_split(lane);
         __syncthreads();
     }
-    if (a.state_out) put_state(a.state_out + ((size_t)s * H + h) * DK * DV);
-    if (a.win_out && tile == 0) put_window(static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
+    if (carry_out) {
+        put_state(carry + ((size_t)s * H + h) * DK * DV);
+    } else {
+        if (a.state_out) put_state(a.state_out + ((size_t)s * H + h) * DK * DV);
+        if (a.win_out && tile == 0) put_window(static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
+    }
     // a checkpoint at the end of the sequence (its length a multiple of the
     // checkpoint spacing)
     if constexpr (CK)
-        if (ckpt_at(nchunks) && nchunks * C == sp.len) put_checkpoint(nchunks);
+        if (ckpt_at(c_end) && c_end * C == sp.len) put_checkpoint(c_end);
     // a state update ran: the next branch of the group reloads the parent's
     if (nchunks > 1 || (need_final && nchunks > 0)) have = false;
     }
 }
 
 template <int DK, int DV, typename TI, typename TO>
-hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
+hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
     auto prep = [&](auto vtag) {
         constexpr int VAR = decltype(vtag)::value;
         if constexpr (VAR == kScalar) return prep_kernel<DK, TI>;
         else return prep_kernel_pk<DK, TI, VAR>;
     };
-    if (a.n_seq == 0) return hipSuccess;
-    const bool pk = a.variant != kScalar;
-    const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, pk);
-    int32_t *chunk_start = static_cast<int32_t *>(a.ws);
-    // Branch calls: groups of up to G consecutive branches of one parent per
-    // scan workgroup, G chosen so that about two workgroups per compute unit
-    // have work (fewer, longer workgroups amortise the parent-state load);
-    // the plan kernel forms them.
-    PrefillArgs sa = a;
+    if (a0.n_seq == 0) return hipSuccess;
+    const bool pk = a0.variant != kScalar;
+    const int nseg = prefill_segments(a0.n_tokens, a0.n_seq, a0.H, DK, pk);
+    const WsLayout wl = ws_layout(a0.n_tokens, a0.n_seq, a0.H, DK, DV, pk, nseg);
+    int32_t *chunk_start = static_cast<int32_t *>(a0.ws);
+    // Branch calls in one segment: groups of up to G consecutive branches
+    // of one parent per scan workgroup, G chosen so that about two
+    // workgroups per compute unit have work (fewer, longer workgroups
+    // amortise the parent-state load); the plan kernel forms them.
+    PrefillArgs a = a0;
+    a.nseg = nseg;
     int G = 1;
-    if (a.parent) {
+    if (a.parent && nseg == 1) {
         const long long units = (long long)a.H * (DV / TV);
         const long long target = std::max(1LL, (kScanResident + units - 1) / units);
         G = (int)std::max(1LL, ((long long)a.n_seq + target - 1) / target);
-        if (G > 1) sa.groups = chunk_start + wl.grp_off;
-    }
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq, a.n_tokens,
-                       (long long)wl.max_chunks, chunk_start, a.parent, G,
-                       sa.groups ? chunk_start + wl.grp_off : nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (wl.max_chunks > 0) {
-        const dim3 grid((unsigned)wl.max_chunks, a.H);
-        if (a.variant == kKda)
-            hipLaunchKernelGGL(prep(std::integral_constant<int, kKda>{}), grid, dim3(kThreads), 0,
-                               stream, a);
-        else if (a.variant == kRwkv6)
-            hipLaunchKernelGGL(prep(std::integral_constant<int, kRwkv6>{}), grid, dim3(kThreads),
-                               0, stream, a);
-        else
-            hipLaunchKernelGGL(prep(std::integral_constant<int, kScalar>{}), grid, dim3(kThreads),
-                               0, stream, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (G > 1) a.groups = chunk_start + wl.grp_off;
     }
     const size_t n_sh = (size_t)a.n_seq * a.H;
     const size_t sh_pad = (n_sh + 7) / 8 * 8;  // see scan_unit
     const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
-    auto scan = [&](auto ck_tag) {
-        constexpr bool CK = decltype(ck_tag)::value;
-        const dim3 grid((unsigned)(sh_pad * (DV / TV)));
-        if (pk)
-            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, CK>), grid, dim3(kThreads), 0,
-                               stream, sa);
-        else
-            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, CK>), grid, dim3(kThreads), 0,
-                               stream, sa);
-    };
-    if (sa.groups) {  // branch calls never take checkpoints
-        const dim3 grid((unsigned)(sh_pad * (DV / TV)));
-        if (pk)
-            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, false, true>), grid,
-                               dim3(kThreads), 0, stream, sa);
-        else
-            hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, false, true>), grid,
-                               dim3(kThreads), 0, stream, sa);
-        return hipGetLastError();
+    const dim3 scan_grid((unsigned)(sh_pad * (DV / TV)));
+    for (int seg = 0; seg < nseg; ++seg) {
+        a.seg = seg;
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq,
+                           a.n_tokens, (long long)wl.max_chunks, chunk_start, a.parent, G,
+                           const_cast<int32_t *>(a.groups), seg, nseg, chunk_start + wl.win_off);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (wl.max_chunks > 0) {
+            const dim3 grid((unsigned)wl.max_chunks, a.H);
+            if (a.variant == kKda)
+                hipLaunchKernelGGL(prep(std::integral_constant<int, kKda>{}), grid, dim3(kThreads),
+                                   0, stream, a);
+            else if (a.variant == kRwkv6)
+                hipLaunchKernelGGL(prep(std::integral_constant<int, kRwkv6>{}), grid,
+                                   dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL(prep(std::integral_constant<int, kScalar>{}), grid,
+                                   dim3(kThreads), 0, stream, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (a.groups) {  // branch calls never take checkpoints
+            if (pk)
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, false, true>), scan_grid,
+                                   dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, false, true>), scan_grid,
+                                   dim3(kThreads), 0, stream, a);
+        } else if (ck) {
+            if (pk)
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, true>), scan_grid,
+                                   dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, true>), scan_grid,
+                                   dim3(kThreads), 0, stream, a);
+        } else {
+            if (pk)
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, false>), scan_grid,
+                                   dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, false>), scan_grid,
+                                   dim3(kThreads), 0, stream, a);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    if (ck) scan(std::true_type{});
-    else scan(std::false_type{});
-    return hipGetLastError();
+    return hipSuccess;
 }
-
 
 // every value width, io and output type for one key width (one translation
 // unit per key width, so the instances compile in parallel)

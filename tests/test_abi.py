@@ -198,3 +198,25 @@ def test_stream_probe_validation(lib):
     assert lib.gdn_stream_probe(FAKE, FAKE, 1000, 0, NULL) == INVALID   # not a multiple of 16
     assert lib.gdn_stream_probe(FAKE, FAKE, 1024, 2, NULL) == INVALID   # mode 0 or 1
     assert lib.gdn_stream_probe(NULL, NULL, 0, 1, NULL) == OK              # nothing to stream
+
+
+def test_prefill_workspace_runs_in_segments(lib):
+    """The fork_prefill prefix (65,536 tokens, 8 sequences, H=16, d=128)
+    runs in segments whose records stay within 256 MiB: its workspace is at
+    most 0.5 KiB per token-head (one segment would need 1.39 KiB), and a
+    smaller bound gives a smaller workspace."""
+    n, R, H, d = 65536, 8, 16, 128
+    env = "GDN_PREFILL_SEGMENT_RECORD_BYTES"
+    old = os.environ.pop(env, None)
+    try:
+        default = lib.gdn_prefill_workspace_bytes(n, R, H, d, d, 64, 0)
+        assert default <= 512 * n * H, default / (n * H)
+        os.environ[env] = str(1 << 40)  # one segment
+        one = lib.gdn_prefill_workspace_bytes(n, R, H, d, d, 64, 0)
+        assert one > 1.3 * 1024 * n * H
+        os.environ[env] = str(64 << 20)
+        assert lib.gdn_prefill_workspace_bytes(n, R, H, d, d, 64, 0) < default
+    finally:
+        os.environ.pop(env, None)
+        if old is not None:
+            os.environ[env] = old
