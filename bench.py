@@ -526,7 +526,7 @@ def prefill_traffic():
         prof = profiling.read_profile_block(os.path.join(here, "profiles", name))
         if not prof or prof.get("source_hash") != profiling.source_hash(profiling.PREFILL_SOURCES):
             return None
-        total += prof["traffic_bytes"]
+        total += prof["traffic_bytes"] * prof.get("dispatches_per_call", 1)
     return total
 
 

@@ -114,6 +114,9 @@ struct PrefillArgs {
     // segment being run and the number of segments of the prefill
     const int32_t *groups;
     int seg, nseg;
+    // set by the launcher: sequences of at most one chunk run in the
+    // one-chunk kernel (the chunked kernels skip them)
+    int fuse1;
 };
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,

@@ -86,6 +86,21 @@ template <> struct Frag<true> {
     f32x4v hi, lo;
 };
 
+// Two values rounded to bf16 (nearest even) as one 32-bit word, a in the
+// low half (the element order of a bf16 vector in memory).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// hi / lo split of two values as bf16 pair words: hi = bf16(x), lo =
+// bf16(x - hi), with hi widened back from the packed word itself (the
+// compiler's own widening converts each value again).
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = bf16_pair(a, b);
+    lo = bf16_pair(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 template <bool F>
 __device__ __forceinline__ Frag<F> frag(const float (&x)[8]) {
     Frag<F> s;
@@ -93,12 +108,13 @@ __device__ __forceinline__ Frag<F> frag(const float (&x)[8]) {
         s.hi = f32x4v{x[0], x[1], x[2], x[3]};
         s.lo = f32x4v{x[4], x[5], x[6], x[7]};
     } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const __bf16 h = (__bf16)x[e];
-            s.hi[e] = h;
-            s.lo[e] = (__bf16)(x[e] - (float)h);
-        }
+        uint4 h, l;
+        split_pair(x[0], x[1], h.x, l.x);
+        split_pair(x[2], x[3], h.y, l.y);
+        split_pair(x[4], x[5], h.z, l.z);
+        split_pair(x[6], x[7], h.w, l.w);
+        s.hi = __builtin_bit_cast(bf16x8, h);
+        s.lo = __builtin_bit_cast(bf16x8, l);
     }
     return s;
 }
@@ -165,10 +181,11 @@ __device__ __forceinline__ void put4(__bf16 *hi, __bf16 *lo, int o, f32x4v x) {
     if constexpr (F) {
         *reinterpret_cast<f32x4v *>(((o & 7) < 4 ? hi : lo) + (o & ~7)) = x;
     } else {
-        const bf16x4 h = __builtin_convertvector(x, bf16x4);
-        const bf16x4 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4v), bf16x4);
-        *reinterpret_cast<bf16x4 *>(hi + o) = h;
-        *reinterpret_cast<bf16x4 *>(lo + o) = l;
+        uint2 h, l;
+        split_pair(x[0], x[1], h.x, l.x);
+        split_pair(x[2], x[3], h.y, l.y);
+        *reinterpret_cast<uint2 *>(hi + o) = h;
+        *reinterpret_cast<uint2 *>(lo + o) = l;
     }
 }
 
@@ -188,8 +205,11 @@ __device__ __forceinline__ Frag4<F> frag4(f32x4v x) {
     if constexpr (F) {
         s.v = x;
     } else {
-        s.hi = __builtin_convertvector(x, bf16x4);
-        s.lo = __builtin_convertvector(x - __builtin_convertvector(s.hi, f32x4v), bf16x4);
+        uint2 h, l;
+        split_pair(x[0], x[1], h.x, l.x);
+        split_pair(x[2], x[3], h.y, l.y);
+        s.hi = __builtin_bit_cast(bf16x4, h);
+        s.lo = __builtin_bit_cast(bf16x4, l);
     }
     return s;
 }
@@ -337,15 +357,54 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t *cu, int s, int n_toke
     return {a, b - a};
 }
 
+// Exclusive scan of x over the workgroup's threads in thread order under op
+// (associative, with identity id); the value over all threads goes to
+// *total when asked. Wave-wide shuffles, then the waves' totals through LDS.
+// Every thread of the workgroup calls it.
+template <typename T>
+__device__ __forceinline__ T shfl_up_any(T x, int off) {
+    if constexpr (sizeof(T) == 8) {
+        const long long v = (long long)x;
+        const int lo = __shfl_up((int)(v & 0xffffffffLL), off, kWave);
+        const int hi = __shfl_up((int)(v >> 32), off, kWave);
+        return (T)(((long long)hi << 32) | (unsigned)lo);
+    } else {
+        return __shfl_up(x, off, kWave);
+    }
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T block_exclusive_scan(T x, T id, Op op, T *total = nullptr) {
+    __shared__ T s_w[kWaves];
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    T inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const T o = shfl_up_any(inc, off);
+        if (lane >= off) inc = op(o, inc);
+    }
+    const T prev = shfl_up_any(inc, 1);
+    if (lane == kWave - 1) s_w[w] = inc;
+    __syncthreads();
+    T before = id, all = id;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        if (i < w) before = op(before, s_w[i]);
+        all = op(all, s_w[i]);
+    }
+    __syncthreads();  // s_w is free for the next call
+    if (total) *total = all;
+    return op(before, lane == 0 ? id : prev);
+}
+
 // Branch groups for the scan: the maximal runs of consecutive branches with
 // one parent, cut into pieces of at most G branches (a workgroup of the scan
 // then runs a group's branches from one load of the parent state).
 // groups[0] = the count, groups[1 + g] = the first branch of group g,
 // groups[1 + count] = n_seq. One workgroup: per-thread slices of the
-// branches, with the run start carried across slices by a max-scan.
+// branches, with the run start carried across slices by a max-scan (run
+// starts grow with the branch index) and the group counts by a sum-scan.
 __device__ __forceinline__ void plan_groups(const int32_t *parent, int n_seq, int G,
                                             int32_t *groups) {
-    __shared__ int s_run[kThreads], s_cnt[kThreads];
     const int tid = threadIdx.x;
     const int per = (n_seq + kThreads - 1) / kThreads;
     const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
@@ -353,37 +412,20 @@ __device__ __forceinline__ void plan_groups(const int32_t *parent, int n_seq, in
     int last = -1;
     for (int b = lo; b < hi; ++b)
         if (starts_run(b)) last = b;
-    s_run[tid] = last;
-    __syncthreads();
-    if (tid == 0) {  // the run start in effect where each slice begins
-        int run = 0;
-        for (int i = 0; i < kThreads; ++i) {
-            const int x = s_run[i];
-            s_run[i] = run;
-            if (x >= 0) run = x;
-        }
-    }
-    __syncthreads();
-    int rs = s_run[tid], cnt = 0;
+    // the run start in effect where each slice begins
+    const int rs0 = block_exclusive_scan(last, 0, [](int x, int y) { return max(x, y); });
+    int rs = rs0, cnt = 0;
     for (int b = lo; b < hi; ++b) {
         if (starts_run(b)) rs = b;
         cnt += (b - rs) % G == 0;
     }
-    s_cnt[tid] = cnt;
-    __syncthreads();
+    int count = 0;
+    int gi = block_exclusive_scan(cnt, 0, [](int x, int y) { return x + y; }, &count);
     if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < kThreads; ++i) {
-            const int x = s_cnt[i];
-            s_cnt[i] = run;
-            run += x;
-        }
-        groups[0] = run;
-        groups[1 + run] = n_seq;
+        groups[0] = count;
+        groups[1 + count] = n_seq;
     }
-    __syncthreads();
-    int gi = s_cnt[tid];
-    rs = s_run[tid];
+    rs = rs0;
     for (int b = lo; b < hi; ++b) {
         if (starts_run(b)) rs = b;
         if ((b - rs) % G == 0) groups[1 + gi++] = b;
@@ -402,31 +444,21 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n
                                                         int32_t *chunk_start,
                                                         const int32_t *parent, int G,
                                                         int32_t *groups, int seg, int nseg,
-                                                        int32_t *win0) {
-    __shared__ long long s_part[kThreads];
+                                                        int32_t *win0, int fuse1) {
     const int tid = threadIdx.x;
     const int per = (n_seq + kThreads - 1) / kThreads;
     const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
     // sequence s's chunks in this segment: [first, first + count)
+    // (none for a sequence the one-chunk kernel takes)
     const auto window = [&](int s, long long &first) {
-        const long long n = (seq_span(cu, s, n_tokens).len + C - 1) / C;
+        const int len = seq_span(cu, s, n_tokens).len;
+        const long long n = (fuse1 && len <= C) ? 0 : (len + C - 1) / C;
         first = n * seg / nseg;
         return n * (seg + 1) / nseg - first;
     };
     long long sum = 0, first;
     for (int s = lo; s < hi; ++s) sum += window(s, first);
-    s_part[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        long long run = 0;
-        for (int i = 0; i < kThreads; ++i) {
-            const long long x = s_part[i];
-            s_part[i] = run;
-            run += x;
-        }
-    }
-    __syncthreads();
-    long long run = s_part[tid];
+    long long run = block_exclusive_scan(sum, 0LL, [](long long x, long long y) { return x + y; });
     for (int s = lo; s < hi; ++s) {
         chunk_start[s] = (int32_t)min(run, max_chunks);
         run += window(s, first);
@@ -807,17 +839,35 @@ __device__ __forceinline__ void put_planes(const float *src, __bf16 *hi, __bf16 
     }
 }
 
-template <int DK, typename TI, int VAR>
-__device__ __forceinline__ void prep_body(const PrefillArgs &a) {
+// The prep's two LDS buffers (floats): s_k holds the staged K rows
+// [C][DK + 4], then K~^T [DK][C + 1], then P and T' [C][C + 1] side by side;
+// s_A holds A [C][C + 4].
+__host__ __device__ constexpr int prep_sk_floats(int dk) {
+    return std::max({C * (dk + 4), dk * (C + 1), 2 * C * (C + 1)});
+}
+constexpr int kPrepAFloats = C * (C + 4);
+
+// What the one-chunk kernel takes from the prep steps instead of a record
+// (FUSED, scalar decay): the chunk's sequence and head (in), the Q and K A
+// operands of the lane's rows, g of row `lane` and g_L (out), and the
+// prep's LDS: P and T' [C][C + 1] at lds_k and lds_k + C (C + 1) when it
+// returns, free for reuse with lds_a once they are read.
+template <int DK, typename TI>
+struct PrepOut {
+    int s, h;
+    Frag<std::is_same<TI, float>::value> qa[DK / 32], ka[DK / 32];
+    float g, gL;
+    float *lds_k, *lds_a;
+};
+
+template <int DK, typename TI, int VAR, bool FUSED = false>
+__device__ __forceinline__ void prep_body(const PrefillArgs &a, PrepOut<DK, TI> *out = nullptr) {
+    static_assert(!FUSED || VAR == kScalar, "the one-chunk kernel takes a scalar decay");
     constexpr bool kPerKey = VAR != kScalar;
     constexpr bool kDelta = VAR != kRwkv6;
     constexpr bool F = std::is_same<TI, float>::value;  // fp32 operands (see Frag)
     constexpr int KS = DK / 32;
-    constexpr int KP = DK + 4;  // padded row of the staged K rows
-    // staged K rows [C][KP]; then K~^T [DK][C + 1]; then P and T' [C][C + 1]
-    // side by side
-    constexpr int SK0 = C * KP > DK * (C + 1) ? C * KP : DK * (C + 1);
-    constexpr int SK = SK0 > 2 * C * (C + 1) ? SK0 : 2 * C * (C + 1);
+    constexpr int SK = prep_sk_floats(DK);
     __shared__ __attribute__((aligned(16))) float s_k[SK];
     // the split B operand rows of KK^T / QK^T [C][DK] hi / lo, in s_k's space
     static_assert(C * DK <= SK, "split K rows fit s_k");
@@ -826,7 +876,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     // j mod 4 (see a_idx), so the substitution reads them as float4
     constexpr int AP = C + 4;
     const auto a_idx = [](int r, int j) { return r * AP + (j % 4) * (C / 4) + j / 4; };
-    __shared__ __attribute__((aligned(16))) float s_A[C * AP];
+    __shared__ __attribute__((aligned(16))) float s_A[kPrepAFloats];
     // the q / k conv taps live in s_A's space until A is formed
     static_assert(2 * DK * 4 <= C * AP, "taps fit the A buffer");
     float *const s_wq = s_A, *const s_wk = s_A + DK * 4;
@@ -843,13 +893,13 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
     __shared__ int s_slow;
 
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
-    const int gc = blockIdx.x, h = blockIdx.y;
-    if (gc >= chunk_start[a.n_seq]) return;
-    const int s = find_seq(chunk_start, a.n_seq, gc);
+    const int gc = FUSED ? 0 : (int)blockIdx.x, h = FUSED ? out->h : (int)blockIdx.y;
+    if (!FUSED && gc >= chunk_start[a.n_seq]) return;
+    const int s = FUSED ? out->s : find_seq(chunk_start, a.n_seq, gc);
     const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
     const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, a.dv, kPerKey, a.nseg);
     // the chunk's index in its sequence (the segment's window starts there)
-    const int c = gc - chunk_start[s] + chunk_start[wl.win_off + s];
+    const int c = FUSED ? 0 : gc - chunk_start[s] + chunk_start[wl.win_off + s];
     const int H = a.H;
     const int CC = H * (2 * DK + a.dv);
     const int src = a.parent ? a.parent[s] : s;
@@ -859,9 +909,10 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
                                          : nullptr};
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     constexpr RecLayout RL = rec_layout(DK, kPerKey);
-    __bf16 *rec = reinterpret_cast<__bf16 *>(static_cast<char *>(a.ws) + wl.rec_off) +
-                  ((size_t)gc * H + h) * wl.rec_elems;
-    float *const fac = reinterpret_cast<float *>(rec + RL.fac);
+    __bf16 *rec = FUSED ? nullptr
+                        : reinterpret_cast<__bf16 *>(static_cast<char *>(a.ws) + wl.rec_off) +
+                              ((size_t)gc * H + h) * wl.rec_elems;
+    float *const fac = FUSED ? nullptr : reinterpret_cast<float *>(rec + RL.fac);
 
     const bool conv = a.conv_w != nullptr;
     if (conv) {
@@ -984,14 +1035,14 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
                 store_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off, frag<F>(qr));
             } else {
                 qa[ks] = frag<F>(qf[ks]);
-                store_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off, qa[ks]);
+                if constexpr (!FUSED) store_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off, qa[ks]);
             }
         }
     }
     if constexpr (kPerKey) load_k();
     float kf[DK / 32][8];
     rows_compute<DK, TI>(rk, cs, w, conv ? s_wk : nullptr, a.qk_norm != 0, kf);
-    if constexpr (!kPerKey) {
+    if constexpr (!kPerKey && !FUSED) {
         // the scan's row factors: gamma_r, e^{g_L - g_r}, and gamma_L
         if (w == 0) {
             fac[lane] = expf(g);
@@ -1023,7 +1074,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             // rows of KK^T and QK^T, split once, in fragment order: the
             // reader of row block ct takes lane l's piece of wave ct
             ka[ks] = frag<F>(kf[ks]);
-            store_frag<F>(rec + RL.khi + off, rec + RL.klo + off, ka[ks]);
+            if constexpr (!FUSED) store_frag<F>(rec + RL.khi + off, rec + RL.klo + off, ka[ks]);
             store_frag<F>(s_bh + off, s_bl + off, ka[ks]);
         }
     }
@@ -1180,8 +1231,20 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a) {
             s_P[(w * RB + (lane / 16) * 4 + i) * (C + 1) + ct * RB + lane % 16] = pv[ct][i];
     for (int idx = tid; idx < C * C; idx += kThreads) s_T[(idx / C) * TP + idx % C] *= b_l;
     __syncthreads();
-    put_planes<C, F, true>(s_P, rec + RL.phi, rec + RL.plo);
-    put_planes<C, F, true>(s_T, rec + RL.thi, rec + RL.tlo);
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            out->qa[ks] = qa[ks];
+            out->ka[ks] = ka[ks];
+        }
+        out->g = g;
+        out->gL = gL;
+        out->lds_k = s_k;
+        out->lds_a = s_A;
+    } else {
+        put_planes<C, F, true>(s_P, rec + RL.phi, rec + RL.plo);
+        put_planes<C, F, true>(s_T, rec + RL.thi, rec + RL.tlo);
+    }
 }
 
 template <int DK, typename TI>
@@ -1199,6 +1262,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ------------------------------------------------------------ scan
+// Conv window after position `end` of the sequence starting at stream row
+// seq0: its last 3 raw inputs (from the incoming window win where end < 3,
+// zeros without one), head h's q, k and v channels, into wo [3][CC].
+template <int DK, int DV, typename TI>
+__device__ __forceinline__ void write_window(const PrefillArgs &a, int h, int seq0, const TI *win,
+                                             TI *wo, int end) {
+    const int H = a.H, CC = H * (2 * DK + DV), W = 2 * DK + DV;
+    for (int idx = threadIdx.x; idx < 3 * W; idx += kThreads) {
+        const int r = idx / W, wc = idx % W;
+        const int p = end - 3 + r;
+        const int part = wc < DK ? 0 : wc < 2 * DK ? 1 : 2;  // q, k or v
+        const int i = wc - part * DK;
+        const int cch = part == 2 ? 2 * H * DK + h * DV + i : part * H * DK + h * DK + i;
+        TI val = from_f32<TI>(0.f);
+        if (p >= 0) {
+            const size_t row = (size_t)(seq0 + p);
+            if (part == 0) val = static_cast<const TI *>(a.q)[row * H * DK + (size_t)h * DK + i];
+            else if (part == 1) val = static_cast<const TI *>(a.k)[row * H * DK + (size_t)h * DK + i];
+            else val = static_cast<const TI *>(a.v)[row * H * DV + (size_t)h * DV + i];
+        } else if (win) {
+            val = win[(size_t)(3 + p) * CC + cch];
+        }
+        wo[(size_t)r * CC + cch] = val;
+    }
+}
+
 // Workgroup -> (sequence-head, value tile): the NT value tiles of one
 // sequence-head get block indices congruent modulo 8, so they are dispatched
 // to the same XCD and share its L2 for the chunk records they all read.
@@ -1361,6 +1450,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     scan_unit(blockIdx.x, NT, shd, tile);
     if (shd >= a.n_seq * a.H) return;
     const int unit = shd / a.H, h = shd % a.H;
+    // one segment and no chunk records: every sequence is the one-chunk
+    // kernel's (a sequence past one chunk has records in the only segment)
+    if (a.fuse1 && a.nseg == 1 && static_cast<const int32_t *>(a.ws)[a.n_seq] == 0) return;
     // this workgroup's sequences: one, or (branch calls) a group of branches
     // of one parent, which run one after another from one load of the
     // parent's state while no branch changes it
@@ -1392,13 +1484,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     const bool want_o = a.o != nullptr;
     const int kmax = (w * RB + RB - 1) / 32;  // T', P lower triangular: k-steps to use
-    const int acol = (lane / 16) * 8;
-    const int r0v = w * RB + (lane / 16) * 4;  // first of this lane's rows in the C/D layout
-    // the q / k / v base pointers as locals: every load below indexes one of
-    // them directly (a pointer chosen between them would keep them in
-    // private memory, and loads through it would be flat loads)
-    const TI *const qs = static_cast<const TI *>(a.q);
-    const TI *const ks_ = static_cast<const TI *>(a.k);
+    // the v base pointer as a local that every V load indexes directly
     const TI *const vs = static_cast<const TI *>(a.v);
     const int cwin_v = 2 * H * DK + h * DV;
 
@@ -1437,28 +1523,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         __syncthreads();
     };
-    // conv window after position `end` of the sequence: its last 3 raw
-    // inputs (from the incoming window where end < 3), head h's channels
-    auto put_window = [&](TI *wo, int end) {
-        const int W = 2 * DK + DV;
-        for (int idx = tid; idx < 3 * W; idx += kThreads) {
-            const int r = idx / W, wc = idx % W;
-            const int p = end - 3 + r;
-            const int part = wc < DK ? 0 : wc < 2 * DK ? 1 : 2;  // q, k or v
-            const int i = wc - part * DK;
-            const int cch = part == 2 ? 2 * H * DK + h * DV + i : part * H * DK + h * DK + i;
-            TI val = from_f32<TI>(0.f);
-            if (p >= 0) {
-                const size_t row = (size_t)(sp.start + p);
-                if (part == 0) val = qs[row * H * DK + (size_t)h * DK + i];
-                else if (part == 1) val = ks_[row * H * DK + (size_t)h * DK + i];
-                else val = vs[row * H * DV + (size_t)h * DV + i];
-            } else if (win) {
-                val = win[(size_t)(3 + p) * CC + cch];
-            }
-            wo[(size_t)r * CC + cch] = val;
-        }
-    };
+    auto put_window = [&](TI *wo, int end) { write_window<DK, DV, TI>(a, h, sp.start, win, wo, end); };
     // checkpoint k of the sequence: the state and window after
     // (k + 1) * ckpt_every chunks; `ckpt_at(c)` says whether the boundary
     // before chunk c is one (k < ckpt_cap)
@@ -1554,6 +1619,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     bool have = false;  // the registers and planes hold the parent's state
     for (; s < s_last; ++s) {
     sp = seq_span(a.cu, s, a.n_tokens);
+    if (a.fuse1 && sp.len <= C) continue;  // the one-chunk kernel's
     src = a.parent ? a.parent[s] : s;
     ChunkRegs<KS, NVT, TI> nxt;
     if (!(src >= 0 && src < a.n_parent)) {  // invalid parent: NaN outputs, nothing else
@@ -1783,6 +1849,315 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
+// ------------------------------------------------------------ one-chunk sequences
+// Workgroup -> (sequence, head) of the one-chunk kernel: with a head count
+// that is a multiple of 8, head h runs on XCD h mod 8 (block indices
+// congruent mod 8) and consecutive sequences follow one another there, so
+// the branches of one parent read its state tile through one L2.
+__device__ __forceinline__ void one_chunk_unit(int b, int H, int &s, int &h) {
+    if (H % 8 == 0) {
+        const int hx = H / 8, k = b / 8;
+        h = b % 8 + 8 * (k % hx);
+        s = k / hx;
+    } else {
+        s = b / H;
+        h = b % H;
+    }
+}
+
+// A sequence of at most C tokens (a branch of the fork, typically) is one
+// chunk: one workgroup per (sequence, head) runs the prep steps with their
+// results kept on chip -- Q and K as A operands in registers, T' and P in
+// LDS, then in registers -- and the chunk step against the incoming state
+// for each value tile in turn. No chunk record goes through memory and
+// nothing waits on a chain of chunk steps. The arithmetic is the prep's and
+// the scan's in the same order, so the outputs are bit for bit those of the
+// two-kernel path. ST: the sequence's final state is written (the state
+// update runs; K^T is formed once in LDS).
+// LDS: the prep's buffers, reused once T' and P are in registers (s_A: the
+// split state planes; s_k: the R and U planes, or with ST the K^T planes),
+// the value channels' conv taps, and with ST the R, U and W planes (which
+// also stage the state write-out).
+template <int DK, int DV, typename TI, typename TO, bool ST>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2 : 3))) void one_chunk_kernel(
+    PrefillArgs a) {
+    constexpr bool F = std::is_same<TI, float>::value;
+    constexpr int KS = DK / 32;
+    constexpr int CB = C + 8;            // padded row of the R^T / U^T / W^T planes
+    constexpr int NVT = TV / 16;
+    constexpr int NFT = NVT * (DK / 16);
+    constexpr int NEG = NFT / kWaves;
+    static_assert(NFT % kWaves == 0 && NVT == 2, "the scan's tiling");
+    static_assert(2 * TV * DK * 2 <= kPrepAFloats * 4, "split state planes fit the prep's A buffer");
+    static_assert(4 * TV * CB * 2 <= prep_sk_floats(DK) * 4, "R and U planes fit the prep's K buffer");
+    static_assert(2 * DK * C * 2 <= prep_sk_floats(DK) * 4, "K^T planes fit the prep's K buffer");
+    static_assert(DK * TV * 4 <= 6 * TV * CB * 2, "state staging fits the plane buffer");
+    __shared__ __attribute__((aligned(16))) float s_wv[DV * 4];
+    __shared__ __attribute__((aligned(16))) __bf16 s_pl_st[ST ? 6 * TV * CB : 8];
+
+    int s, h;
+    one_chunk_unit(blockIdx.x, a.H, s, h);
+    if (s >= a.n_seq) return;
+    const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
+    if (!a.fuse1 || sp.len > C) return;  // the chunked kernels take it
+    const int H = a.H, CC = H * (2 * DK + DV);
+    const int tid = threadIdx.x;
+    const int src = a.parent ? a.parent[s] : s;
+    TO *const o = static_cast<TO *>(a.o);
+    float *const st_out = ST ? a.state_out + ((size_t)s * H + h) * DK * DV : nullptr;
+    if (!(src >= 0 && src < a.n_parent)) {  // invalid parent: NaN outputs, nothing else
+        if (o)
+            for (int idx = tid; idx < sp.len * DV; idx += kThreads)
+                o[((size_t)(sp.start + idx / DV) * H + h) * DV + idx % DV] = from_f32<TO>(quiet_nan());
+        if constexpr (ST)
+            for (int idx = tid; idx < DK * DV; idx += kThreads) st_out[idx] = quiet_nan();
+        return;
+    }
+    const TI *const win = a.win_in ? static_cast<const TI *>(a.win_in) + (size_t)src * 3 * CC : nullptr;
+    const float *const sin = a.state_in ? a.state_in + ((size_t)src * H + h) * DK * DV : nullptr;
+    if (a.win_out) write_window<DK, DV, TI>(a, h, sp.start, win, static_cast<TI *>(a.win_out) + (size_t)s * 3 * CC, sp.len);
+    if (sp.len == 0) {  // no tokens: the final state is the incoming one
+        if constexpr (ST)
+            for (int idx = tid; idx < DK * DV; idx += kThreads) st_out[idx] = sin ? sin[idx] : 0.f;
+        return;
+    }
+    const bool conv = a.conv_w != nullptr;
+    if (conv) stage_taps(a.conv_w, 2 * H * DK + h * DV, DV, s_wv);  // visible after the prep's barriers
+
+    PrepOut<DK, TI> po;
+    po.s = s;
+    po.h = h;
+    prep_body<DK, TI, kScalar, true>(a, &po);
+
+    const int lane = tid % kWave, w = tid / kWave;
+    const int L = sp.len;
+    const TI *const vs = static_cast<const TI *>(a.v);
+    // A value tile's inputs, requested ahead of use (loads only): the
+    // incoming state tile in this lane's update layout, and the raw V rows
+    // r0v - 3 .. r0v + 3 of its column pair (rows before the sequence from
+    // the incoming window). Addresses: wave-uniform bases plus unsigned
+    // 32-bit lane offsets (the scalar-base form); offsets come from an
+    // opaque copy of the lane.
+    typedef typename VPair<TI>::type VRaw;
+    const unsigned vstride = (unsigned)H * DV * (unsigned)sizeof(TI);  // one stream row of v
+    const auto load_tile = [&](int j0, float (&m4)[NEG][4], VRaw (&vr)[7]) {
+        const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
+        const int r0v = w * RB + (lane / 16) * 4;
+        if (sin) {
+#pragma unroll
+            for (int m = 0; m < NEG; ++m) {
+                const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
+                const unsigned off = 4u * (unsigned)(key0 * DV + j0 + vcol(t * 16 + lane % 16));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m4[m][i] = *byte_at(sin + i * DV, off);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < NEG; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m4[m][i] = 0.f;
+        }
+        const TI *const vbase = vs + ((size_t)sp.start * H + h) * DV + j0;
+        const unsigned col = 2u * (unsigned)(lane % 16) * (unsigned)sizeof(TI);
+#pragma unroll
+        for (int q = 0; q < 7; ++q) {
+            const int p = r0v - 3 + q;
+            vr[q] = *reinterpret_cast<const VRaw *>(byte_at(vbase, (unsigned)min(max(p, 0), L - 1) * vstride + col));
+            if (q < 3 && win && p < 0)  // wave 0's first rows: the incoming window
+                vr[q] = *reinterpret_cast<const VRaw *>(
+                    win + (size_t)(3 + p) * CC + 2 * H * DK + h * DV + j0 + 2 * (lane % 16));
+        }
+    };
+    float nm[NEG][4];
+    VRaw nv[7];
+    load_tile(0, nm, nv);
+    const int kmax = (w * RB + RB - 1) / 32;  // T', P lower triangular: k-steps to use
+    const int acol = (lane / 16) * 8;
+    const int r0v = w * RB + (lane / 16) * 4;  // first of this lane's rows in the C/D layout
+    // T' and P A operands of this wave's rows (the scan's record blocks)
+    Frag<F> ta[2], pa[2];
+    {
+        const float *const s_P = po.lds_k, *const s_T = po.lds_k + C * (C + 1);
+        const int row = w * RB + lane % 16;
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+            if (kq <= kmax) {
+                float x[8], y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    x[e] = s_T[row * (C + 1) + kq * 32 + acol + e];
+                    y[e] = s_P[row * (C + 1) + kq * 32 + acol + e];
+                }
+                ta[kq] = frag<F>(x);
+                pa[kq] = frag<F>(y);
+            }
+    }
+    // the row factors gamma_r, e^{g_L - g_r} of this lane's rows, gamma_L
+    f32x4v gam, gu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float gr = __shfl(po.g, r0v + i, kWave);
+        gam[i] = expf(gr);
+        gu[i] = expf(po.gL - gr);
+    }
+    const float gamL = expf(po.gL);
+    __syncthreads();  // T' and P are read: the prep's LDS is free
+
+    __bf16 *const s_Sh = reinterpret_cast<__bf16 *>(po.lds_a), *const s_Sl = s_Sh + TV * DK;
+    __bf16 *const s_pl = ST ? s_pl_st : reinterpret_cast<__bf16 *>(po.lds_k);
+    __bf16 *const s_Rh = s_pl, *const s_Rl = s_pl + TV * CB;
+    __bf16 *const s_Uh = s_pl + 2 * TV * CB, *const s_Ul = s_pl + 3 * TV * CB;
+    __bf16 *const s_Wh = s_pl + 4 * TV * CB, *const s_Wl = s_pl + 5 * TV * CB;  // ST only
+    __bf16 *const s_Kh = reinterpret_cast<__bf16 *>(po.lds_k), *const s_Kl = s_Kh + DK * C;  // ST only
+    float *const s_stage = reinterpret_cast<float *>(s_pl_st);  // ST only
+    if constexpr (ST)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) put_kt(po.ka[ks], ks * 32 + acol, w * RB + lane % 16, s_Kh, s_Kl);
+
+    const bool want_o = o != nullptr;
+#pragma unroll 1
+    for (int j0 = 0; j0 < DV; j0 += TV) {
+        // lane-derived offsets formed per tile from an opaque copy of the
+        // lane (hoisted out of the loop, they would stay live and spill)
+        const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
+        const int acol = (lane / 16) * 8, r0v = w * RB + (lane / 16) * 4;
+        // this tile's inputs (requested during the previous tile): the
+        // state tile split into the planes (kept with ST for the update),
+        // the V rows convolved
+        float mst[NEG][4];
+#pragma unroll
+        for (int m = 0; m < NEG; ++m) {
+            const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mst[m][i] = nm[m][i];
+            put4<F>(s_Sh, s_Sl, st_off<DK>(t * 16 + lane % 16, key0),
+                    f32x4v{mst[m][0], mst[m][1], mst[m][2], mst[m][3]});
+        }
+        float vf[NVT][4];
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const int jt = j0 + vcol(t * 16 + lane % 16);
+            float xr[7];
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                const int row = r0v - 3 + q;
+                const bool ok = (conv || q >= 3) && ((row < L && row >= 0) || (row < 0 && win));
+                xr[q] = ok ? VPair<TI>::get(nv[q], t) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float y = xr[i + 3];
+                if (conv) {
+                    y = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) y = fmaf(s_wv[jt * 4 + r], xr[i + r], y);
+                }
+                vf[t][i] = r0v + i < L ? y : 0.f;
+            }
+        }
+        __syncthreads();  // the state planes
+
+        // R = V - diag(gamma) K Sig0 -> planes; Q Sig0 in registers
+        f32x4v acc_o[NVT];
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+            acc_o[t] = acc;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int so = st_off<DK>(t * 16 + lane % 16, ks * 32 + acol);
+                const Frag<F> bs = read_frag<F>(s_Sh + so, s_Sl + so);
+                acc = mma(po.ka[ks], bs, acc);
+                if (want_o) acc_o[t] = mma(po.qa[ks], bs, acc_o[t]);
+            }
+            f32x4v rv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rv[i] = vf[t][i] - gam[i] * acc[i];
+            put4<F>(s_Rh, s_Rl, (t * 16 + lane % 16) * CB + r0v, rv);
+        }
+        if (j0 + TV < DV) load_tile(j0 + TV, nm, nv);  // the next tile's inputs
+        __syncthreads();
+
+        // U = T' R (and W = diag(e^{g_L - g}) U for the state update)
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq)
+                if (kq <= kmax) {
+                    const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                    acc = mma(ta[kq], read_frag<F>(s_Rh + off, s_Rl + off), acc);
+                }
+            const int uo = (t * 16 + lane % 16) * CB + r0v;
+            put4<F>(s_Uh, s_Ul, uo, acc);
+            if constexpr (ST) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] *= gu[i];
+                put4<F>(s_Wh, s_Wl, uo, acc);
+            }
+        }
+        __syncthreads();
+
+        // O = diag(gamma) Q Sig0 + P U
+        if (want_o) {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc_o[t][i] *= gam[i];
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq)
+                    if (kq <= kmax) {
+                        const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                        acc_o[t] = mma(pa[kq], read_frag<F>(s_Uh + off, s_Ul + off), acc_o[t]);
+                    }
+            }
+            TO *const obase = o + ((size_t)sp.start * H + h) * DV + j0;
+            const unsigned ostride = (unsigned)H * DV;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0v + i;
+                if (r < L)
+                    store_pair(byte_at(obase, ((unsigned)r * ostride + 2u * (lane % 16)) * (unsigned)sizeof(TO)),
+                               acc_o[0][i], acc_o[1][i]);
+            }
+        }
+
+        if constexpr (ST) {
+            // Sig <- gamma_L Sig + K^T W, then the tile out through the staging
+#pragma unroll
+            for (int m = 0; m < NEG; ++m) {
+                const int ft = w + m * kWaves, t = ft % NVT, dt = ft / NVT;
+                f32x4v acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = gamL * mst[m][i];
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) {
+                    const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
+                    const int ok = kt_off(dt * 16 + lane % 16, kq * 32 + acol);
+                    acc = mma(read_frag<F>(s_Kh + ok, s_Kl + ok), read_frag<F>(s_Wh + ou, s_Wl + ou), acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mst[m][i] = acc[i];
+            }
+            __syncthreads();  // U and W are read: the plane buffer stages the tile
+#pragma unroll
+            for (int m = 0; m < NEG; ++m) {
+                const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
+                const int col = vcol(t * 16 + lane % 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_stage[(key0 + i) * TV + col] = mst[m][i];
+            }
+            __syncthreads();
+            for (int idx = tid; idx < DK * TV / 4; idx += kThreads) {
+                const int d = idx / (TV / 4), j = 4 * (idx % (TV / 4));
+                *reinterpret_cast<float4 *>(st_out + (size_t)d * DV + j0 + j) =
+                    *reinterpret_cast<const float4 *>(s_stage + d * TV + j);
+            }
+            __syncthreads();
+        }
+    }
+}
+
 template <int DK, int DV, typename TI, typename TO>
 hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
     auto prep = [&](auto vtag) {
@@ -1812,11 +2187,27 @@ hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
     const size_t sh_pad = (n_sh + 7) / 8 * 8;  // see scan_unit
     const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
     const dim3 scan_grid((unsigned)(sh_pad * (DV / TV)));
+    // Sequences of at most one chunk (scalar decay, no checkpoints) run in
+    // the one-chunk kernel; the plan gives them no records and the scan
+    // skips them. GDN_PREFILL_ONE_CHUNK=0 sends them through the chunked
+    // kernels instead (the same results bit for bit; for tests).
+    const char *oc = std::getenv("GDN_PREFILL_ONE_CHUNK");
+    a.fuse1 = a.variant == kScalar && !ck && !(oc && oc[0] == '0');
+    if (a.fuse1) {
+        const dim3 g1((unsigned)n_sh);
+        if (a.state_out)
+            hipLaunchKernelGGL((one_chunk_kernel<DK, DV, TI, TO, true>), g1, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((one_chunk_kernel<DK, DV, TI, TO, false>), g1, dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     for (int seg = 0; seg < nseg; ++seg) {
         a.seg = seg;
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq,
                            a.n_tokens, (long long)wl.max_chunks, chunk_start, a.parent, G,
-                           const_cast<int32_t *>(a.groups), seg, nseg, chunk_start + wl.win_off);
+                           const_cast<int32_t *>(a.groups), seg, nseg, chunk_start + wl.win_off,
+                           a.fuse1);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (wl.max_chunks > 0) {

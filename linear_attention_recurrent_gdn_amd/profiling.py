@@ -5,7 +5,8 @@
         <kernel-substring> <pass_dir> [<pass_dir> ...] [--sources attention|decode|prefill] \
         [--grid N]
     python -m linear_attention_recurrent_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
-        <out.md> "<command>" <kernel-substring> [--grid N] [--copy-bytes B] [--sources decode|prefill]
+        <out.md> "<command>" <kernel-substring> [--grid N] [--copy-bytes B] [--per-call K] \
+        [--sources decode|prefill]
 
 `counters` averages every counter of one or more --pmc passes per dispatch
 of the named kernel (e.g. SQ_* utilisation and LDS counters).
@@ -17,6 +18,9 @@ kernel (optionally only its dispatches of one grid size), each counter
 scaled by what it reads for a plain device copy of known size in the same
 run (the bench's bandwidth probe copies 4 GiB), and records a hash of the
 kernel sources so a later reader can tell whether the numbers still apply.
+--per-call K records that one call of the operation launches the kernel K
+times at that grid (a prefill in K segments), so per-call bytes are K times
+the per-dispatch mean.
 The machine-readable figures sit in a ```json block of the markdown.
 """
 
@@ -88,7 +92,7 @@ def _counter_rows(d):
 
 
 def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_bytes=4 << 30,
-                    sources=DECODE_SOURCES, grid=None):
+                    sources=DECODE_SOURCES, grid=None, per_call=1):
     fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
     copy_kib = copy_bytes / 1024
 
@@ -114,7 +118,7 @@ def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_byte
     wr = statistics.mean(kw) * w_scale * 1024
     data = dict(kernel=kname, grid=grid, dispatches=len(kf), fetch_kib_raw=statistics.mean(kf),
                 write_kib_raw=statistics.mean(kw), fetch_scale=f_scale, write_scale=w_scale,
-                read_bytes=rd, write_bytes=wr, traffic_bytes=rd + wr,
+                read_bytes=rd, write_bytes=wr, traffic_bytes=rd + wr, dispatches_per_call=per_call,
                 calibration=f"plain device copy of {copy_bytes} bytes: FETCH_SIZE "
                             f"{statistics.median(cf):.0f} KiB, WRITE_SIZE "
                             f"{statistics.median(cw):.0f} KiB per dispatch",
@@ -129,7 +133,9 @@ def traffic_summary(fetch_dir, write_dir, out_md, command, kernel_sub, copy_byte
              f"{rd/1e6:.1f} MB read",
              f"- WRITE_SIZE {data['write_kib_raw']:.0f} KiB/dispatch x {w_scale:.4f} = "
              f"{wr/1e6:.1f} MB written",
-             f"- traffic {(rd+wr)/1e6:.1f} MB per dispatch",
+             f"- traffic {(rd+wr)/1e6:.1f} MB per dispatch"
+             + (f", {per_call} dispatches per call: {per_call*(rd+wr)/1e6:.1f} MB per call"
+                if per_call > 1 else ""),
              f"- scale factors from a {data['calibration']}", "",
              "```json", json.dumps(data, indent=1), "```", ""]
     open(out_md, "w").write("\n".join(lines))
@@ -174,6 +180,7 @@ def main(argv):
         f.add_argument(name)
     f.add_argument("--grid", type=int, default=None)
     f.add_argument("--copy-bytes", type=int, default=4 << 30)
+    f.add_argument("--per-call", type=int, default=1)
     f.add_argument("--sources", choices=("decode", "prefill"), default="decode")
     c = sub.add_parser("counters")
     c.add_argument("out_md")
@@ -190,7 +197,7 @@ def main(argv):
                          grid=a.grid)
     else:
         traffic_summary(a.fetch_dir, a.write_dir, a.out_md, a.command, a.kernel_sub,
-                        copy_bytes=a.copy_bytes, grid=a.grid,
+                        copy_bytes=a.copy_bytes, grid=a.grid, per_call=a.per_call,
                         sources=DECODE_SOURCES if a.sources == "decode" else PREFILL_SOURCES)
 
 

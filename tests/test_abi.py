@@ -202,7 +202,7 @@ def test_stream_probe_validation(lib):
 
 def test_prefill_workspace_runs_in_segments(lib):
     """The fork_prefill prefix (65,536 tokens, 8 sequences, H=16, d=128)
-    runs in segments whose records stay within 256 MiB: its workspace is at
+    runs in segments whose records stay within 512 MiB: its workspace is at
     most 0.5 KiB per token-head (one segment would need 1.39 KiB), and a
     smaller bound gives a smaller workspace."""
     n, R, H, d = 65536, 8, 16, 128
