@@ -1876,8 +1876,7 @@ __device__ __forceinline__ void one_chunk_unit(int b, int H, int &s, int &h) {
 // update runs; K^T is formed once in LDS).
 // LDS: the prep's buffers, reused once T' and P are in registers (s_A: the
 // split state planes; s_k: the R and U planes, or with ST the K^T planes),
-// the value channels' conv taps, and with ST the R, U and W planes (which
-// also stage the state write-out).
+// the value channels' conv taps, and with ST the R, U and W planes.
 template <int DK, int DV, typename TI, typename TO, bool ST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2 : 3))) void one_chunk_kernel(
     PrefillArgs a) {
@@ -1891,7 +1890,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
     static_assert(2 * TV * DK * 2 <= kPrepAFloats * 4, "split state planes fit the prep's A buffer");
     static_assert(4 * TV * CB * 2 <= prep_sk_floats(DK) * 4, "R and U planes fit the prep's K buffer");
     static_assert(2 * DK * C * 2 <= prep_sk_floats(DK) * 4, "K^T planes fit the prep's K buffer");
-    static_assert(DK * TV * 4 <= 6 * TV * CB * 2, "state staging fits the plane buffer");
     __shared__ __attribute__((aligned(16))) float s_wv[DV * 4];
     __shared__ __attribute__((aligned(16))) __bf16 s_pl_st[ST ? 6 * TV * CB : 8];
 
@@ -2009,7 +2007,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
     __bf16 *const s_Uh = s_pl + 2 * TV * CB, *const s_Ul = s_pl + 3 * TV * CB;
     __bf16 *const s_Wh = s_pl + 4 * TV * CB, *const s_Wl = s_pl + 5 * TV * CB;  // ST only
     __bf16 *const s_Kh = reinterpret_cast<__bf16 *>(po.lds_k), *const s_Kl = s_Kh + DK * C;  // ST only
-    float *const s_stage = reinterpret_cast<float *>(s_pl_st);  // ST only
     if constexpr (ST)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) put_kt(po.ka[ks], ks * 32 + acol, w * RB + lane % 16, s_Kh, s_Kl);
@@ -2123,7 +2120,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
         }
 
         if constexpr (ST) {
-            // Sig <- gamma_L Sig + K^T W, then the tile out through the staging
+            // Sig <- gamma_L Sig + K^T W, each lane's 4 keys of its value
+            // column straight out (the next tile rewrites no buffer this
+            // reads before its own barriers)
 #pragma unroll
             for (int m = 0; m < NEG; ++m) {
                 const int ft = w + m * kWaves, t = ft % NVT, dt = ft / NVT;
@@ -2136,24 +2135,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
                     const int ok = kt_off(dt * 16 + lane % 16, kq * 32 + acol);
                     acc = mma(read_frag<F>(s_Kh + ok, s_Kl + ok), read_frag<F>(s_Wh + ou, s_Wl + ou), acc);
                 }
+                const unsigned off = 4u * (unsigned)((dt * 16 + (lane / 16) * 4) * DV + j0 + vcol(t * 16 + lane % 16));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mst[m][i] = acc[i];
+                for (int i = 0; i < 4; ++i) *byte_at(st_out + i * DV, off) = acc[i];
             }
-            __syncthreads();  // U and W are read: the plane buffer stages the tile
-#pragma unroll
-            for (int m = 0; m < NEG; ++m) {
-                const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
-                const int col = vcol(t * 16 + lane % 16);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s_stage[(key0 + i) * TV + col] = mst[m][i];
-            }
-            __syncthreads();
-            for (int idx = tid; idx < DK * TV / 4; idx += kThreads) {
-                const int d = idx / (TV / 4), j = 4 * (idx % (TV / 4));
-                *reinterpret_cast<float4 *>(st_out + (size_t)d * DV + j0 + j) =
-                    *reinterpret_cast<const float4 *>(s_stage + d * TV + j);
-            }
-            __syncthreads();
         }
     }
 }
