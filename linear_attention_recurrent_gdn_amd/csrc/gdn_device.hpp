@@ -115,8 +115,9 @@ struct PrefillArgs {
     const int32_t *groups;
     int seg, nseg;
     // set by the launcher: sequences of at most one chunk run in the
-    // one-chunk kernel (the chunked kernels skip them)
-    int fuse1;
+    // one-chunk kernel (the chunked kernels skip them); the branch group
+    // size
+    int fuse1, group_size;
 };
 
 size_t prefill_workspace_bytes(int n_tokens, int n_seq, int H, int dk, int dv,

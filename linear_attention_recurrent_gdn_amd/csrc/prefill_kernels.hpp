@@ -438,13 +438,13 @@ __device__ __forceinline__ void plan_groups(const int32_t *parent, int n_seq, in
 // chunk_start[s] = min(sum of the earlier sequences' counts, max_chunks) is
 // its first record, and it owns chunk_start[s+1] - chunk_start[s]. With
 // valid offsets the cap never binds; with overlapping (invalid) offsets it
-// keeps every record inside the workspace.
-__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n_seq, int n_tokens,
-                                                        long long max_chunks,
-                                                        int32_t *chunk_start,
-                                                        const int32_t *parent, int G,
-                                                        int32_t *groups, int seg, int nseg,
-                                                        int32_t *win0, int fuse1) {
+// keeps every record inside the workspace. One workgroup; plan_kernel
+// launches it alone, and the one-chunk kernel runs it for the first segment
+// in an extra workgroup of its own grid.
+__device__ __forceinline__ void plan_body(const int32_t *cu, int n_seq, int n_tokens,
+                                          long long max_chunks, int32_t *chunk_start,
+                                          const int32_t *parent, int G, int32_t *groups, int seg,
+                                          int nseg, int32_t *win0, int fuse1) {
     const int tid = threadIdx.x;
     const int per = (n_seq + kThreads - 1) / kThreads;
     const int lo = min(tid * per, n_seq), hi = min(lo + per, n_seq);
@@ -466,6 +466,16 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n
     }
     if (tid == kThreads - 1) chunk_start[n_seq] = (int32_t)min(run, max_chunks);
     if (groups) plan_groups(parent, n_seq, G, groups);  // branch calls
+}
+
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *cu, int n_seq, int n_tokens,
+                                                        long long max_chunks,
+                                                        int32_t *chunk_start,
+                                                        const int32_t *parent, int G,
+                                                        int32_t *groups, int seg, int nseg,
+                                                        int32_t *win0, int fuse1) {
+    plan_body(cu, n_seq, n_tokens, max_chunks, chunk_start, parent, G, groups, seg, nseg, win0,
+              fuse1);
 }
 
 __device__ __forceinline__ int find_seq(const int32_t *chunk_start, int n_seq, int gc) {
@@ -1893,6 +1903,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
     __shared__ __attribute__((aligned(16))) float s_wv[DV * 4];
     __shared__ __attribute__((aligned(16))) __bf16 s_pl_st[ST ? 6 * TV * CB : 8];
 
+    if (blockIdx.x == gridDim.x - 1) {  // the extra workgroup: the first segment's plan
+        const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, DV, false, a.nseg);
+        int32_t *const chunk_start = static_cast<int32_t *>(a.ws);
+        plan_body(a.cu, a.n_seq, a.n_tokens, (long long)wl.max_chunks, chunk_start, a.parent,
+                  a.group_size, const_cast<int32_t *>(a.groups), 0, a.nseg,
+                  chunk_start + wl.win_off, a.fuse1);
+        return;
+    }
     int s, h;
     one_chunk_unit(blockIdx.x, a.H, s, h);
     if (s >= a.n_seq) return;
@@ -2178,8 +2196,9 @@ hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
     // kernels instead (the same results bit for bit; for tests).
     const char *oc = std::getenv("GDN_PREFILL_ONE_CHUNK");
     a.fuse1 = a.variant == kScalar && !ck && !(oc && oc[0] == '0');
-    if (a.fuse1) {
-        const dim3 g1((unsigned)n_sh);
+    a.group_size = G;
+    if (a.fuse1) {  // with one more workgroup: the first segment's plan
+        const dim3 g1((unsigned)(n_sh + 1));
         if (a.state_out)
             hipLaunchKernelGGL((one_chunk_kernel<DK, DV, TI, TO, true>), g1, dim3(kThreads), 0, stream, a);
         else
@@ -2189,12 +2208,15 @@ hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
     }
     for (int seg = 0; seg < nseg; ++seg) {
         a.seg = seg;
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq,
-                           a.n_tokens, (long long)wl.max_chunks, chunk_start, a.parent, G,
-                           const_cast<int32_t *>(a.groups), seg, nseg, chunk_start + wl.win_off,
-                           a.fuse1);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        hipError_t e = hipSuccess;
+        if (seg > 0 || !a.fuse1) {
+            hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu, a.n_seq,
+                               a.n_tokens, (long long)wl.max_chunks, chunk_start, a.parent, G,
+                               const_cast<int32_t *>(a.groups), seg, nseg, chunk_start + wl.win_off,
+                               a.fuse1);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         if (wl.max_chunks > 0) {
             const dim3 grid((unsigned)wl.max_chunks, a.H);
             if (a.variant == kKda)
