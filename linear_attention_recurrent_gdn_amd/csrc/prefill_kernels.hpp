@@ -1960,13 +1960,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
         const int lane = __builtin_amdgcn_update_dpp(0, tid % kWave, 0xE4, 0xf, 0xf, false);
         const int r0v = w * RB + (lane / 16) * 4;
         if (sin) {
+            // tile m of the wave is keys 32 m further down (ft = w + 4 m, two
+            // value sub-tiles): one lane offset, the rest in the uniform base
+            static_assert(kWaves == 4 && NVT == 2, "key step of the wave's state tiles");
+            const int key0 = (w / NVT) * 16 + (lane / 16) * 4;
+            const unsigned off = 4u * (unsigned)(key0 * DV + j0 + vcol((w % NVT) * 16 + lane % 16));
 #pragma unroll
-            for (int m = 0; m < NEG; ++m) {
-                const int ft = w + m * kWaves, t = ft % NVT, key0 = (ft / NVT) * 16 + (lane / 16) * 4;
-                const unsigned off = 4u * (unsigned)(key0 * DV + j0 + vcol(t * 16 + lane % 16));
+            for (int m = 0; m < NEG; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) m4[m][i] = *byte_at(sin + i * DV, off);
-            }
+                for (int i = 0; i < 4; ++i) m4[m][i] = *byte_at(sin + (32 * m + i) * DV, off);
         } else {
 #pragma unroll
             for (int m = 0; m < NEG; ++m)
