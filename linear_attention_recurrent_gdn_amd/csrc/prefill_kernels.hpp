@@ -857,22 +857,33 @@ __host__ __device__ constexpr int prep_sk_floats(int dk) {
 }
 constexpr int kPrepAFloats = C * (C + 4);
 
-// What the one-chunk kernel takes from the prep steps instead of a record
-// (FUSED, scalar decay): the chunk's sequence and head (in), the Q and K A
-// operands of the lane's rows, g of row `lane` and g_L (out), and the
-// prep's LDS: P and T' [C][C + 1] at lds_k and lds_k + C (C + 1) when it
-// returns, free for reuse with lds_a once they are read.
+// How prep_body finds its chunk and where its results go: kPrepGrid, the
+// prep kernel (chunk and head from the block index, the record in the
+// workspace); for the one-chunk kernel (chunk 0 of out->s, head out->h),
+// kPrepOnChip (scalar decay: no record, the operands handed over in
+// PrepOut) or kPrepToSlot (per-key decay: the record written to the
+// workspace slot of the (sequence, head), read back by the same
+// workgroup).
+enum PrepMode { kPrepGrid = 0, kPrepOnChip = 1, kPrepToSlot = 2 };
+
+// What the one-chunk kernel takes from the prep steps: the chunk's sequence
+// and head (in), with kPrepOnChip the Q and K A operands of the lane's rows,
+// g of row `lane` and g_L (out), and the prep's LDS: P and T' [C][C + 1] at
+// lds_k and lds_k + C (C + 1) when it returns, free for reuse with lds_a
+// and lds_tab (per key, [4 kWaves + 10] DK floats) once they are read.
 template <int DK, typename TI>
 struct PrepOut {
     int s, h;
     Frag<std::is_same<TI, float>::value> qa[DK / 32], ka[DK / 32];
     float g, gL;
-    float *lds_k, *lds_a;
+    float *lds_k, *lds_a, *lds_tab;
 };
 
-template <int DK, typename TI, int VAR, bool FUSED = false>
+template <int DK, typename TI, int VAR, int MODE = kPrepGrid>
 __device__ __forceinline__ void prep_body(const PrefillArgs &a, PrepOut<DK, TI> *out = nullptr) {
-    static_assert(!FUSED || VAR == kScalar, "the one-chunk kernel takes a scalar decay");
+    constexpr bool FUSED = MODE == kPrepOnChip;  // operands kept on chip, no record
+    constexpr bool ONE = MODE != kPrepGrid;      // the one-chunk kernel's chunk
+    static_assert(!FUSED || VAR == kScalar, "operands on chip with a scalar decay only");
     constexpr bool kPerKey = VAR != kScalar;
     constexpr bool kDelta = VAR != kRwkv6;
     constexpr bool F = std::is_same<TI, float>::value;  // fp32 operands (see Frag)
@@ -903,13 +914,13 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a, PrepOut<DK, TI> 
     __shared__ int s_slow;
 
     const int32_t *chunk_start = static_cast<const int32_t *>(a.ws);
-    const int gc = FUSED ? 0 : (int)blockIdx.x, h = FUSED ? out->h : (int)blockIdx.y;
-    if (!FUSED && gc >= chunk_start[a.n_seq]) return;
-    const int s = FUSED ? out->s : find_seq(chunk_start, a.n_seq, gc);
+    const int gc = ONE ? 0 : (int)blockIdx.x, h = ONE ? out->h : (int)blockIdx.y;
+    if (!ONE && gc >= chunk_start[a.n_seq]) return;
+    const int s = ONE ? out->s : find_seq(chunk_start, a.n_seq, gc);
     const SeqSpan sp = seq_span(a.cu, s, a.n_tokens);
     const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, a.dv, kPerKey, a.nseg);
     // the chunk's index in its sequence (the segment's window starts there)
-    const int c = FUSED ? 0 : gc - chunk_start[s] + chunk_start[wl.win_off + s];
+    const int c = ONE ? 0 : gc - chunk_start[s] + chunk_start[wl.win_off + s];
     const int H = a.H;
     const int CC = H * (2 * DK + a.dv);
     const int src = a.parent ? a.parent[s] : s;
@@ -919,9 +930,10 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a, PrepOut<DK, TI> 
                                          : nullptr};
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     constexpr RecLayout RL = rec_layout(DK, kPerKey);
+    // the record: of chunk gc, or (kPrepToSlot) in slot s H + h
     __bf16 *rec = FUSED ? nullptr
                         : reinterpret_cast<__bf16 *>(static_cast<char *>(a.ws) + wl.rec_off) +
-                              ((size_t)gc * H + h) * wl.rec_elems;
+                              ((size_t)(ONE ? s : gc) * H + h) * wl.rec_elems;
     float *const fac = FUSED ? nullptr : reinterpret_cast<float *>(rec + RL.fac);
 
     const bool conv = a.conv_w != nullptr;
@@ -1254,6 +1266,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs &a, PrepOut<DK, TI> 
     } else {
         put_planes<C, F, true>(s_P, rec + RL.phi, rec + RL.plo);
         put_planes<C, F, true>(s_T, rec + RL.thi, rec + RL.tlo);
+        if constexpr (ONE) {
+            out->lds_k = s_k;
+            out->lds_a = s_A;
+            out->lds_tab = s_tab;
+        }
     }
 }
 
@@ -1884,12 +1901,22 @@ __device__ __forceinline__ void one_chunk_unit(int b, int H, int &s, int &h) {
 // the scan's in the same order, so the outputs are bit for bit those of the
 // two-kernel path. ST: the sequence's final state is written (the state
 // update runs; K^T is formed once in LDS).
+// Per-key decay (VAR kKda / kRwkv6): the prep steps write the chunk record
+// into the workspace slot of the (sequence, head) as the prep kernel would,
+// and the workgroup reads its operands back from there (mostly from L2):
+// Q^ and K^ into registers, with ST K~^T and e^{g_L} per key into LDS; the
+// chunk step is the scan's per-key one (gamma = 1, the state decayed per
+// key column).
 // LDS: the prep's buffers, reused once T' and P are in registers (s_A: the
 // split state planes; s_k: the R and U planes, or with ST the K^T planes),
-// the value channels' conv taps, and with ST the R, U and W planes.
-template <int DK, int DV, typename TI, typename TO, bool ST>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2 : 3))) void one_chunk_kernel(
+// the value channels' conv taps, and with ST the R, U and W planes (per
+// key: R and U in one pair of planes in the prep's table buffer, U written
+// over R behind a barrier, and e^{g_L} after them).
+template <int DK, int DV, typename TI, typename TO, bool ST, int VAR = kScalar>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST || VAR != kScalar ? 2 : 3))) void one_chunk_kernel(
     PrefillArgs a) {
+    constexpr bool PK = VAR != kScalar;
+    constexpr bool RU1 = PK && ST;  // R and U share one pair of planes
     constexpr bool F = std::is_same<TI, float>::value;
     constexpr int KS = DK / 32;
     constexpr int CB = C + 8;            // padded row of the R^T / U^T / W^T planes
@@ -1900,11 +1927,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
     static_assert(2 * TV * DK * 2 <= kPrepAFloats * 4, "split state planes fit the prep's A buffer");
     static_assert(4 * TV * CB * 2 <= prep_sk_floats(DK) * 4, "R and U planes fit the prep's K buffer");
     static_assert(2 * DK * C * 2 <= prep_sk_floats(DK) * 4, "K^T planes fit the prep's K buffer");
+    // per key with ST: the shared R / U planes and e^{g_L} after the K~^T
+    // planes in the prep's K buffer where they fit, else in its table
+    constexpr int kRUBytes = 2 * TV * CB * 2 + DK * 4;
+    constexpr bool RU_IN_K = prep_sk_floats(DK) * 4 - 2 * DK * C * 2 >= kRUBytes;
+    static_assert(!RU1 || RU_IN_K || kRUBytes <= (4 * kWaves + 10) * DK * 4,
+                  "per key: R / U planes and e^{g_L} fit the prep's buffers");
     __shared__ __attribute__((aligned(16))) float s_wv[DV * 4];
-    __shared__ __attribute__((aligned(16))) __bf16 s_pl_st[ST ? 6 * TV * CB : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 s_pl_st[ST && !PK ? 6 * TV * CB : 8];
 
     if (blockIdx.x == gridDim.x - 1) {  // the extra workgroup: the first segment's plan
-        const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, DV, false, a.nseg);
+        const WsLayout wl = ws_layout(a.n_tokens, a.n_seq, a.H, DK, DV, PK, a.nseg);
         int32_t *const chunk_start = static_cast<int32_t *>(a.ws);
         plan_body(a.cu, a.n_seq, a.n_tokens, (long long)wl.max_chunks, chunk_start, a.parent,
                   a.group_size, const_cast<int32_t *>(a.groups), 0, a.nseg,
@@ -1943,7 +1976,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
     PrepOut<DK, TI> po;
     po.s = s;
     po.h = h;
-    prep_body<DK, TI, kScalar, true>(a, &po);
+    prep_body<DK, TI, VAR, PK ? kPrepToSlot : kPrepOnChip>(a, &po);
+    constexpr RecLayout RL = rec_layout(DK, PK);
+    const __bf16 *const rec =
+        PK ? reinterpret_cast<const __bf16 *>(static_cast<const char *>(a.ws) +
+                                              ws_layout(a.n_tokens, a.n_seq, H, DK, DV, PK, a.nseg).rec_off) +
+                 ((size_t)s * H + h) * rec_layout(DK, PK).elems
+           : nullptr;
+    if constexpr (PK) __syncthreads();  // the record in the slot is complete
 
     const int lane = tid % kWave, w = tid / kWave;
     const int L = sp.len;
@@ -2011,25 +2051,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
             }
     }
     // the row factors gamma_r, e^{g_L - g_r} of this lane's rows, gamma_L
-    f32x4v gam, gu;
+    // (per key: 1, the decay sits in the operands and e^{g_L})
+    f32x4v gam = {1.f, 1.f, 1.f, 1.f}, gu = gam;
+    float gamL = 1.f;
+    if constexpr (!PK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float gr = __shfl(po.g, r0v + i, kWave);
-        gam[i] = expf(gr);
-        gu[i] = expf(po.gL - gr);
+        for (int i = 0; i < 4; ++i) {
+            const float gr = __shfl(po.g, r0v + i, kWave);
+            gam[i] = expf(gr);
+            gu[i] = expf(po.gL - gr);
+        }
+        gamL = expf(po.gL);
+    } else {  // Q^, K^ from the record
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off = frag_off(KS, w, ks, lane);
+            po.ka[ks] = read_frag<F>(rec + RL.khi + off, rec + RL.klo + off);
+            po.qa[ks] = read_frag<F>(rec + RL.qhi + off, rec + RL.qlo + off);
+        }
     }
-    const float gamL = expf(po.gL);
     __syncthreads();  // T' and P are read: the prep's LDS is free
 
     __bf16 *const s_Sh = reinterpret_cast<__bf16 *>(po.lds_a), *const s_Sl = s_Sh + TV * DK;
-    __bf16 *const s_pl = ST ? s_pl_st : reinterpret_cast<__bf16 *>(po.lds_k);
+    __bf16 *const s_pl = RU1 ? (RU_IN_K ? reinterpret_cast<__bf16 *>(po.lds_k) + 2 * DK * C
+                                        : reinterpret_cast<__bf16 *>(po.lds_tab))
+                             : ST ? s_pl_st : reinterpret_cast<__bf16 *>(po.lds_k);
     __bf16 *const s_Rh = s_pl, *const s_Rl = s_pl + TV * CB;
-    __bf16 *const s_Uh = s_pl + 2 * TV * CB, *const s_Ul = s_pl + 3 * TV * CB;
-    __bf16 *const s_Wh = s_pl + 4 * TV * CB, *const s_Wl = s_pl + 5 * TV * CB;  // ST only
-    __bf16 *const s_Kh = reinterpret_cast<__bf16 *>(po.lds_k), *const s_Kl = s_Kh + DK * C;  // ST only
-    if constexpr (ST)
+    __bf16 *const s_Uh = RU1 ? s_Rh : s_pl + 2 * TV * CB, *const s_Ul = RU1 ? s_Rl : s_pl + 3 * TV * CB;
+    __bf16 *const s_Wh = s_pl + 4 * TV * CB, *const s_Wl = s_pl + 5 * TV * CB;  // ST, scalar decay
+    __bf16 *const s_Kh = reinterpret_cast<__bf16 *>(po.lds_k), *const s_Kl = s_Kh + DK * C;  // ST
+    float *const s_eg = reinterpret_cast<float *>(s_pl + 2 * TV * CB);  // ST, per key: e^{g_L}
+    if constexpr (ST) {
+        if constexpr (PK) {
+            // K~^T planes (swizzled rows, as the scan stages them) and e^{g_L}
+            // from the record by direct-to-LDS copies, finished before the
+            // first tile's barrier
+            constexpr int PER_WAVE = DK * C * 2 / 16 / kThreads;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) put_kt(po.ka[ks], ks * 32 + acol, w * RB + lane % 16, s_Kh, s_Kl);
+            for (int q = 0; q < PER_WAVE; ++q) {
+                const int piece = (q * kWaves + w) * kWave + lane;
+                const int r = piece / 8, chl = piece % 8, chg = chl ^ (r & 7);
+                const int lds0 = (q * kWaves + w) * kWave * 8;
+                lds_dma16(rec + RL.kthi + r * C + chg * 8, s_Kh + lds0);
+                lds_dma16(rec + RL.ktlo + r * C + chg * 8, s_Kl + lds0);
+            }
+            if (w == 0 && lane < DK / 4)
+                lds_dma16(rec + RL.fac + lane * 8, reinterpret_cast<__bf16 *>(s_eg));
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) put_kt(po.ka[ks], ks * 32 + acol, w * RB + lane % 16, s_Kh, s_Kl);
+        }
+    }
 
     const bool want_o = o != nullptr;
 #pragma unroll 1
@@ -2095,7 +2168,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
         if (j0 + TV < DV) load_tile(j0 + TV, nm, nv);  // the next tile's inputs
         __syncthreads();
 
-        // U = T' R (and W = diag(e^{g_L - g}) U for the state update)
+        // U = T' R (and W = diag(e^{g_L - g}) U for the scalar-decay update)
+        f32x4v uacc[NVT];
 #pragma unroll
         for (int t = 0; t < NVT; ++t) {
             f32x4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -2105,9 +2179,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
                     const int off = (t * 16 + lane % 16) * CB + kq * 32 + acol;
                     acc = mma(ta[kq], read_frag<F>(s_Rh + off, s_Rl + off), acc);
                 }
+            uacc[t] = acc;
+        }
+        if constexpr (RU1) __syncthreads();  // R is read: U goes over it
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            f32x4v acc = uacc[t];
             const int uo = (t * 16 + lane % 16) * CB + r0v;
             put4<F>(s_Uh, s_Ul, uo, acc);
-            if constexpr (ST) {
+            if constexpr (ST && !PK) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] *= gu[i];
                 put4<F>(s_Wh, s_Wl, uo, acc);
@@ -2140,20 +2220,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST ? 2
         }
 
         if constexpr (ST) {
-            // Sig <- gamma_L Sig + K^T W, each lane's 4 keys of its value
-            // column straight out (the next tile rewrites no buffer this
-            // reads before its own barriers)
+            // Sig <- gamma_L Sig + K^T W (per key: diag(e^{g_L}) Sig +
+            // K~^T U), each lane's 4 keys of its value column straight out
+            // (the next tile rewrites no buffer this reads before its own
+            // barriers)
 #pragma unroll
             for (int m = 0; m < NEG; ++m) {
                 const int ft = w + m * kWaves, t = ft % NVT, dt = ft / NVT;
+                f32x4v dec = {gamL, gamL, gamL, gamL};
+                if constexpr (PK) dec = *reinterpret_cast<const f32x4v *>(s_eg + dt * 16 + (lane / 16) * 4);
                 f32x4v acc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = gamL * mst[m][i];
+                for (int i = 0; i < 4; ++i) acc[i] = dec[i] * mst[m][i];
 #pragma unroll
                 for (int kq = 0; kq < 2; ++kq) {
                     const int ou = (t * 16 + lane % 16) * CB + kq * 32 + acol;
-                    const int ok = kt_off(dt * 16 + lane % 16, kq * 32 + acol);
-                    acc = mma(read_frag<F>(s_Kh + ok, s_Kl + ok), read_frag<F>(s_Wh + ou, s_Wl + ou), acc);
+                    if constexpr (PK) {
+                        const int ok = kt_swz(dt * 16 + lane % 16, kq * 4 + lane / 16);
+                        acc = mma(read_frag<F>(s_Kh + ok, s_Kl + ok), read_frag<F>(s_Uh + ou, s_Ul + ou), acc);
+                    } else {
+                        const int ok = kt_off(dt * 16 + lane % 16, kq * 32 + acol);
+                        acc = mma(read_frag<F>(s_Kh + ok, s_Kl + ok), read_frag<F>(s_Wh + ou, s_Wl + ou), acc);
+                    }
                 }
                 const unsigned off = 4u * (unsigned)((dt * 16 + (lane / 16) * 4) * DV + j0 + vcol(t * 16 + lane % 16));
 #pragma unroll
@@ -2192,19 +2280,27 @@ hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
     const size_t sh_pad = (n_sh + 7) / 8 * 8;  // see scan_unit
     const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
     const dim3 scan_grid((unsigned)(sh_pad * (DV / TV)));
-    // Sequences of at most one chunk (scalar decay, no checkpoints) run in
+    // Sequences of at most one chunk (calls without checkpoints) run in
     // the one-chunk kernel; the plan gives them no records and the scan
     // skips them. GDN_PREFILL_ONE_CHUNK=0 sends them through the chunked
     // kernels instead (the same results bit for bit; for tests).
     const char *oc = std::getenv("GDN_PREFILL_ONE_CHUNK");
-    a.fuse1 = a.variant == kScalar && !ck && !(oc && oc[0] == '0');
+    a.fuse1 = !ck && !(oc && oc[0] == '0');
     a.group_size = G;
     if (a.fuse1) {  // with one more workgroup: the first segment's plan
         const dim3 g1((unsigned)(n_sh + 1));
-        if (a.state_out)
-            hipLaunchKernelGGL((one_chunk_kernel<DK, DV, TI, TO, true>), g1, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((one_chunk_kernel<DK, DV, TI, TO, false>), g1, dim3(kThreads), 0, stream, a);
+        const auto go = [&](auto vtag) {
+            constexpr int VAR = decltype(vtag)::value;
+            if (a.state_out)
+                hipLaunchKernelGGL((one_chunk_kernel<DK, DV, TI, TO, true, VAR>), g1, dim3(kThreads), 0,
+                                   stream, a);
+            else
+                hipLaunchKernelGGL((one_chunk_kernel<DK, DV, TI, TO, false, VAR>), g1, dim3(kThreads), 0,
+                                   stream, a);
+        };
+        if (a.variant == kKda) go(std::integral_constant<int, kKda>{});
+        else if (a.variant == kRwkv6) go(std::integral_constant<int, kRwkv6>{});
+        else go(std::integral_constant<int, kScalar>{});
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -1,10 +1,12 @@
 """GPU parity of the one-chunk kernel.
 
-With a scalar decay, sequences of at most one chunk (64 tokens) -- the
-fork's branches, and short sequences of a shared-context call -- run in one
-kernel that keeps the chunk's operands on chip instead of passing a chunk
-record from the prep kernel to the scan. Its arithmetic is theirs in the
-same order, so every output must equal the chunked path's bit for bit
+Sequences of at most one chunk (64 tokens) -- the fork's branches, and
+short sequences of a shared-context call -- run in one kernel instead of
+passing a chunk record from the prep kernel to a later scan: with a scalar
+decay the chunk's operands stay on chip, per key the record goes through
+the (sequence, head)'s workspace slot and back within the workgroup. Its
+arithmetic is theirs in the same order, so every output must equal the
+chunked path's bit for bit
 (GDN_PREFILL_ONE_CHUNK=0 sends the same sequences through the chunked
 kernels), and both must hold the fp64 oracle's bar. The rounds mix short
 and long sequences (the long ones still take the chunked kernels in the
@@ -52,7 +54,7 @@ def io_window(inp, w0):
     return f32(w0), w0
 
 
-def run(inp, states, s0=None, w0_dev=None):
+def run(inp, states, s0=None, w0_dev=None, variant="gdn"):
     """Both calls; returns host copies (windows as bits)."""
     H, dk, dv, Np, Nb = inp.H, inp.dk, inp.dv, inp.Np, inp.Nb
     R, NB = len(inp.cu_seqlens) - 1, len(inp.branch_cu) - 1
@@ -66,7 +68,7 @@ def run(inp, states, s0=None, w0_dev=None):
     gdn.gdn_prefill_shared(q[:Np], k[:Np], v[:Np], la[:Np], beta[:Np], i32(inp.cu_seqlens), st,
                            o=o_p, conv_w=conv_w, qk_l2norm=True,
                            init_state=None if s0 is None else f32(s0), init_window=w0_dev,
-                           final_window=win)
+                           final_window=win, variant=variant)
     out = dict(o_p=o_p.cpu().numpy(), st=st.cpu().numpy(), win=window_to_bits(win))
     if NB > 0:
         o_b = torch.full((Nb, H, dv), float("nan"), device=DEV)
@@ -75,7 +77,7 @@ def run(inp, states, s0=None, w0_dev=None):
         gdn.gdn_fork_branches(q[Np:], k[Np:], v[Np:], la[Np:], beta[Np:], i32(inp.branch_cu),
                               i32(inp.branch_parent), st, o_b, parent_window=win,
                               branch_state=st_b, branch_window=win_b, conv_w=conv_w,
-                              qk_l2norm=True)
+                              qk_l2norm=True, variant=variant)
         out["o_b"] = o_b.cpu().numpy()
         if states:
             out["st_b"] = st_b.cpu().numpy()
@@ -90,14 +92,14 @@ def assert_bitwise(a, b):
         assert np.array_equal(a[name], b[name], equal_nan=True), name
 
 
-def prefix_oracle(inp, s0=None, w0=None):
+def prefix_oracle(inp, s0=None, w0=None, variant="gdn"):
     Np = inp.Np
     return oracle.prefill(inp.q[:Np], inp.k[:Np], inp.v[:Np], inp.log_alpha[:Np], inp.beta[:Np],
                           inp.cu_seqlens, conv_w=inp.conv_w, qk_norm=True, state_in=s0,
-                          win_in=w0)
+                          win_in=w0, variant=variant)
 
 
-def branch_oracle(inp, st, win):
+def branch_oracle(inp, st, win, variant="gdn"):
     """Oracle outputs of the branches with a valid parent, as a reduced round."""
     Np, R = inp.Np, len(inp.cu_seqlens) - 1
     bcu, par = inp.branch_cu, inp.branch_parent
@@ -106,7 +108,7 @@ def branch_oracle(inp, st, win):
     vcu = np.concatenate([[0], np.cumsum([bcu[b + 1] - bcu[b] for b in valid])]).astype(np.int32)
     o_b, st_b, win_b = oracle.fork(inp.q[rows], inp.k[rows], inp.v[rows], inp.log_alpha[rows],
                                    inp.beta[rows], vcu, par[valid], st, win, conv_w=inp.conv_w,
-                                   qk_norm=True)
+                                   qk_norm=True, variant=variant)
     return valid, vcu, o_b, st_b, win_b
 
 
@@ -115,28 +117,33 @@ BRANCHES = [0, 1, 5, 63, 64, 65, 130, 17, 40, 64, 3, 33]
 PARENT = [0, 0, 1, 2, 3, 5, 5, -1, 4, 6, 2, 1]  # -1 and 6 (= R): invalid
 
 
+SHAPES = [(16, 128, 128), (3, 64, 128), (3, 128, 32), (2, 32, 64)]
+CASES = ([("gdn", H, dk, dv, io) for H, dk, dv in SHAPES for io in ("bf16", "f32")]
+         + [(var, H, dk, dv, "bf16") for var in ("kda", "rwkv6") for H, dk, dv in SHAPES]
+         + [(var, 16, 128, 128, "f32") for var in ("kda", "rwkv6")])
+
+
 @pytest.mark.parametrize("states", [False, True])
-@pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("H,dk,dv", [(16, 128, 128), (3, 64, 128), (3, 128, 32), (2, 32, 64)])
-def test_one_chunk_is_bitwise_the_chunked_path(H, dk, dv, io, states):
+@pytest.mark.parametrize("variant,H,dk,dv,io", CASES)
+def test_one_chunk_is_bitwise_the_chunked_path(variant, H, dk, dv, io, states):
     inp = gi.seq_inputs(PREFIX, BRANCHES, PARENT, H, dk, dv, io=io, conv=True,
-                        seed=dk + dv + H + states)
-    fused = run(inp, states)
+                        per_key=variant != "gdn", seed=dk + dv + H + states)
+    fused = run(inp, states, variant=variant)
     with chunked_path():
-        chunked = run(inp, states)
+        chunked = run(inp, states, variant=variant)
     assert_bitwise(fused, chunked)
 
     tol = TOL if io == "bf16" else TOL_F32
-    o_p, st, win = prefix_oracle(inp)
+    o_p, st, win = prefix_oracle(inp, variant=variant)
     e_p = slice_err(fused["o_p"], o_p, inp.cu_seqlens, H)
     e_s = oracle.rel_err(fused["st"], st, axes=(2, 3))
     assert np.array_equal(fused["win"], window_ref(win, io))
-    valid, vcu, o_r, st_r, win_r = branch_oracle(inp, st, win)
+    valid, vcu, o_r, st_r, win_r = branch_oracle(inp, st, win, variant=variant)
     bcu = inp.branch_cu
     g_rows = np.concatenate([np.arange(bcu[b], bcu[b + 1]) for b in valid])
     e_b = slice_err(fused["o_b"][g_rows], o_r, vcu, H)
     e_bs = oracle.rel_err(fused["st_b"][valid], st_r, axes=(2, 3)) if states else 0.0
-    print(f"H={H} dk={dk} dv={dv} {io} states={states}: o_p {e_p:.2e} st {e_s:.2e} "
+    print(f"{variant} H={H} dk={dk} dv={dv} {io} states={states}: o_p {e_p:.2e} st {e_s:.2e} "
           f"o_b {e_b:.2e} st_b {e_bs:.2e}", flush=True)
     assert max(e_p, e_s, e_b, e_bs) <= tol
     if states:
