@@ -213,6 +213,14 @@ int gdn_prefill_checkpointed(const void *q, const void *k, const void *v,
  *  branch_window [n_branch, 3, CC] io_dtype or NULL
  * A branch whose parent is out of range is skipped and its o rows are set
  * to NaN. Errors as gdn_prefill_shared.
+ * Branches of at most 64 tokens (the common case) run the chunk
+ * preparation and the chunk step in one workgroup per (branch, head),
+ * with no chunk record in the workspace (per-key variants pass it through
+ * the (branch, head)'s own workspace slot); so do sequences of at most 64
+ * tokens in gdn_prefill_shared. The results are bit for bit those of the
+ * chunked path, which GDN_PREFILL_ONE_CHUNK=0 in the environment selects
+ * (read at each call; for tests). Calls with checkpoints always take the
+ * chunked path.
  */
 int gdn_fork_branches(const void *q, const void *k, const void *v,
                       const float *log_alpha, const float *beta,
