@@ -1910,8 +1910,9 @@ __device__ __forceinline__ void one_chunk_unit(int b, int H, int &s, int &h) {
 // LDS: the prep's buffers, reused once T' and P are in registers (s_A: the
 // split state planes; s_k: the R and U planes, or with ST the K^T planes),
 // the value channels' conv taps, and with ST the R, U and W planes (per
-// key: R and U in one pair of planes in the prep's table buffer, U written
-// over R behind a barrier, and e^{g_L} after them).
+// key: K~^T in the K buffer, then R and U in one pair of planes, U written
+// over R behind a barrier, and e^{g_L} after them, behind K~^T where they
+// fit (d_k <= 64), else in the prep's table buffer).
 template <int DK, int DV, typename TI, typename TO, bool ST, int VAR = kScalar>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST || VAR != kScalar ? 2 : 3))) void one_chunk_kernel(
     PrefillArgs a) {
@@ -1981,7 +1982,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST || 
     const __bf16 *const rec =
         PK ? reinterpret_cast<const __bf16 *>(static_cast<const char *>(a.ws) +
                                               ws_layout(a.n_tokens, a.n_seq, H, DK, DV, PK, a.nseg).rec_off) +
-                 ((size_t)s * H + h) * rec_layout(DK, PK).elems
+                 ((size_t)s * H + h) * RL.elems
            : nullptr;
     if constexpr (PK) __syncthreads();  // the record in the slot is complete
 
