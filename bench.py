@@ -238,7 +238,19 @@ def bench_fork(torch, gdn, gi, reps, variant="gdn"):
                 "frac": achieved / HBM_PEAK_GBPS, "algorithmic_bytes": alg_bytes,
                 "traffic": traffic,
                 "traffic_over_algorithmic": None if traffic is None else traffic / alg_bytes}
+    # roofline of call 2 (the one-chunk kernel for these one-chunk
+    # branches): the same algorithmic bytes per branch token-head plus each
+    # parent's state once per (parent, head)
+    b_alg = Nb * H * (3 * d * 2 + 8 + d * 4) + R * H * d * d * 4
+    b_ach = b_alg / (tf_ms / 1e3) / 1e9
+    b_traffic = one_chunk_traffic() if variant == "gdn" else None
+    b_roofline = {"bound": "hbm", "kernels": "the branch call (one-chunk kernel and the empty "
+                  "chunked-path launches)", "achieved": b_ach, "peak": HBM_PEAK_GBPS,
+                  "unit": "GB/s", "frac": b_ach / HBM_PEAK_GBPS, "algorithmic_bytes": b_alg,
+                  "traffic": b_traffic,
+                  "traffic_over_algorithmic": None if b_traffic is None else b_traffic / b_alg}
     return dict(branches=NB, prefill_ms=tp_ms, fork_ms=tf_ms, prefill_roofline=roofline,
+                branch_roofline=b_roofline,
                 fork_with_states_ms=tfs_ms,
                 branches_per_s_with_states=NB / ((tp_ms + tfs_ms) / 1e3),
                 prefill_dense_tile_tflops=pre_tflops,
@@ -528,6 +540,20 @@ def prefill_traffic():
             return None
         total += prof["traffic_bytes"] * prof.get("dispatches_per_call", 1)
     return total
+
+
+def one_chunk_traffic():
+    """HBM bytes of the branch call's one-chunk kernel on fork_prefill from
+    the committed counter summary, or None when the prefill sources changed
+    since the counters were taken."""
+    from linear_attention_recurrent_gdn_amd import profiling
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    prof = profiling.read_profile_block(
+        os.path.join(here, "profiles", "fork_branches_one_chunk_traffic.md"))
+    if not prof or prof.get("source_hash") != profiling.source_hash(profiling.PREFILL_SOURCES):
+        return None
+    return prof["traffic_bytes"]
 
 
 def measured_traffic(ms_per_launch):
