@@ -1441,8 +1441,11 @@ struct ChunkRegs {
 // a separate instance so the plain scan keeps its register budget.
 // GRP: branch groups (a.groups set); else one sequence per workgroup, so
 // the sequence loop below runs once and compiles away.
-template <int DK, int DV, typename TI, typename TO, bool PK, bool CK, bool GRP = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void scan_kernel(PrefillArgs a) {
+// scan_body runs workgroup unit b (a sequence-head or branch group, and a
+// value tile; see scan_unit) and returns false, having done nothing, when
+// neither b nor any unit b + 8 k has work.
+template <int DK, int DV, typename TI, typename TO, bool PK, bool CK, bool GRP>
+__device__ __forceinline__ bool scan_body(const PrefillArgs &a, int b) {
     constexpr bool F = std::is_same<TI, float>::value;  // fp32 operands (see Frag)
     constexpr int KS = DK / 32;          // k-steps over d_k
     constexpr int CB = C + 8;            // padded row of the R^T / U^T / W^T planes
@@ -1474,18 +1477,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     constexpr int NT = DV / TV;
     int shd, tile;
-    scan_unit(blockIdx.x, NT, shd, tile);
-    if (shd >= a.n_seq * a.H) return;
+    scan_unit(b, NT, shd, tile);
+    if (shd >= a.n_seq * a.H) return false;
     const int unit = shd / a.H, h = shd % a.H;
     // one segment and no chunk records: every sequence is the one-chunk
     // kernel's (a sequence past one chunk has records in the only segment)
-    if (a.fuse1 && a.nseg == 1 && static_cast<const int32_t *>(a.ws)[a.n_seq] == 0) return;
+    if (a.fuse1 && a.nseg == 1 && static_cast<const int32_t *>(a.ws)[a.n_seq] == 0) return false;
     // this workgroup's sequences: one, or (branch calls) a group of branches
     // of one parent, which run one after another from one load of the
     // parent's state while no branch changes it
     int s_first = unit, s_last = unit + 1;
     if constexpr (GRP) {
-        if (unit >= a.groups[0]) return;
+        if (unit >= a.groups[0]) return false;
         s_first = a.groups[1 + unit];
         s_last = a.groups[2 + unit];
     }
@@ -1874,6 +1877,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // a state update ran: the next branch of the group reloads the parent's
     if (nchunks > 1 || (need_final && nchunks > 0)) have = false;
     }
+    return true;
+}
+
+// Branch groups (GRP): a grid of at most kScanResident workgroups (a
+// multiple of 8), block b taking the units b, b + gridDim.x, ... (one XCD)
+// while they have work, so that a branch call whose branches all take the
+// one-chunk kernel, or that forms few groups, runs one round of
+// workgroups. Otherwise one unit per workgroup.
+template <int DK, int DV, typename TI, typename TO, bool PK, bool CK, bool GRP = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void scan_kernel(PrefillArgs a) {
+    if constexpr (GRP) {
+#pragma unroll 1
+        for (int b = blockIdx.x; scan_body<DK, DV, TI, TO, PK, CK, GRP>(a, b); b += gridDim.x)
+            __syncthreads();  // the LDS of one unit before the next
+    } else {
+        scan_body<DK, DV, TI, TO, PK, CK, GRP>(a, blockIdx.x);
+    }
 }
 
 // ------------------------------------------------------------ one-chunk sequences
@@ -2131,8 +2151,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ST || 
             float xr[7];
 #pragma unroll
             for (int q = 0; q < 7; ++q) {
-                const int row = r0v - 3 + q;
-                const bool ok = (conv || q >= 3) && ((row < L && row >= 0) || (row < 0 && win));
+                // rows before the sequence: the incoming window's, else
+                // zero; rows past its end feed only rows zeroed below
+                const bool ok = q >= 3 || (conv && (r0v - 3 + q >= 0 || win));
                 xr[q] = ok ? VPair<TI>::get(nv[q], t) : 0.f;
             }
 #pragma unroll
@@ -2281,6 +2302,7 @@ hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
     const size_t sh_pad = (n_sh + 7) / 8 * 8;  // see scan_unit
     const bool ck = a.ckpt_state != nullptr && a.ckpt_every > 0 && a.ckpt_cap > 0;
     const dim3 scan_grid((unsigned)(sh_pad * (DV / TV)));
+    const dim3 grp_grid((unsigned)std::min((long long)(sh_pad * (DV / TV)), kScanResident));
     // Sequences of at most one chunk (calls without checkpoints) run in
     // the one-chunk kernel; the plan gives them no records and the scan
     // skips them. GDN_PREFILL_ONE_CHUNK=0 sends them through the chunked
@@ -2332,10 +2354,10 @@ hipError_t launch_typed(const PrefillArgs &a0, hipStream_t stream) {
         }
         if (a.groups) {  // branch calls never take checkpoints
             if (pk)
-                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, false, true>), scan_grid,
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, true, false, true>), grp_grid,
                                    dim3(kThreads), 0, stream, a);
             else
-                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, false, true>), scan_grid,
+                hipLaunchKernelGGL((scan_kernel<DK, DV, TI, TO, false, false, true>), grp_grid,
                                    dim3(kThreads), 0, stream, a);
         } else if (ck) {
             if (pk)
