@@ -122,3 +122,30 @@ def test_outputs_do_not_depend_on_branch_states(variant):
     o_without, _, _ = run(inp, variant, False)
     o_with, _, _ = run(inp, variant, True)
     assert np.array_equal(o_without, o_with, equal_nan=True)
+
+
+@pytest.mark.parametrize("variant,states", [("gdn", True), ("kda", False)])
+def test_more_groups_than_resident_workgroups(variant, states):
+    """Parents that alternate make every branch its own group: 80 groups x
+    4 heads x 4 value tiles = 1,280 scan units against a grid of 512, so a
+    workgroup runs units b, b + 512 and b + 1024 in turn. Most branches
+    pass one chunk (the scan's), the rest take the one-chunk kernel."""
+    H, d = 4, 128
+    prefix = [70, 130]
+    parent = [i % 2 for i in range(80)]
+    cycle = [65, 100, 3, 130, 64, 0, 70]
+    branches = [cycle[i % len(cycle)] for i in range(len(parent))]
+    target = -(-2 * 256 // (H * d // 32))  # groups giving one resident round
+    G = -(-len(parent) // target)
+    assert G > 1 and len(parent) * H * (d // 32) > 2 * 256  # groups of one branch each
+    inp = gi.seq_inputs(prefix, branches, parent, H, d, d, io="bf16", conv=True,
+                        per_key=variant != "gdn", seed=11)
+    o_b, st_b, win_b = run(inp, variant, states)
+    valid, vcu, o_r, st_r, win_r = reference(inp, variant)
+    assert valid == list(range(len(parent)))
+    e_o = slice_err(o_b, o_r, vcu, H)
+    e_s = oracle.rel_err(st_b, st_r, axes=(2, 3)) if states else 0.0
+    print(f"{variant} states={states}: o {e_o:.2e} state {e_s:.2e}", flush=True)
+    assert e_o <= TOL and e_s <= TOL
+    if states:
+        assert np.array_equal(window_to_bits(win_b), window_ref(win_r, "bf16"))
