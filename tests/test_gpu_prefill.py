@@ -379,7 +379,14 @@ def test_full_size_fork_prefill_sampled():
                           t["beta"][Np:], t["branch_cu"], t["branch_parent"], st, o_b,
                           parent_window=win, branch_state=st_b, conv_w=t["conv_w"],
                           qk_l2norm=True)
+    # the call as the bench times it (o only): the same o bit for bit (the
+    # state update runs after the outputs and changes nothing they read)
+    o_b2 = torch.full((Nb, H, d), float("nan"), device=DEV)
+    gdn.gdn_fork_branches(t["q"][Np:], t["k"][Np:], t["v"][Np:], t["log_alpha"][Np:],
+                          t["beta"][Np:], t["branch_cu"], t["branch_parent"], st, o_b2,
+                          parent_window=win, conv_w=t["conv_w"], qk_l2norm=True)
     torch.cuda.synchronize()
+    assert torch.equal(o_b2, o_b)
     P, bpr, L = w["prefix"], w["branches_per_req"], w["branch_len"]
     host = lambda x: x.float().cpu().numpy()  # noqa: E731
     cw = host(t["conv_w"])
