@@ -355,15 +355,17 @@ def test_invalid_parent_gives_nan_outputs():
     assert np.isnan(g["st_b"][1]).all()
 
 
-def test_full_size_fork_prefill_sampled():
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+def test_full_size_fork_prefill_sampled(variant):
     """8 requests x 8192-token contexts, 20 branches of 64 tokens each,
-    H=16, d=128, chunk 64, conv width 4, bf16 I/O: the GPU runs the whole
+    H=16, d=128, chunk 64, conv width 4, bf16 I/O (and the same with
+    per-key decay, as the bench also times it): the GPU runs the whole
     workload in the launch configuration the bench times; the oracle checks
     two requests and all of their branches (every head)."""
     w = gi.WORKLOADS["fork_prefill"]
     R, H, d = w["R"], w["H"], w["d"]
     pl, bl, par = gi.fork_layout(R, w["prefix"], w["branches_per_req"], w["branch_len"])
-    t = gi.torch_seq_inputs(pl, bl, par, H, d, d, conv=True, seed=0)
+    t = gi.torch_seq_inputs(pl, bl, par, H, d, d, conv=True, per_key=variant != "gdn", seed=0)
     Np, Nb = t["Np"], t["Nb"]
     cc = H * 3 * d
     st = torch.empty((R, H, d, d), device=DEV)
@@ -371,20 +373,20 @@ def test_full_size_fork_prefill_sampled():
     o_p = torch.empty((Np, H, d), device=DEV)
     gdn.gdn_prefill_shared(t["q"][:Np], t["k"][:Np], t["v"][:Np], t["log_alpha"][:Np],
                            t["beta"][:Np], t["cu_seqlens"], st, o=o_p, conv_w=t["conv_w"],
-                           qk_l2norm=True, final_window=win)
+                           qk_l2norm=True, final_window=win, variant=variant)
     NB = len(bl)
     o_b = torch.empty((Nb, H, d), device=DEV)
     st_b = torch.empty((NB, H, d, d), device=DEV)
     gdn.gdn_fork_branches(t["q"][Np:], t["k"][Np:], t["v"][Np:], t["log_alpha"][Np:],
                           t["beta"][Np:], t["branch_cu"], t["branch_parent"], st, o_b,
                           parent_window=win, branch_state=st_b, conv_w=t["conv_w"],
-                          qk_l2norm=True)
+                          qk_l2norm=True, variant=variant)
     # the call as the bench times it (o only): the same o bit for bit (the
     # state update runs after the outputs and changes nothing they read)
     o_b2 = torch.full((Nb, H, d), float("nan"), device=DEV)
     gdn.gdn_fork_branches(t["q"][Np:], t["k"][Np:], t["v"][Np:], t["log_alpha"][Np:],
                           t["beta"][Np:], t["branch_cu"], t["branch_parent"], st, o_b2,
-                          parent_window=win, conv_w=t["conv_w"], qk_l2norm=True)
+                          parent_window=win, conv_w=t["conv_w"], qk_l2norm=True, variant=variant)
     torch.cuda.synchronize()
     assert torch.equal(o_b2, o_b)
     P, bpr, L = w["prefix"], w["branches_per_req"], w["branch_len"]
@@ -394,7 +396,8 @@ def test_full_size_fork_prefill_sampled():
         rows = slice(r * P, (r + 1) * P)
         o_r, st_r, win_r = oracle.prefill(host(t["q"][rows]), host(t["k"][rows]),
                                           host(t["v"][rows]), host(t["log_alpha"][rows]),
-                                          host(t["beta"][rows]), [0, P], conv_w=cw, qk_norm=True)
+                                          host(t["beta"][rows]), [0, P], conv_w=cw, qk_norm=True,
+                                          variant=variant)
         e_o = oracle.rel_err(host(o_p[rows]), o_r, axes=(0, 2))
         e_s = oracle.rel_err(host(st[r:r + 1]), st_r, axes=(2, 3))
         brow = slice(Np + r * bpr * L, Np + (r + 1) * bpr * L)
@@ -402,14 +405,16 @@ def test_full_size_fork_prefill_sampled():
         o_br, st_br, _ = oracle.fork(host(t["q"][brow]), host(t["k"][brow]), host(t["v"][brow]),
                                      host(t["log_alpha"][brow]), host(t["beta"][brow]), bcu,
                                      np.zeros(bpr, dtype=np.int32), st_r, win_r, conv_w=cw,
-                                     qk_norm=True)
+                                     qk_norm=True, variant=variant)
         g_ob = host(o_b[r * bpr * L:(r + 1) * bpr * L])
         e_ob = max(oracle.rel_err(g_ob[i * L:(i + 1) * L], o_br[i * L:(i + 1) * L], axes=(0, 2))
                    for i in range(bpr))
         e_sb = oracle.rel_err(host(st_b[r * bpr:(r + 1) * bpr]), st_br, axes=(2, 3))
-        print(f"request {r}: o={e_o:.3e} state={e_s:.3e} branch o={e_ob:.3e} "
+        print(f"{variant} request {r}: o={e_o:.3e} state={e_s:.3e} branch o={e_ob:.3e} "
               f"branch state={e_sb:.3e}", flush=True)
-        cfg = "C3 fork_prefill (requests 0 and 7, all heads and their branches)"
+        cfg = ("C3 fork_prefill (requests 0 and 7, all heads and their branches)" if variant == "gdn"
+               else "C3 fork_prefill with per-key decay, KDA (requests 0 and 7, all heads and "
+                    "their branches)")
         _parity.record(cfg, "o_prefix", e_o, _parity.elementwise(host(o_p[rows]), o_r, (0, 2)),
                        TOL)
         _parity.record(cfg, "state", e_s, _parity.elementwise(host(st[r:r + 1]), st_r, (2, 3)),
